@@ -1,0 +1,53 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the oracle's pins reject every one of them.  The copy is compiled to a
+temporary library; the pin suite runs in a child process pointed at it."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "q8_0_d_big_endian": ("const float d = oracle_fp16_to_f32(load_le16(blk));\n            for (int t = 0; t < Q8_0_ELEMS",
+                          "const float d = oracle_fp16_to_f32((uint16_t)((blk[0] << 8) | blk[1]));\n            for (int t = 0; t < Q8_0_ELEMS"),
+    "q8_0_q_unsigned": ("const int8_t q = (int8_t)blk[2 + t];", "const int q = (uint8_t)blk[2 + t];"),
+    "q4k_nibbles_swapped": ("q = qs[32 * p + u] & 0x0f;", "q = qs[32 * p + u] >> 4;"),
+    "q4k_nibbles_interleaved": ("const int p = e / 64, u = e % 64;", "const int p = (e / 2) / 64 * 0 + e / 64, u = (e % 2) * 32 + (e % 64) / 2;"),
+    "q4k_subblock_index": ("sub = 2 * p + 1;", "sub = 2 * p;"),
+    "q4k_min_sign": ("out[i * n_in + k * Q4K_ELEMS + e] = a - b;", "out[i * n_in + k * Q4K_ELEMS + e] = a + b;"),
+    "q4k_min_dropped": ("out[i * n_in + k * Q4K_ELEMS + e] = a - b;", "out[i * n_in + k * Q4K_ELEMS + e] = a - 0.0f * b;"),
+    "q4k_scale_high_bits_from_wrong_byte": ("((s[j - 4] >> 6) << 4)", "((s[j] >> 6) << 4)"),
+    "q4k_mins_low_from_scale_bytes": ("m[j] = s[j + 4] & 63;", "m[j] = s[j] & 63;"),
+    "q4k_dmin_offset": ("load_le16(blk + 2)", "load_le16(blk)"),
+    "gemv_ignores_batch_row": ("(double)x[b * n_in + j];", "(double)x[j];"),
+    "gemv_transposed_weight": ("(double)W[i * n_in + j]", "(double)W[(j * n_out + i) % (n_out * n_in)]"),
+    "s_without_abs": ("sa += fabs(p);", "sa += p;"),
+    "residual_dropped": ("out[k] += (double)residual[k];", "out[k] += 0.0 * residual[k];"),
+    "silu_wrong_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "swiglu_operands_swapped": ("if (out) out[k] = oracle_silu(gg[k]) * uu[k];", "if (out) out[k] = oracle_silu(uu[k]) * gg[k];"),
+    "qkv_k_reads_q": ("oracle_q8_0_gemv(wk, n_in, n_kv", "oracle_q8_0_gemv(wq, n_in, n_kv"),
+    "fp16_bias": ("ldexpf((float)(1024 + f), e - 25)", "ldexpf((float)(1024 + f), e - 24)"),
+    "fp16_subnormal_scale": ("ldexpf((float)f, -24)", "ldexpf((float)f, -25)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new, 1)
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "mutant.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", str(so_path), str(c_path), "-lm"], check=True)
+    env = dict(os.environ, QDEC_ORACLE_LIB=str(so_path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the oracle pins"
