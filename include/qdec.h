@@ -1,0 +1,177 @@
+/*
+ * qdec.h -- C ABI of libqdec, block-quantized dequant-GEMV/GEMM for AMD MI355X
+ * (gfx950).
+ *
+ * Operations follow three rustdoc pages of the qualia_core_db crate:
+ *   [cuda_lane]    "Module cuda_lane" (inference::cuda_lane), Functions and
+ *                  Constants sections;
+ *   [weight_cache] the source view of inference/cuda_lane/weight_cache.rs
+ *                  (try_cuda_batch_gemv and the cache functions);
+ *   [QTensorEngine] "Struct QTensorEngine" (gguf_bridge), its methods.
+ * The GGML block layouts are not printed on those pages; the ones used are the
+ * workload definitions that accompany them:
+ *   Q8_0: 34-byte blocks of 32 weights = fp16 d (little-endian) then 32 int8 q;
+ *         w = d*q.
+ *   Q4_K: 144-byte super-blocks of 256 weights = fp16 d, fp16 dmin, 12 bytes of
+ *         eight 6-bit scales and eight 6-bit mins (GGML K-quant packing), 128
+ *         bytes of nibbles (low nibbles of each 64-element chunk p = sub-block
+ *         2p, high nibbles = sub-block 2p+1); w = d*sc*q - dmin*m.
+ *
+ * Conventions for every call below
+ *   - Weights are GGML raw block bytes in DEVICE memory, row-major: row i of an
+ *     n_out x n_in matrix starts at byte i*(n_in/32)*34 (Q8_0) or
+ *     i*(n_in/256)*144 (Q4_K) ("rows = out", [weight_cache] WeightEntry).
+ *   - x is DEVICE f32, packed batch x n_in; out is DEVICE f32, packed
+ *     batch x n_out ([weight_cache] try_cuda_batch_gemv doc comment):
+ *     out[b*n_out + i] = sum_j deq(W)[i][j] * x[b*n_in + j].
+ *   - Every call is asynchronous and ordered on `stream` (0 = the null stream).
+ *     Nothing is read back; faults inside kernels surface at the caller's next
+ *     synchronisation, as usual for HIP.
+ *   - The caller owns w, x, out and residual and keeps them alive until the
+ *     stream has passed the call.  out must not overlap x or the weights
+ *     (aliasing residual is allowed where stated).
+ *   - Repacked weights: the first use of a weight pointer (or qdec_prepare)
+ *     copies its blocks once into a library-owned, aligned device layout
+ *     ("Call once at plan build", [cuda_lane] preload_q4k_soa_weights).  The
+ *     copy is keyed by (device, pointer, type, n_in, n_out); the caller promises
+ *     that the bytes behind a cached pointer do not change until qdec_release
+ *     or qdec_clear_cache ("immutable", [cuda_lane] preload_resident_blob).
+ *   - Return value: QDEC_OK (0) or a negative qdec_status.  Invalid arguments
+ *     are rejected with QDEC_EINVAL before any HIP call; a failed allocation
+ *     returns QDEC_ENOMEM; a failed launch or HIP call returns QDEC_EHIP.
+ *     The library never falls back to a CPU path.  qdec_last_error() describes
+ *     the last failure on the calling thread.
+ *   - Thread safety: calls may come from several host threads; the repack
+ *     cache is guarded by a mutex.
+ */
+#ifndef QDEC_H
+#define QDEC_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(QDEC_BUILDING)
+#define QDEC_API __attribute__((visibility("default")))
+#else
+#define QDEC_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QDEC_OK = 0,
+    QDEC_EINVAL = -1,        /* bad dimension, null pointer, batch out of range */
+    QDEC_ENOMEM = -2,        /* device allocation for a repacked copy failed */
+    QDEC_EHIP = -3,          /* a HIP runtime call or kernel launch failed */
+    QDEC_EUNSUPPORTED = -4   /* no kernel for this device or shape */
+} qdec_status;
+
+/* GGML type ids. */
+typedef enum { QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12 } qdec_type;
+
+/* Largest batch accepted by the GEMV-shaped calls (decode).  The batched GEMM
+ * calls take any batch >= 1. */
+#define QDEC_GEMV_MAX_BATCH 8
+
+/* ------------------------------------------------------------ compute -- */
+
+/* Q8_0 dequant-GEMV ([cuda_lane] try_q8_0_cuda_gemv, q8_0_gemv_oracle_into):
+ * out[b][i] = sum_j deq(W)[i][j] * x[b][j] for 1 <= batch <= 8.
+ * n_in % 32 == 0, n_in, n_out >= 1.  f32 accumulation. */
+QDEC_API int q8_0_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
+              const float* x, float* out, hipStream_t stream);
+
+/* Down-projection with residual ([cuda_lane] try_q4k_soa_ffn_block_residual):
+ * out[b][i] = residual[b][i] + sum_j deq(W)[i][j] * x[b][j].
+ * residual is device f32 batch x n_out; out may be the same buffer as
+ * residual (in-place update).  Other conditions as q8_0_gemv. */
+QDEC_API int q8_0_gemv_residual(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
+                       const float* x, const float* residual, float* out,
+                       hipStream_t stream);
+
+/* Fused QKV with GQA ([cuda_lane] try_q4k_soa_qkv): one launch computes
+ * q = Wq x (n_q rows), k = Wk x and v = Wv x (n_kv rows each) from one shared
+ * x.  q_out is batch x n_q, k_out and v_out are batch x n_kv, three separate
+ * device buffers.  1 <= n_kv <= n_q; other conditions as q8_0_gemv. */
+QDEC_API int q8_0_qkv(const void* wq, const void* wk, const void* wv, int64_t n_in,
+             int64_t n_q, int64_t n_kv, int64_t batch, const float* x,
+             float* q_out, float* k_out, float* v_out, hipStream_t stream);
+
+/* Fused SwiGLU expansion ([cuda_lane] try_q4k_soa_fused_swiglu):
+ * out[b][i] = silu(g) * u, g = gate_row_i . x_b, u = up_row_i . x_b,
+ * silu(z) = z / (1 + exp(-z)).  Both weights are n_out x n_in Q8_0.
+ * Conditions as q8_0_gemv. */
+QDEC_API int q8_0_swiglu(const void* w_gate, const void* w_up, int64_t n_in, int64_t n_out,
+                int64_t batch, const float* x, float* out, hipStream_t stream);
+
+/* Q4_K dequant-GEMV ([cuda_lane] try_q4k_soa_gemv): as q8_0_gemv over Q4_K
+ * weights; n_in % 256 == 0, 1 <= batch <= 8. */
+QDEC_API int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
+             const float* x, float* out, hipStream_t stream);
+
+/* Batched prefill-shaped GEMM over Q8_0 weights ([weight_cache]
+ * try_cuda_batch_gemv: C[m x n] = A[m x k] B[k x n] with m = batch,
+ * k = n_in, n = n_out, B = W transposed).  Dequantised weight tiles and x
+ * tiles are rounded to bf16 and contracted on MFMA with f32 accumulation
+ * (relative error bound about 4e-3 of sum_j |w_ij x_bj|).  Any batch >= 1;
+ * n_in % 32 == 0.  The pages' padding to multiples of 16 adds zero terms
+ * only and is handled inside the kernel. */
+QDEC_API int q8_0_gemm_batched(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
+                      const float* x, float* out, hipStream_t stream);
+
+/* The same contraction over dense f32 row-major weights (n_out x n_in, device
+ * memory, used in place -- no repacked copy), bf16 MFMA with f32
+ * accumulation.  Any batch >= 1, n_in % 32 == 0. */
+QDEC_API int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
+                     const float* x, float* out, hipStream_t stream);
+
+/* -------------------------------------------------------- repack cache -- */
+
+/* Repack w now (load time, not timed), type QDEC_TYPE_Q8_0 or QDEC_TYPE_Q4_K
+ * ([cuda_lane] preload_q4k_soa_weights).  Idempotent. */
+QDEC_API int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream);
+
+/* Free every repacked copy made from w (all types and shapes) on the current
+ * device.  Returns QDEC_EINVAL if there was none.  Waits for the device. */
+QDEC_API int qdec_release(const void* w);
+
+/* Free every repacked copy on every device ([cuda_lane] clear_weight_cache,
+ * "tests / model swap").  Waits for the devices. */
+QDEC_API void qdec_clear_cache(void);
+
+/* Number of repacked copies currently held ([cuda_lane] weight_cache_len). */
+QDEC_API int64_t qdec_cache_len(void);
+
+/* ----------------------------------------------- dequantisation exports -- */
+
+/* Write deq(W) as device f32, n_out x n_in row-major, from the same repacked
+ * copy the compute calls read.  Bit-exact with the block definition: Q8_0
+ * products are exact in f32; Q4_K rounds once, in the final subtraction. */
+QDEC_API int q8_0_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream);
+QDEC_API int q4k_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream);
+
+/* ---------------------------------------------------------- diagnostics -- */
+
+/* Text of the last failure on this thread ("" if none).  Owned by the library,
+ * valid until the next call on the same thread. */
+QDEC_API const char* qdec_last_error(void);
+
+/* Number of kernels the library has launched in this process (a witness that
+ * the GPU path ran; [QTensorEngine] gemm_parity_probe). */
+QDEC_API uint64_t qdec_launch_count(void);
+
+/* One empty kernel on `stream` (launch-latency probe, the analogue of
+ * [QTensorEngine] bench_empty_submit_roundtrip). */
+QDEC_API int qdec_empty_kernel(hipStream_t stream);
+
+/* Plain device copy of `bytes` bytes (bytes % 16 == 0, both pointers 16-byte
+ * aligned): the known-size reference kernel for HBM byte counters. */
+QDEC_API int qdec_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDEC_H */

@@ -1,0 +1,206 @@
+"""Python binding of libqdec (include/qdec.h): block-quantized dequant-GEMV/GEMM
+for AMD MI355X (gfx950).
+
+Argument marshalling only.  Every function takes torch tensors that live on the
+GPU, passes their device pointers and the current HIP stream to the C ABI of the
+same name, and raises QdecError on a non-zero status.  All arithmetic runs in
+the library's HIP kernels; there is no CPU path.  The library must have been
+built (``python -m quantized_decode_ggml_amd._build`` or
+``__graft_entry__.build()``); importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqdec.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qdec.h")
+
+QDEC_OK, QDEC_EINVAL, QDEC_ENOMEM, QDEC_EHIP, QDEC_EUNSUPPORTED = 0, -1, -2, -3, -4
+TYPE_Q8_0, TYPE_Q4_K = 8, 12
+GEMV_MAX_BATCH = 8
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (quantized_decode_ggml_amd._build.build())")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+_SIGS = {
+    "q8_0_gemv": [_P, _I, _I, _I, _P, _P, _P],
+    "q8_0_gemv_residual": [_P, _I, _I, _I, _P, _P, _P, _P],
+    "q8_0_qkv": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P],
+    "q8_0_swiglu": [_P, _P, _I, _I, _I, _P, _P, _P],
+    "q4k_gemv": [_P, _I, _I, _I, _P, _P, _P],
+    "q8_0_gemm_batched": [_P, _I, _I, _I, _P, _P, _P],
+    "f32_gemm_batched": [_P, _I, _I, _I, _P, _P, _P],
+    "qdec_prepare": [_P, ctypes.c_int, _I, _I, _P],
+    "qdec_release": [_P],
+    "q8_0_dequantize": [_P, _I, _I, _P, _P],
+    "q4k_dequantize": [_P, _I, _I, _P, _P],
+    "qdec_empty_kernel": [_P],
+    "qdec_copy": [_P, _P, _I, _P],
+}
+for _name, _args in _SIGS.items():
+    getattr(lib, _name).argtypes = _args
+    getattr(lib, _name).restype = ctypes.c_int
+lib.qdec_clear_cache.argtypes = []
+lib.qdec_clear_cache.restype = None
+lib.qdec_cache_len.argtypes = []
+lib.qdec_cache_len.restype = ctypes.c_int64
+lib.qdec_last_error.argtypes = []
+lib.qdec_last_error.restype = ctypes.c_char_p
+lib.qdec_launch_count.argtypes = []
+lib.qdec_launch_count.restype = ctypes.c_uint64
+
+
+class QdecError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"qdec status {status}: {msg}")
+        self.status = status
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/qdec.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return re.findall(r"^QDEC_API\s+[\w\s\*]+?\b(\w+)\s*\(", text, re.M)
+
+
+def _check(status: int):
+    if status != QDEC_OK:
+        raise QdecError(status, lib.qdec_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _batch(x: torch.Tensor, n_in: int) -> int:
+    if x.numel() % n_in:
+        raise ValueError(f"x has {x.numel()} elements, not a multiple of n_in={n_in}")
+    return x.numel() // n_in
+
+
+def _f32_out(out, batch, n, like):
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=like.device)
+    return out
+
+
+def q8_0_gemv(w, n_in, n_out, x, out=None, stream=None):
+    """out[b, i] = sum_j deq(W)[i, j] x[b, j]; w holds raw GGML Q8_0 bytes."""
+    batch = _batch(x, n_in)
+    out = _f32_out(out, batch, n_out, x)
+    _check(lib.q8_0_gemv(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def q8_0_gemv_residual(w, n_in, n_out, x, residual, out=None, stream=None):
+    batch = _batch(x, n_in)
+    out = _f32_out(out, batch, n_out, x)
+    _check(lib.q8_0_gemv_residual(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(residual), _ptr(out),
+                                  _stream(stream)))
+    return out
+
+
+def q8_0_qkv(wq, wk, wv, n_in, n_q, n_kv, x, q_out=None, k_out=None, v_out=None, stream=None):
+    batch = _batch(x, n_in)
+    q_out = _f32_out(q_out, batch, n_q, x)
+    k_out = _f32_out(k_out, batch, n_kv, x)
+    v_out = _f32_out(v_out, batch, n_kv, x)
+    _check(lib.q8_0_qkv(_ptr(wq), _ptr(wk), _ptr(wv), n_in, n_q, n_kv, batch, _ptr(x), _ptr(q_out),
+                        _ptr(k_out), _ptr(v_out), _stream(stream)))
+    return q_out, k_out, v_out
+
+
+def q8_0_swiglu(w_gate, w_up, n_in, n_out, x, out=None, stream=None):
+    batch = _batch(x, n_in)
+    out = _f32_out(out, batch, n_out, x)
+    _check(lib.q8_0_swiglu(_ptr(w_gate), _ptr(w_up), n_in, n_out, batch, _ptr(x), _ptr(out),
+                           _stream(stream)))
+    return out
+
+
+def q4k_gemv(w, n_in, n_out, x, out=None, stream=None):
+    batch = _batch(x, n_in)
+    out = _f32_out(out, batch, n_out, x)
+    _check(lib.q4k_gemv(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def q8_0_gemm_batched(w, n_in, n_out, x, out=None, stream=None):
+    batch = _batch(x, n_in)
+    out = _f32_out(out, batch, n_out, x)
+    _check(lib.q8_0_gemm_batched(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def f32_gemm_batched(w, n_in, n_out, x, out=None, stream=None):
+    batch = _batch(x, n_in)
+    out = _f32_out(out, batch, n_out, x)
+    _check(lib.f32_gemm_batched(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def prepare(w, qtype, n_in, n_out, stream=None):
+    _check(lib.qdec_prepare(_ptr(w), int(qtype), n_in, n_out, _stream(stream)))
+
+
+def release(w):
+    _check(lib.qdec_release(_ptr(w)))
+
+
+def clear_cache():
+    lib.qdec_clear_cache()
+
+
+def cache_len() -> int:
+    return int(lib.qdec_cache_len())
+
+
+def q8_0_dequantize(w, n_in, n_out, out=None, stream=None):
+    if out is None:
+        out = torch.empty((n_out, n_in), dtype=torch.float32, device=w.device)
+    _check(lib.q8_0_dequantize(_ptr(w), n_in, n_out, _ptr(out), _stream(stream)))
+    return out
+
+
+def q4k_dequantize(w, n_in, n_out, out=None, stream=None):
+    if out is None:
+        out = torch.empty((n_out, n_in), dtype=torch.float32, device=w.device)
+    _check(lib.q4k_dequantize(_ptr(w), n_in, n_out, _ptr(out), _stream(stream)))
+    return out
+
+
+def launch_count() -> int:
+    return int(lib.qdec_launch_count())
+
+
+def last_error() -> str:
+    return lib.qdec_last_error().decode(errors="replace")
+
+
+def empty_kernel(stream=None):
+    _check(lib.qdec_empty_kernel(_stream(stream)))
+
+
+def copy(dst, src, nbytes, stream=None):
+    _check(lib.qdec_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))

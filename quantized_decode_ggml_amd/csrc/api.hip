@@ -1,0 +1,401 @@
+// C ABI of libqdec (declared in include/qdec.h): argument validation, the
+// repack cache, error reporting and the launch counter.  All device work is in
+// the kernels of the other translation units; nothing here computes on the CPU.
+#include "qdec.h"
+#include "qdec_internal.h"
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+namespace qdec {
+
+namespace {
+
+thread_local std::string t_error;
+std::atomic<uint64_t> g_launches{0};
+
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(QDEC_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ------------------------------------------------------------ repack cache --
+// Keyed by (device, raw pointer, type, n_in, n_out), guarded by one mutex (the
+// pages' weight cache is likewise a mutex-guarded global map).  The repack is
+// enqueued on the caller's stream; an event records its completion so that a
+// first use from another stream waits for it.
+struct Key {
+    int dev;
+    uintptr_t ptr;
+    int type;
+    int64_t n_in, n_out;
+    bool operator<(const Key& o) const
+    {
+        return std::tie(dev, ptr, type, n_in, n_out) < std::tie(o.dev, o.ptr, o.type, o.n_in, o.n_out);
+    }
+};
+
+struct Entry {
+    void* buf = nullptr;
+    int64_t bytes = 0;
+    hipEvent_t ready = nullptr;
+    hipStream_t made_on = nullptr;
+    bool done = false;
+};
+
+std::mutex g_mu;
+std::map<Key, Entry> g_cache;
+
+bool fail_alloc_hook()
+{
+    const char* v = std::getenv("QDEC_FAIL_ALLOC");
+    return v && v[0] == '1';
+}
+
+void destroy(Entry& e)
+{
+    if (e.ready) (void)hipEventDestroy(e.ready);
+    if (e.buf) (void)hipFree(e.buf);
+    e = Entry{};
+}
+
+// Returns the repacked copy of w, making it on first use.
+int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s, const void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const Key key{dev, reinterpret_cast<uintptr_t>(w), type, n_in, n_out};
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_cache.find(key);
+    if (it == g_cache.end()) {
+        if (fail_alloc_hook()) return fail(QDEC_ENOMEM, "repack allocation refused (QDEC_FAIL_ALLOC=1)");
+        Entry ent;
+        ent.bytes = type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out) : q4k_plane_bytes(n_in, n_out);
+        e = hipMalloc(&ent.buf, (size_t)ent.bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(QDEC_ENOMEM, "hipMalloc(%lld bytes) for a repacked copy: %s",
+                        (long long)ent.bytes, hipGetErrorString(e));
+        }
+        e = type == QDEC_TYPE_Q8_0
+                ? launch_repack_q8_0(static_cast<const uint8_t*>(w), n_in, n_out, ent.buf, s)
+                : launch_repack_q4k(static_cast<const uint8_t*>(w), n_in, n_out, ent.buf, s);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ent.ready, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventRecord(ent.ready, s);
+        if (e != hipSuccess) {
+            destroy(ent);
+            return hip_fail(e, "repack launch");
+        }
+        ent.made_on = s;
+        it = g_cache.emplace(key, ent).first;
+    }
+    Entry& ent = it->second;
+    if (!ent.done) {
+        if (hipEventQuery(ent.ready) == hipSuccess) {
+            ent.done = true;
+        } else if (s != ent.made_on) {
+            e = hipStreamWaitEvent(s, ent.ready, 0);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        }
+    }
+    *out = ent.buf;
+    return QDEC_OK;
+}
+
+// ------------------------------------------------------------ validation --
+
+int check_dims(const char* fn, int64_t n_in, int64_t n_out, int64_t batch, int64_t kmult,
+               int64_t max_batch)
+{
+    if (n_in <= 0 || n_out <= 0) return fail(QDEC_EINVAL, "%s: n_in=%lld n_out=%lld must be > 0", fn, (long long)n_in, (long long)n_out);
+    if (n_in % kmult != 0) return fail(QDEC_EINVAL, "%s: n_in=%lld is not a multiple of %lld", fn, (long long)n_in, (long long)kmult);
+    if (batch < 1 || (max_batch > 0 && batch > max_batch))
+        return fail(QDEC_EINVAL, "%s: batch=%lld outside [1, %lld]", fn, (long long)batch, (long long)(max_batch > 0 ? max_batch : INT32_MAX));
+    if (batch > INT32_MAX || n_in > INT32_MAX / 2 || n_out > INT32_MAX)
+        return fail(QDEC_EINVAL, "%s: dimension too large", fn);
+    return QDEC_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, uintptr_t align)
+{
+    if (!p) return fail(QDEC_EINVAL, "%s: %s is NULL", fn, name);
+    if (!aligned(p, align)) return fail(QDEC_EINVAL, "%s: %s is not %u-byte aligned", fn, name, (unsigned)align);
+    return QDEC_OK;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)bbytes && pb < pa + (uintptr_t)abytes;
+}
+
+#define QDEC_TRY(expr)                 \
+    do {                               \
+        const int _rc = (expr);        \
+        if (_rc != QDEC_OK) return _rc; \
+    } while (0)
+
+int finish(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return hip_fail(e, what);
+    return QDEC_OK;
+}
+
+int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw, int64_t n_in,
+                   const int64_t* rows, int64_t batch, const float* x, const float* residual,
+                   float* const* outs, int nout, hipStream_t s)
+{
+    for (int k = 0; k < nw; ++k) QDEC_TRY(check_ptr(fn, "weight", ws[k], 2));
+    QDEC_TRY(check_ptr(fn, "x", x, 16));
+    for (int k = 0; k < nout; ++k) {
+        QDEC_TRY(check_ptr(fn, "out", outs[k], 4));
+        if (overlaps(outs[k], batch * rows[k] * 4, x, batch * n_in * 4))
+            return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
+    }
+    if (mode == kResidual) QDEC_TRY(check_ptr(fn, "residual", residual, 4));
+    Q8GemvProblem p{};
+    p.mode = mode;
+    p.nseg = nw;
+    for (int k = 0; k < nw; ++k) {
+        const void* buf = nullptr;
+        QDEC_TRY(repacked(ws[k], QDEC_TYPE_Q8_0, n_in, rows[k], s, &buf));
+        p.w[k] = q8_view(buf, n_in, rows[k]);
+        p.rows[k] = rows[k];
+        p.out[k] = outs[k < nout ? k : 0];
+    }
+    p.x = x;
+    p.residual = residual;
+    p.n_in = n_in;
+    p.batch = batch;
+    return finish(launch_q8_0_gemv(p, s), fn);
+}
+
+}  // namespace
+
+void count_launch(uint64_t n) { g_launches.fetch_add(n, std::memory_order_relaxed); }
+
+int device_cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+}  // namespace qdec
+
+using namespace qdec;
+
+extern "C" {
+
+int q8_0_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
+              hipStream_t stream)
+{
+    QDEC_TRY(check_dims("q8_0_gemv", n_in, n_out, batch, 32, QDEC_GEMV_MAX_BATCH));
+    const void* ws[1] = {w};
+    const int64_t rows[1] = {n_out};
+    float* outs[1] = {out};
+    return q8_gemv_common(kPlain, "q8_0_gemv", ws, 1, n_in, rows, batch, x, nullptr, outs, 1, stream);
+}
+
+int q8_0_gemv_residual(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
+                       const float* residual, float* out, hipStream_t stream)
+{
+    QDEC_TRY(check_dims("q8_0_gemv_residual", n_in, n_out, batch, 32, QDEC_GEMV_MAX_BATCH));
+    if (residual != out && residual && out && overlaps(residual, batch * n_out * 4, out, batch * n_out * 4))
+        return fail(QDEC_EINVAL, "q8_0_gemv_residual: residual partially overlaps out");
+    const void* ws[1] = {w};
+    const int64_t rows[1] = {n_out};
+    float* outs[1] = {out};
+    return q8_gemv_common(kResidual, "q8_0_gemv_residual", ws, 1, n_in, rows, batch, x, residual,
+                          outs, 1, stream);
+}
+
+int q8_0_qkv(const void* wq, const void* wk, const void* wv, int64_t n_in, int64_t n_q,
+             int64_t n_kv, int64_t batch, const float* x, float* q_out, float* k_out, float* v_out,
+             hipStream_t stream)
+{
+    QDEC_TRY(check_dims("q8_0_qkv", n_in, n_q, batch, 32, QDEC_GEMV_MAX_BATCH));
+    if (n_kv < 1 || n_kv > n_q) return fail(QDEC_EINVAL, "q8_0_qkv: n_kv=%lld must be in [1, n_q=%lld]", (long long)n_kv, (long long)n_q);
+    if (q_out && k_out && v_out &&
+        (overlaps(q_out, batch * n_q * 4, k_out, batch * n_kv * 4) ||
+         overlaps(q_out, batch * n_q * 4, v_out, batch * n_kv * 4) ||
+         overlaps(k_out, batch * n_kv * 4, v_out, batch * n_kv * 4)))
+        return fail(QDEC_EINVAL, "q8_0_qkv: output buffers overlap");
+    const void* ws[3] = {wq, wk, wv};
+    const int64_t rows[3] = {n_q, n_kv, n_kv};
+    float* outs[3] = {q_out, k_out, v_out};
+    return q8_gemv_common(kQKV, "q8_0_qkv", ws, 3, n_in, rows, batch, x, nullptr, outs, 3, stream);
+}
+
+int q8_0_swiglu(const void* w_gate, const void* w_up, int64_t n_in, int64_t n_out, int64_t batch,
+                const float* x, float* out, hipStream_t stream)
+{
+    QDEC_TRY(check_dims("q8_0_swiglu", n_in, n_out, batch, 32, QDEC_GEMV_MAX_BATCH));
+    const void* ws[2] = {w_gate, w_up};
+    const int64_t rows[2] = {n_out, n_out};
+    float* outs[1] = {out};
+    return q8_gemv_common(kSwiGLU, "q8_0_swiglu", ws, 2, n_in, rows, batch, x, nullptr, outs, 1,
+                          stream);
+}
+
+int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
+             hipStream_t stream)
+{
+    const char* fn = "q4k_gemv";
+    QDEC_TRY(check_dims(fn, n_in, n_out, batch, 256, QDEC_GEMV_MAX_BATCH));
+    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    QDEC_TRY(check_ptr(fn, "x", x, 16));
+    QDEC_TRY(check_ptr(fn, "out", out, 4));
+    if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4)) return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
+    const void* buf = nullptr;
+    QDEC_TRY(repacked(w, QDEC_TYPE_Q4_K, n_in, n_out, stream, &buf));
+    return finish(launch_q4k_gemv(q4k_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
+}
+
+int q8_0_gemm_batched(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
+                      float* out, hipStream_t stream)
+{
+    const char* fn = "q8_0_gemm_batched";
+    QDEC_TRY(check_dims(fn, n_in, n_out, batch, 32, 0));
+    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    QDEC_TRY(check_ptr(fn, "x", x, 16));
+    QDEC_TRY(check_ptr(fn, "out", out, 4));
+    if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4)) return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
+    const void* buf = nullptr;
+    QDEC_TRY(repacked(w, QDEC_TYPE_Q8_0, n_in, n_out, stream, &buf));
+    return finish(launch_q8_0_gemm(q8_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
+}
+
+int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
+                     float* out, hipStream_t stream)
+{
+    const char* fn = "f32_gemm_batched";
+    QDEC_TRY(check_dims(fn, n_in, n_out, batch, 32, 0));
+    QDEC_TRY(check_ptr(fn, "weight", w, 16));
+    QDEC_TRY(check_ptr(fn, "x", x, 16));
+    QDEC_TRY(check_ptr(fn, "out", out, 4));
+    if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4) ||
+        overlaps(out, batch * n_out * 4, w, n_out * n_in * 4))
+        return fail(QDEC_EINVAL, "%s: out overlaps an input", fn);
+    return finish(launch_f32_gemm(w, n_in, n_out, batch, x, out, stream), fn);
+}
+
+int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream)
+{
+    const char* fn = "qdec_prepare";
+    if (type != QDEC_TYPE_Q8_0 && type != QDEC_TYPE_Q4_K) return fail(QDEC_EINVAL, "%s: unknown type %d", fn, type);
+    QDEC_TRY(check_dims(fn, n_in, n_out, 1, type == QDEC_TYPE_Q8_0 ? 32 : 256, 0));
+    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    const void* buf = nullptr;
+    return repacked(w, type, n_in, n_out, stream, &buf);
+}
+
+int qdec_release(const void* w)
+{
+    int dev = 0;
+    if (!w) return fail(QDEC_EINVAL, "qdec_release: w is NULL");
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    int n = 0;
+    for (auto it = g_cache.begin(); it != g_cache.end();) {
+        if (it->first.dev == dev && it->first.ptr == reinterpret_cast<uintptr_t>(w)) {
+            (void)hipDeviceSynchronize();
+            destroy(it->second);
+            it = g_cache.erase(it);
+            ++n;
+        } else {
+            ++it;
+        }
+    }
+    return n ? QDEC_OK : fail(QDEC_EINVAL, "qdec_release: no repacked copy of %p", w);
+}
+
+void qdec_clear_cache(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cur = 0;
+    const bool have_dev = hipGetDevice(&cur) == hipSuccess;
+    for (auto& kv : g_cache) {
+        if (have_dev) (void)hipSetDevice(kv.first.dev);
+        (void)hipDeviceSynchronize();
+        destroy(kv.second);
+    }
+    g_cache.clear();
+    if (have_dev) (void)hipSetDevice(cur);
+}
+
+int64_t qdec_cache_len(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    return (int64_t)g_cache.size();
+}
+
+int q8_0_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream)
+{
+    const char* fn = "q8_0_dequantize";
+    QDEC_TRY(check_dims(fn, n_in, n_out, 1, 32, 0));
+    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    QDEC_TRY(check_ptr(fn, "out", out, 16));
+    const void* buf = nullptr;
+    QDEC_TRY(repacked(w, QDEC_TYPE_Q8_0, n_in, n_out, stream, &buf));
+    return finish(launch_dequant_q8_0(q8_view(buf, n_in, n_out), n_in, n_out, out, stream), fn);
+}
+
+int q4k_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream)
+{
+    const char* fn = "q4k_dequantize";
+    QDEC_TRY(check_dims(fn, n_in, n_out, 1, 256, 0));
+    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    QDEC_TRY(check_ptr(fn, "out", out, 16));
+    const void* buf = nullptr;
+    QDEC_TRY(repacked(w, QDEC_TYPE_Q4_K, n_in, n_out, stream, &buf));
+    return finish(launch_dequant_q4k(q4k_view(buf, n_in, n_out), n_in, n_out, out, stream), fn);
+}
+
+const char* qdec_last_error(void) { return t_error.c_str(); }
+
+uint64_t qdec_launch_count(void) { return g_launches.load(std::memory_order_relaxed); }
+
+int qdec_empty_kernel(hipStream_t stream) { return finish(launch_empty(stream), "qdec_empty_kernel"); }
+
+int qdec_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream)
+{
+    const char* fn = "qdec_copy";
+    if (bytes <= 0 || bytes % 16 != 0) return fail(QDEC_EINVAL, "%s: bytes=%lld must be a positive multiple of 16", fn, (long long)bytes);
+    QDEC_TRY(check_ptr(fn, "dst", dst, 16));
+    QDEC_TRY(check_ptr(fn, "src", src, 16));
+    if (overlaps(dst, bytes, src, bytes)) return fail(QDEC_EINVAL, "%s: buffers overlap", fn);
+    return finish(launch_copy(dst, src, bytes, stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,490 @@
+// Q8_0 dequant-GEMV family for gfx950: plain, residual epilogue, fused QKV
+// (GQA) and fused SwiGLU, batch 1..8.
+//
+// What is computed (rustdoc "Module cuda_lane", Functions section):
+//   try_q8_0_cuda_gemv / q8_0_gemv_oracle_into : out[b][i] = sum_j (d*q)[i][j] x[b][j]
+//   try_q4k_soa_ffn_block_residual             : out = residual + W x
+//   try_q4k_soa_qkv                            : q, k, v from one shared x;
+//                                                K and V have n_kv rows
+//   try_q4k_soa_fused_swiglu                   : out[i] = silu(gate_i.x) * (up_i.x)
+//
+// The weights are read exactly once, so every variant is bound by HBM; the
+// design keeps the whole weight stream of a workgroup in flight from its first
+// instructions and finishes each output row inside one workgroup (device-wide
+// reductions would need cross-XCD fences, which cost more than the kernel).
+//
+// Fast path (n_in a multiple of 1024, chunks per row NCH = n_in/1024 in
+// {1,2,3,4,6,8,12,16}): a row's 16-byte chunks are split over the 64 lanes of a
+// wave (lane j takes chunks j, j+64, ...) and over KS waves of the workgroup
+// (each takes CH = NCH/KS consecutive chunk columns).  A wave computes R rows
+// (x 2 matrices for SwiGLU) at once, so each x value in registers serves R
+// rows.  Per wave the order is: x of its columns (registers), every fp16 scale,
+// every q chunk, then the arithmetic, so the loads return in use order while
+// later ones are still in flight.  Lane sums are folded with DPP row
+// operations and lane reads into scalar registers (no LDS), the KS wave
+// partials through LDS.
+//
+// General path (other n_in): rows are split over "row groups" of LPR lanes
+// (LPR = largest power of two not above the chunk count), with a bounds-checked
+// chunk loop and shuffle reductions.
+//
+// Arithmetic per chunk: t = sum of 16 products q*x (f32 FMA chain), then
+// acc = fma(d, t, acc), then the lane tree.  The longest rounding chain is
+// 16 + NCH + 6 + 2 operations (32 at n_in = 8192), so
+// |err| <= 33 * 2^-24 * sum_j|w x| < 2e-6 * sum_j|w x|, inside the 1e-5 bound.
+#include "qdec_internal.h"
+
+namespace qdec {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float fp16_bits_to_f32(uint16_t h)
+{
+    _Float16 v;
+    __builtin_memcpy(&v, &h, sizeof v);
+    return static_cast<float>(v);
+}
+
+struct Q8GemvArgs {
+    // Segment 1 and 2 are addressed as element offsets from segment 0, and a
+    // row picks its segment with 0/1 multipliers: selecting between argument
+    // fields would make the compiler copy the arguments to scratch memory.
+    const int8_t* q0;
+    const uint16_t* d0;
+    float* out0;
+    int64_t dq1, dq2;      // q plane offsets (bytes) of segments 1, 2
+    int64_t dd1, dd2;      // d plane offsets (elements)
+    int64_t dout1, dout2;  // output offsets (elements)
+    int64_t end0, end1;    // flat row where segment 1 and segment 2 start
+    int64_t rows0, rows1, rows2;
+    const float* x;
+    const float* residual;
+    int64_t n_in;
+    int64_t total_rows;   // flat rows (output rows for SwiGLU)
+    int batch;
+    int lpr_log2;         // general path: lanes per row group = 1 << lpr_log2
+    int nch;              // 16-byte chunks per row = n_in / 16
+};
+
+__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Sum of 16 products of the int8 weights in `qv` with x[0..15].
+__device__ inline float dot16(const uint4& qv, const float* x)
+{
+    const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
+    float t = (float)(int8_t)(w[0] & 0xff) * x[0];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int b = (k == 0 ? 1 : 0); b < 4; ++b)
+            t = __builtin_fmaf((float)(int8_t)((w[k] >> (8 * b)) & 0xff), x[4 * k + b], t);
+    }
+    return t;
+}
+
+// Weight bytes are read once per launch: non-temporal loads keep them from
+// displacing x and the outputs in the caches.
+__device__ inline uint4 stream_load16(const int8_t* p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline uint16_t stream_load2(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
+__device__ inline void load_x16(const float* p, float (&xv)[16])
+{
+    const float4* xp = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float4 v = xp[k];
+        xv[4 * k] = v.x; xv[4 * k + 1] = v.y; xv[4 * k + 2] = v.z; xv[4 * k + 3] = v.w;
+    }
+}
+
+template <int CTRL>
+__device__ inline float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave, result in every lane: rotations and quad
+// permutes within each 16-lane row (DPP), then the four row sums read into
+// scalar registers.  (The gfx950 permlane swaps would need two distinct copies
+// of the value; the compiler merges equal operands into one register.)
+__device__ inline float wave_sum(float v)
+{
+    v += dpp<0x128>(v);  // row_ror:8
+    v += dpp<0x124>(v);  // row_ror:4
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Weight planes of one flat row (matrix m of SwiGLU).
+struct Seg {
+    const int8_t* q;
+    const uint16_t* d;
+};
+
+template <int MODE>
+__device__ inline Seg row_seg(const Q8GemvArgs& a, int64_t rr, int m)
+{
+    const int64_t nb = a.n_in >> 5;
+    if constexpr (MODE == kSwiGLU) {
+        return Seg{a.q0 + m * a.dq1 + rr * a.n_in, a.d0 + m * a.dd1 + rr * nb};
+    } else if constexpr (MODE == kQKV) {
+        const int64_t s1 = rr >= a.end0, s2 = rr >= a.end1;   // 0 or 1
+        const int64_t seg1 = s1 - s2;                         // 1 in segment 1 only
+        const int64_t local = rr - s1 * a.end0 - s2 * (a.end1 - a.end0);
+        return Seg{a.q0 + seg1 * a.dq1 + s2 * a.dq2 + local * a.n_in,
+                   a.d0 + seg1 * a.dd1 + s2 * a.dd2 + local * nb};
+    } else {
+        (void)m;
+        return Seg{a.q0 + rr * a.n_in, a.d0 + rr * nb};
+    }
+}
+
+// Final value of output row `rw`, batch row b (v1 is the up product of SwiGLU).
+template <int MODE>
+__device__ inline void store_row(const Q8GemvArgs& a, int64_t rw, int b, float v0, float v1)
+{
+    if constexpr (MODE == kPlain) {
+        a.out0[(int64_t)b * a.total_rows + rw] = v0;
+    } else if constexpr (MODE == kResidual) {
+        const int64_t o = (int64_t)b * a.total_rows + rw;
+        a.out0[o] = a.residual[o] + v0;
+    } else if constexpr (MODE == kQKV) {
+        const int64_t s1 = rw >= a.end0, s2 = rw >= a.end1;
+        const int64_t seg1 = s1 - s2;
+        const int64_t local = rw - s1 * a.end0 - s2 * (a.end1 - a.end0);
+        const int64_t rows = a.rows0 + seg1 * (a.rows1 - a.rows0) + s2 * (a.rows2 - a.rows0);
+        a.out0[seg1 * a.dout1 + s2 * a.dout2 + (int64_t)b * rows + local] = v0;
+    } else {
+        a.out0[(int64_t)b * a.total_rows + rw] = silu(v0) * v1;
+    }
+}
+
+// Fast path.  MODE: GemvMode.  B: batch rows handled (>= the real batch;
+// padding rows use the last real x row and are never stored).  R: rows per
+// wave.  CH: chunk columns per lane in this wave.  KS: waves per row group.
+template <int MODE, int B, int R, int CH, int KS>
+__global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
+{
+    constexpr int NM = (MODE == kSwiGLU) ? 2 : 1;   // weight matrices per output row
+    constexpr int GROUPS = 4 / KS;                   // row groups per workgroup
+    constexpr bool XREG = B * CH <= 4;               // x in registers (<= 64 VGPRs)
+    __shared__ float part[KS > 1 ? 4 : 1][R][NM][B];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = w / KS, ks = w % KS;
+    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * R;
+    const int cbase = ks * CH;                       // first chunk column of this wave
+
+    const float* xrow[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) xrow[b] = a.x + (int64_t)(b < a.batch ? b : a.batch - 1) * a.n_in;
+
+    float xr[XREG ? CH : 1][XREG ? B : 1][16];
+    if constexpr (XREG) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+#pragma unroll
+            for (int b = 0; b < B; ++b) load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xr[k][b]);
+    }
+
+    Seg sg[R][NM];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t rw = row0 + r;
+        const int64_t rr = rw < a.total_rows ? rw : a.total_rows - 1;  // keep loads in bounds
+#pragma unroll
+        for (int m = 0; m < NM; ++m) sg[r][m] = row_seg<MODE>(a, rr, m);
+    }
+    uint16_t dv[CH][R][NM];
+    uint4 qv[CH][R][NM];
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) dv[k][r][m] = stream_load2(sg[r][m].d + ((lane + 64 * (cbase + k)) >> 1));
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                qv[k][r][m] = stream_load16(sg[r][m].q + (int64_t)(lane + 64 * (cbase + k)) * 16);
+    // The weight loads must stay ahead of the arithmetic (the weight planes
+    // are not marked restrict, so this fence pins them).
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    float acc[R][NM][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][m][b] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float xv[16];
+            if constexpr (XREG) {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) xv[t] = xr[XREG ? k : 0][XREG ? b : 0][t];
+            } else {
+                load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xv);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    acc[r][m][b] = __builtin_fmaf(fp16_bits_to_f32(dv[k][r][m]), dot16(qv[k][r][m], xv),
+                                                  acc[r][m][b]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][m][b] = wave_sum(acc[r][m][b]);
+
+    if constexpr (KS > 1) {
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) part[w][r][m][b] = acc[r][m][b];
+        }
+        __syncthreads();
+        if (ks != 0) return;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    float v = part[w][r][m][b];
+#pragma unroll
+                    for (int k = 1; k < KS; ++k) v += part[w + k][r][m][b];
+                    acc[r][m][b] = v;
+                }
+    }
+    // lane r*B + b stores the (row r, batch b) value
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (lane == r * B + b && b < a.batch && row0 + r < a.total_rows)
+                store_row<MODE>(a, row0 + r, b, acc[r][0][b], acc[r][NM - 1][b]);
+        }
+}
+
+// General path: row groups of LPR lanes, one row per group, bounds-checked loop.
+template <int MODE, int B>
+__global__ __launch_bounds__(256) void q8_0_gemv_general(Q8GemvArgs a)
+{
+    constexpr int NM = (MODE == kSwiGLU) ? 2 : 1;
+    const int lpr = 1 << a.lpr_log2;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> a.lpr_log2;
+    const int j = lane & (lpr - 1);
+    const int groups = 64 >> a.lpr_log2;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+
+    const float* xrow[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) xrow[b] = a.x + (int64_t)(b < a.batch ? b : a.batch - 1) * a.n_in;
+
+    const int64_t row = wave * groups + g;
+    const int64_t rr = row < a.total_rows ? row : a.total_rows - 1;
+    Seg sg[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) sg[m] = row_seg<MODE>(a, rr, m);
+    float acc[NM][B];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+    for (int c = j; c < a.nch; c += lpr) {
+        uint4 qv[NM];
+        uint16_t dv[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            dv[m] = stream_load2(sg[m].d + (c >> 1));
+            qv[m] = stream_load16(sg[m].q + (int64_t)c * 16);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float xv[16];
+            load_x16(xrow[b] + (int64_t)c * 16, xv);
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                acc[m][b] = __builtin_fmaf(fp16_bits_to_f32(dv[m]), dot16(qv[m], xv), acc[m][b]);
+        }
+    }
+    for (int off = lpr >> 1; off > 0; off >>= 1) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[m][b] += __shfl_xor(acc[m][b], off);
+    }
+    if (j != 0 || row >= a.total_rows) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+        if (b < a.batch) store_row<MODE>(a, row, b, acc[0][b], acc[NM - 1][b]);
+}
+
+using KernelFn = void (*)(Q8GemvArgs);
+
+// Fast-path instantiations: (CH, KS) from the chunk count per row; R from the
+// row count; B from the batch.  Register use grows with R*NM*B, so wide
+// batches and SwiGLU take fewer rows per wave.
+template <int MODE, int B, int R>
+KernelFn pick_split(int nch64)
+{
+    switch (nch64) {
+        case 1: return q8_0_gemv_fast<MODE, B, R, 1, 1>;
+        case 2: return q8_0_gemv_fast<MODE, B, R, 2, 1>;
+        case 3: return q8_0_gemv_fast<MODE, B, R, 3, 1>;
+        case 4: return q8_0_gemv_fast<MODE, B, R, 2, 2>;
+        case 6: return q8_0_gemv_fast<MODE, B, R, 3, 2>;
+        case 8: return q8_0_gemv_fast<MODE, B, R, 2, 4>;
+        case 12: return q8_0_gemv_fast<MODE, B, R, 3, 4>;
+        case 16: return q8_0_gemv_fast<MODE, B, R, 4, 4>;
+        default: return nullptr;
+    }
+}
+
+int split_ks(int nch64) { return nch64 <= 3 ? 1 : (nch64 <= 6 ? 2 : 4); }
+
+// R actually instantiated for (mode, bt, requested r).
+int fast_r(GemvMode mode, int bt, int r)
+{
+    if (mode == kSwiGLU) return bt == 1 ? (r >= 2 ? 2 : 1) : 1;
+    if (bt == 1) return r;
+    if (bt == 8) return 1;
+    return r >= 2 ? 2 : 1;
+}
+
+template <int MODE>
+KernelFn pick_fast(int bt, int r, int nch64)
+{
+    if constexpr (MODE == kSwiGLU) {
+        switch (bt) {
+            case 1: return r >= 2 ? pick_split<MODE, 1, 2>(nch64) : pick_split<MODE, 1, 1>(nch64);
+            case 2: return pick_split<MODE, 2, 1>(nch64);
+            case 4: return pick_split<MODE, 4, 1>(nch64);
+            default: return pick_split<MODE, 8, 1>(nch64);
+        }
+    } else {
+        switch (bt) {
+            case 1: return r == 4 ? pick_split<MODE, 1, 4>(nch64)
+                                  : (r == 2 ? pick_split<MODE, 1, 2>(nch64) : pick_split<MODE, 1, 1>(nch64));
+            case 2: return r >= 2 ? pick_split<MODE, 2, 2>(nch64) : pick_split<MODE, 2, 1>(nch64);
+            case 4: return r >= 2 ? pick_split<MODE, 4, 2>(nch64) : pick_split<MODE, 4, 1>(nch64);
+            default: return pick_split<MODE, 8, 1>(nch64);
+        }
+    }
+}
+
+template <int MODE>
+KernelFn pick_general(int bt)
+{
+    switch (bt) {
+        case 1: return q8_0_gemv_general<MODE, 1>;
+        case 2: return q8_0_gemv_general<MODE, 2>;
+        case 4: return q8_0_gemv_general<MODE, 4>;
+        default: return q8_0_gemv_general<MODE, 8>;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
+{
+    Q8GemvArgs a{};
+    const int last = p.nseg - 1;
+    const int s1 = last < 1 ? last : 1;
+    a.q0 = p.w[0].q;
+    a.d0 = p.w[0].d;
+    a.out0 = p.out[0];
+    // byte distances between independent allocations, in elements of each type
+    auto dist = [](const void* from, const void* to, int64_t elem) {
+        return (int64_t)(reinterpret_cast<uintptr_t>(to) - reinterpret_cast<uintptr_t>(from)) / elem;
+    };
+    a.dq1 = dist(p.w[0].q, p.w[s1].q, 1);
+    a.dq2 = dist(p.w[0].q, p.w[last].q, 1);
+    a.dd1 = dist(p.w[0].d, p.w[s1].d, 2);
+    a.dd2 = dist(p.w[0].d, p.w[last].d, 2);
+    a.dout1 = dist(p.out[0], p.out[s1], 4);
+    a.dout2 = dist(p.out[0], p.out[last], 4);
+    a.rows0 = p.rows[0];
+    a.rows1 = p.rows[s1];
+    a.rows2 = p.rows[last];
+    int64_t end = 0;
+    for (int k = 0; k < p.nseg; ++k) end += p.rows[k];
+    a.end0 = p.rows[0];
+    a.end1 = p.nseg > 1 ? p.rows[0] + p.rows[1] : p.rows[0];
+    a.x = p.x;
+    a.residual = p.residual;
+    a.n_in = p.n_in;
+    a.total_rows = p.mode == kSwiGLU ? p.rows[0] : end;
+    a.batch = (int)p.batch;
+    a.nch = (int)(p.n_in / 16);
+
+    // Batch rounds up to 1, 2, 4 or 8 (padding rows are never stored).
+    const int bt = a.batch <= 1 ? 1 : a.batch <= 2 ? 2 : a.batch <= 4 ? 4 : 8;
+    const int nch64 = a.nch % 64 == 0 ? a.nch / 64 : 0;
+    KernelFn fn = nullptr;
+    int64_t blocks = 0;
+    if (nch64 > 0) {
+        const int ks = split_ks(nch64);
+        const int groups = 4 / ks;
+        // largest R in {4, 2, 1} that still gives >= 512 workgroups
+        int r = 4;
+        while (r > 1 && a.total_rows / ((int64_t)groups * r) < 512) r >>= 1;
+        switch (p.mode) {
+            case kPlain: fn = pick_fast<kPlain>(bt, r, nch64); break;
+            case kResidual: fn = pick_fast<kResidual>(bt, r, nch64); break;
+            case kQKV: fn = pick_fast<kQKV>(bt, r, nch64); break;
+            default: fn = pick_fast<kSwiGLU>(bt, r, nch64); break;
+        }
+        const int64_t rows_per_block = (int64_t)groups * fast_r(p.mode, bt, r);
+        blocks = (a.total_rows + rows_per_block - 1) / rows_per_block;
+    }
+    if (!fn) {
+        int lpr_log2 = 6;
+        while (lpr_log2 > 1 && (1 << lpr_log2) > a.nch) --lpr_log2;
+        a.lpr_log2 = lpr_log2;
+        switch (p.mode) {
+            case kPlain: fn = pick_general<kPlain>(bt); break;
+            case kResidual: fn = pick_general<kResidual>(bt); break;
+            case kQKV: fn = pick_general<kQKV>(bt); break;
+            default: fn = pick_general<kSwiGLU>(bt); break;
+        }
+        const int64_t rows_per_wave = 64 >> lpr_log2;
+        const int64_t waves = (a.total_rows + rows_per_wave - 1) / rows_per_wave;
+        blocks = (waves + 3) / 4;
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    count_launch();
+    return hipGetLastError();
+}
+
+}  // namespace qdec

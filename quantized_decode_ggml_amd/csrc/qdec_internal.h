@@ -1,0 +1,108 @@
+// Internal declarations shared by the libqdec translation units (host and
+// device).  Not installed; the public ABI is include/qdec.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qdec {
+
+// ---------------------------------------------------------------- layouts --
+//
+// Repacked Q8_0 matrix (one device allocation, 256-byte aligned planes):
+//   q plane : n_out rows x n_in int8, row stride n_in bytes.  Row i's chunk c
+//             (16 bytes, weights 16c..16c+15) is one aligned 16-byte load.
+//   d plane : n_out rows x (n_in/32) fp16 scale bits, row stride n_in/32.
+// Total bytes = n_out*n_in*17/16 (the GGML size) plus plane alignment.
+//
+// Repacked Q4_K matrix:
+//   qs plane   : n_out rows x n_in/2 bytes of nibbles, in GGML order within each
+//                super-block (128 bytes per super-block).
+//   meta plane : n_out rows x (n_in/256) 16-byte headers = the first 16 bytes of
+//                the GGML super-block (fp16 d, fp16 dmin, 12 packed scale bytes).
+struct Q8View {
+    const int8_t* q;
+    const uint16_t* d;
+};
+
+struct Q4KView {
+    const uint8_t* qs;
+    const uint4* meta;
+};
+
+constexpr int64_t kAlign = 256;
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+inline int64_t q8_plane_bytes(int64_t n_in, int64_t n_out)
+{
+    return align_up(n_out * n_in, kAlign) + align_up(n_out * (n_in / 32) * 2, kAlign);
+}
+
+inline Q8View q8_view(const void* base, int64_t n_in, int64_t n_out)
+{
+    const char* p = static_cast<const char*>(base);
+    return Q8View{reinterpret_cast<const int8_t*>(p),
+                  reinterpret_cast<const uint16_t*>(p + align_up(n_out * n_in, kAlign))};
+}
+
+inline int64_t q4k_plane_bytes(int64_t n_in, int64_t n_out)
+{
+    return align_up(n_out * (n_in / 2), kAlign) + align_up(n_out * (n_in / 256) * 16, kAlign);
+}
+
+inline Q4KView q4k_view(const void* base, int64_t n_in, int64_t n_out)
+{
+    const char* p = static_cast<const char*>(base);
+    return Q4KView{reinterpret_cast<const uint8_t*>(p),
+                   reinterpret_cast<const uint4*>(p + align_up(n_out * (n_in / 2), kAlign))};
+}
+
+// ------------------------------------------------------------- launchers --
+// Each returns the hipError_t of its launch (hipGetLastError after launch).
+// Arguments are validated by the caller (api.hip).
+
+hipError_t launch_repack_q8_0(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
+                              hipStream_t s);
+hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
+                             hipStream_t s);
+hipError_t launch_dequant_q8_0(Q8View w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
+hipError_t launch_dequant_q4k(Q4KView w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
+
+enum GemvMode { kPlain = 0, kResidual = 1, kQKV = 2, kSwiGLU = 3 };
+
+// Up to three row segments share one launch (QKV); SwiGLU uses segment 0 as
+// gate and segment 1 as up, with the same rows.
+struct Q8GemvProblem {
+    GemvMode mode;
+    int nseg;
+    Q8View w[3];
+    int64_t rows[3];
+    float* out[3];
+    const float* x;
+    const float* residual;
+    int64_t n_in;
+    int64_t batch;
+};
+
+hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s);
+
+hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
+                           float* out, hipStream_t s);
+
+hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
+                            float* out, hipStream_t s);
+hipError_t launch_f32_gemm(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
+                           const float* x, float* out, hipStream_t s);
+
+hipError_t launch_empty(hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// Kernel-launch counter (a witness that the device path ran).
+void count_launch(uint64_t n = 1);
+
+}  // namespace qdec

@@ -1,0 +1,226 @@
+// Load-time repack of GGML blocks into the aligned plane layouts, the
+// bit-exact dequantisation exports, and two diagnostic kernels.
+//
+// Block layouts (the workload definitions that accompany the rustdoc
+// "Module cuda_lane" page; its Constants section names Q8_0_BLOCK_BYTES and
+// Q8_0_BLOCK_ELEMS):
+//   Q8_0 block, 34 bytes : fp16 d | int8 q[32]             w = d*q
+//   Q4_K block, 144 bytes: fp16 d | fp16 dmin | 12 scale bytes | 128 nibble bytes
+//                                                          w = d*sc*q - dmin*m
+// The repack ("call once at plan build", preload_q4k_soa_weights on that page)
+// only moves bytes: the q bytes and nibbles go to one plane, the per-block
+// headers to another, so every row starts on a 16-byte boundary and the hot
+// kernels read each row with aligned 16-byte loads.
+#include "qdec_internal.h"
+
+namespace qdec {
+
+namespace {
+
+constexpr int kQ8Bytes = 34;
+constexpr int kQ4KBytes = 144;
+
+__device__ inline float fp16_bits_to_f32(uint16_t h)
+{
+    _Float16 v;
+    __builtin_memcpy(&v, &h, sizeof v);
+    return static_cast<float>(v);
+}
+
+// One thread per Q8_0 block.  The raw blocks are 2-byte aligned (34 is even),
+// so they are read as 17 halfwords.
+__global__ __launch_bounds__(256) void repack_q8_0_kernel(const uint16_t* __restrict__ raw,
+                                                          int64_t nblocks, int64_t nb_row,
+                                                          int64_t n_in, int8_t* __restrict__ qp,
+                                                          uint16_t* __restrict__ dp)
+{
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= nblocks) return;
+    const uint16_t* src = raw + blk * (kQ8Bytes / 2);
+    uint32_t words[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        words[k] = (uint32_t)src[1 + 2 * k] | ((uint32_t)src[2 + 2 * k] << 16);
+    const int64_t row = blk / nb_row;
+    const int64_t kb = blk % nb_row;
+    uint4* dst = reinterpret_cast<uint4*>(qp + row * n_in + kb * 32);
+    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    dp[blk] = src[0];
+}
+
+// One thread per Q4_K super-block (72 halfwords).
+__global__ __launch_bounds__(256) void repack_q4k_kernel(const uint16_t* __restrict__ raw,
+                                                         int64_t nblocks,
+                                                         uint8_t* __restrict__ qsp,
+                                                         uint4* __restrict__ meta)
+{
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= nblocks) return;
+    const uint16_t* src = raw + blk * (kQ4KBytes / 2);
+    uint32_t words[36];
+#pragma unroll
+    for (int k = 0; k < 36; ++k)
+        words[k] = (uint32_t)src[2 * k] | ((uint32_t)src[2 * k + 1] << 16);
+    meta[blk] = make_uint4(words[0], words[1], words[2], words[3]);
+    // n_in/2 bytes per row and 128 per super-block: super-block blk's nibbles
+    // land at byte blk*128 of the qs plane.
+    uint4* dst = reinterpret_cast<uint4*>(qsp + blk * 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        dst[k] = make_uint4(words[4 + 4 * k], words[5 + 4 * k], words[6 + 4 * k], words[7 + 4 * k]);
+}
+
+// One thread per 16 weights of the repacked Q8_0 matrix.
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(Q8View w, int64_t n_in, int64_t nchunks,
+                                                           float* __restrict__ out)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= nchunks) return;
+    const uint4 qv = *reinterpret_cast<const uint4*>(w.q + c * 16);
+    // chunk c covers weights 16c..16c+15 of the flattened matrix; its block
+    // is (16c)/32 because n_in is a multiple of 32.
+    const float d = fp16_bits_to_f32(w.d[c >> 1]);
+    const uint32_t words[4] = {qv.x, qv.y, qv.z, qv.w};
+    float4* o = reinterpret_cast<float4*>(out + c * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t v = words[k];
+        o[k] = make_float4(d * (float)(int8_t)(v & 0xff), d * (float)(int8_t)((v >> 8) & 0xff),
+                           d * (float)(int8_t)((v >> 16) & 0xff), d * (float)(int8_t)(v >> 24));
+    }
+    (void)n_in;
+}
+
+__device__ inline uint32_t byte_of(uint4 m, int idx)
+{
+    // idx indexes the 12 scale bytes that follow d and dmin in the header.
+    const uint32_t word = idx < 4 ? m.y : (idx < 8 ? m.z : m.w);
+    return (word >> (8 * (idx & 3))) & 0xffu;
+}
+
+// 6-bit scale and min of sub-block s (GGML K-quant packing).
+__device__ inline void q4k_scale_min(uint4 m, int s, uint32_t& sc, uint32_t& mn)
+{
+    if (s < 4) {
+        sc = byte_of(m, s) & 63u;
+        mn = byte_of(m, s + 4) & 63u;
+    } else {
+        const uint32_t lo = byte_of(m, s + 4);
+        sc = (lo & 15u) | ((byte_of(m, s - 4) >> 6) << 4);
+        mn = (lo >> 4) | ((byte_of(m, s) >> 6) << 4);
+    }
+}
+
+// One thread per 16 nibble bytes (32 weights: 16 in sub-block 2p, 16 in 2p+1).
+__global__ __launch_bounds__(256) void dequant_q4k_kernel(Q4KView w, int64_t n_in, int64_t nchunks,
+                                                          float* __restrict__ out)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= nchunks) return;
+    const int64_t sbg = c >> 3;          // global super-block index
+    const int cc = (int)(c & 7);
+    const int p = cc >> 1, h = cc & 1;
+    const uint4 m = w.meta[sbg];
+    const float d = fp16_bits_to_f32((uint16_t)(m.x & 0xffff));
+    const float dmin = fp16_bits_to_f32((uint16_t)(m.x >> 16));
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(m, 2 * p, sc0, m0);
+    q4k_scale_min(m, 2 * p + 1, sc1, m1);
+    const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
+    const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
+    const uint4 qv = *reinterpret_cast<const uint4*>(w.qs + c * 16);
+    const uint32_t words[4] = {qv.x, qv.y, qv.z, qv.w};
+    // flattened element index of the first low-nibble weight
+    const int64_t base = sbg * 256 + 64 * p + 16 * h;
+    float* lo = out + base;
+    float* hi = out + base + 32;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t byte = (words[k] >> (8 * t)) & 0xffu;
+            // products are exact in f32; the subtraction rounds once
+            lo[4 * k + t] = a0 * (float)(byte & 15u) - b0;
+            hi[4 * k + t] = a1 * (float)(byte >> 4) - b1;
+        }
+    }
+    (void)n_in;
+}
+
+__global__ void empty_kernel() {}
+
+__global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst,
+                                                   const uint4* __restrict__ src, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src[i];
+}
+
+inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+}  // namespace
+
+hipError_t launch_repack_q8_0(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
+                              hipStream_t s)
+{
+    const Q8View v = q8_view(dst, n_in, n_out);
+    const int64_t nb = n_in / 32, nblocks = nb * n_out;
+    hipLaunchKernelGGL(repack_q8_0_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(raw), nblocks, nb, n_in,
+                       const_cast<int8_t*>(v.q), const_cast<uint16_t*>(v.d));
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
+                             hipStream_t s)
+{
+    const Q4KView v = q4k_view(dst, n_in, n_out);
+    const int64_t nblocks = (n_in / 256) * n_out;
+    hipLaunchKernelGGL(repack_q4k_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(raw), nblocks,
+                       const_cast<uint8_t*>(v.qs), const_cast<uint4*>(v.meta));
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q8_0(Q8View w, int64_t n_in, int64_t n_out, float* out, hipStream_t s)
+{
+    const int64_t nchunks = n_out * n_in / 16;
+    hipLaunchKernelGGL(dequant_q8_0_kernel, dim3(grid_for(nchunks, 256)), dim3(256), 0, s, w, n_in,
+                       nchunks, out);
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q4k(Q4KView w, int64_t n_in, int64_t n_out, float* out, hipStream_t s)
+{
+    const int64_t nchunks = n_out * n_in / 32;
+    hipLaunchKernelGGL(dequant_q4k_kernel, dim3(grid_for(nchunks, 256)), dim3(256), 0, s, w, n_in,
+                       nchunks, out);
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_empty(hipStream_t s)
+{
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s)
+{
+    const int64_t n = bytes / 16;
+    int64_t blocks = grid_for(n, 256);
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
+    count_launch();
+    return hipGetLastError();
+}
+
+}  // namespace qdec

@@ -1,0 +1,75 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/qdec.h declares, and rejects invalid arguments with QDEC_EINVAL before
+it makes any HIP call."""
+import ctypes
+
+import pytest
+
+qd = pytest.importorskip("quantized_decode_ggml_amd")
+
+FAKE = 0x10000       # never dereferenced: every call below fails validation first
+
+
+def test_every_declared_function_is_exported():
+    names = qd.declared_functions()
+    assert len(names) >= 17
+    for name in names:
+        assert hasattr(qd.lib, name), f"{name} declared in qdec.h but not exported"
+    for core in ("q8_0_gemv", "q8_0_qkv", "q8_0_swiglu", "q8_0_gemv_residual", "q4k_gemv",
+                 "q8_0_gemm_batched"):
+        assert core in names
+
+
+def test_initial_state():
+    assert qd.cache_len() == 0
+    assert qd.launch_count() == 0
+
+
+@pytest.mark.parametrize("call", [
+    lambda L: L.q8_0_gemv(FAKE, 33, 16, 1, FAKE, FAKE * 2, None),          # n_in % 32
+    lambda L: L.q8_0_gemv(FAKE, 0, 16, 1, FAKE, FAKE * 2, None),           # n_in = 0
+    lambda L: L.q8_0_gemv(FAKE, 64, -1, 1, FAKE, FAKE * 2, None),          # n_out < 0
+    lambda L: L.q8_0_gemv(FAKE, 64, 16, 0, FAKE, FAKE * 2, None),          # batch 0
+    lambda L: L.q8_0_gemv(FAKE, 64, 16, 9, FAKE, FAKE * 2, None),          # batch > 8
+    lambda L: L.q8_0_gemv(None, 64, 16, 1, FAKE, FAKE * 2, None),          # null weight
+    lambda L: L.q8_0_gemv(FAKE, 64, 16, 1, FAKE + 4, FAKE * 2, None),      # x not 16-aligned
+    lambda L: L.q8_0_gemv(FAKE + 1, 64, 16, 1, FAKE, FAKE * 2, None),      # w odd address
+    lambda L: L.q8_0_gemv(FAKE, 64, 16, 1, FAKE, FAKE + 16, None),         # out overlaps x
+    lambda L: L.q8_0_gemv_residual(FAKE, 64, 16, 1, FAKE, None, FAKE * 2, None),
+    lambda L: L.q8_0_gemv_residual(FAKE, 64, 16, 1, FAKE, FAKE * 2 + 8, FAKE * 2, None),
+    lambda L: L.q8_0_qkv(FAKE, FAKE, FAKE, 64, 8, 9, 1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None),
+    lambda L: L.q8_0_qkv(FAKE, FAKE, FAKE, 64, 8, 0, 1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None),
+    lambda L: L.q8_0_qkv(FAKE, FAKE, FAKE, 64, 8, 4, 1, FAKE, FAKE * 2, FAKE * 2 + 16, FAKE * 4, None),
+    lambda L: L.q8_0_swiglu(FAKE, None, 64, 8, 1, FAKE, FAKE * 2, None),
+    lambda L: L.q4k_gemv(FAKE, 128, 8, 1, FAKE, FAKE * 2, None),           # n_in % 256
+    lambda L: L.q8_0_gemm_batched(FAKE, 64, 8, 0, FAKE, FAKE * 2, None),
+    lambda L: L.f32_gemm_batched(FAKE + 4, 64, 8, 1, FAKE * 4, FAKE * 8, None),
+    lambda L: L.qdec_prepare(FAKE, 7, 64, 8, None),                       # unknown type
+    lambda L: L.qdec_prepare(FAKE, 12, 64, 8, None),                      # Q4_K needs n_in % 256
+    lambda L: L.q8_0_dequantize(FAKE, 64, 8, FAKE * 2 + 4, None),         # out not 16-aligned
+    lambda L: L.qdec_copy(FAKE, FAKE * 2, 24, None),                      # bytes % 16
+    lambda L: L.qdec_release(None),
+])
+def test_invalid_arguments_rejected(call):
+    before = qd.launch_count()
+    assert call(qd.lib) == qd.QDEC_EINVAL
+    assert qd.last_error() != ""
+    assert qd.launch_count() == before
+    assert qd.cache_len() == 0
+
+
+def test_python_wrapper_raises():
+    class Fake:
+        def __init__(self, p, n):
+            self.p, self.n = p, n
+
+        def data_ptr(self):
+            return self.p
+
+        def numel(self):
+            return self.n
+
+    with pytest.raises(qd.QdecError) as ei:
+        qd.q8_0_gemv(Fake(FAKE, 1), 33, 4, Fake(FAKE, 33), out=Fake(FAKE * 2, 4), stream=0)
+    assert ei.value.status == qd.QDEC_EINVAL
+    assert "multiple of 32" in str(ei.value)

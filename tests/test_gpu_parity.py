@@ -1,0 +1,296 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded
+bytes and activations.
+
+Bars: dequantised weights bit-exact (compared as uint32); f32 paths
+|gpu - oracle| <= 1e-5 * S + 1e-6 with S = sum_j |w_ij x_bj| from the oracle;
+the bf16-MFMA batched GEMM <= 5e-3 * S; SwiGLU with the first-order propagated
+bound (helpers.swiglu_tol).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import BF16_REL, check_f32, f32_bits, q8_weights, swiglu_tol, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_decode_ggml_amd as q
+    return q
+
+
+@pytest.fixture(autouse=True)
+def fresh_cache(qd):
+    """The repack cache is keyed by device pointer and the caller promises the
+    bytes behind a cached pointer do not change until it is released.  Tests
+    free and reallocate weights through torch's caching allocator, which hands
+    the same addresses back, so every test starts and ends with an empty cache."""
+    qd.clear_cache()
+    yield
+    qd.clear_cache()
+
+
+def dev(a):
+    return to_dev(a, torch)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def host(t):
+    sync()
+    return t.cpu().numpy()
+
+
+# -------------------------------------------------------------- dequant --
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 32), (7, 96), (256, 512), (33, 3072)])
+def test_q8_0_dequant_bitexact(qd, n_out, n_in):
+    raw = q8_weights(11 + n_in, n_out, n_in)
+    got = host(qd.q8_0_dequantize(dev(raw), n_in, n_out))
+    ref = oracle.q8_0_dequantize(raw, n_in, n_out)
+    assert np.array_equal(f32_bits(got), f32_bits(ref))
+
+
+def test_q8_0_dequant_bitexact_all_scales(qd):
+    """Every finite fp16 d (including subnormals and -0) with every int8 q."""
+    d_bits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    d_bits = d_bits[(d_bits & 0x7C00) != 0x7C00]             # finite only
+    n = d_bits.size
+    q = np.tile(np.arange(-128, 128, dtype=np.int32).astype(np.int8), (n * 32 + 255) // 256)[: n * 32]
+    raw = np.empty((n, 34), np.uint8)
+    raw[:, 0:2] = d_bits.view(np.uint8).reshape(n, 2)
+    raw[:, 2:] = q.reshape(n, 32).view(np.uint8)
+    n_out = n // 8
+    raw = raw[: n_out * 8].reshape(-1)
+    got = host(qd.q8_0_dequantize(dev(raw), 256, n_out))
+    ref = oracle.q8_0_dequantize(raw, 256, n_out)
+    assert np.array_equal(f32_bits(got), f32_bits(ref))
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (5, 768), (64, 3072)])
+def test_q4k_dequant_bitexact(qd, n_out, n_in):
+    raw = synth.q4k_weights(21 + n_in, n_out, n_in)
+    got = host(qd.q4k_dequantize(dev(raw), n_in, n_out))
+    ref = oracle.q4k_dequantize(raw, n_in, n_out)
+    assert np.array_equal(f32_bits(got), f32_bits(ref))
+
+
+def test_q4k_dequant_bitexact_full_fp16_range(qd):
+    """d and dmin over the whole finite fp16 range with random signs: the single
+    rounding of the subtraction must match the oracle bit for bit."""
+    rng = np.random.default_rng(77)
+    n = 4096
+    raw = rng.integers(0, 256, (n, 144)).astype(np.uint8)
+    for off in (0, 2):
+        bits = (rng.integers(0, 0x7C00, n) | (rng.integers(0, 2, n) << 15)).astype(np.uint16)
+        raw[:, off:off + 2] = bits.view(np.uint8).reshape(n, 2)
+    raw = raw.reshape(-1)
+    got = host(qd.q4k_dequantize(dev(raw), 256 * 8, n // 8))
+    ref = oracle.q4k_dequantize(raw, 256 * 8, n // 8)
+    assert np.array_equal(f32_bits(got), f32_bits(ref))
+
+
+def test_golden_blocks_on_gpu(qd, golden_dir):
+    import json
+    with open(os.path.join(golden_dir, "q8_0_blocks.json")) as f:
+        cases = json.load(f)["cases"]
+    raw = np.concatenate([np.frombuffer(bytes.fromhex(c["d_bytes"]) + np.asarray(c["q"], np.int8).tobytes(),
+                                        np.uint8) for c in cases])
+    got = host(qd.q8_0_dequantize(dev(raw), 32, len(cases)))
+    exp = np.array([[float.fromhex(s) for s in c["expected"]] for c in cases], np.float32)
+    assert np.array_equal(f32_bits(got), f32_bits(exp))
+
+
+# ----------------------------------------------------------- Q8_0 GEMV --
+
+GEMV_SHAPES = [(1, 32), (3, 64), (5, 96), (17, 288), (256, 512), (100, 768), (1000, 1024),
+               (130, 3072), (67, 8192), (8, 2560)]
+
+
+@pytest.mark.parametrize("n_out,n_in", GEMV_SHAPES)
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 7, 8])
+def test_q8_0_gemv(qd, n_out, n_in, batch):
+    raw = q8_weights(1000 + n_in + n_out, n_out, n_in)
+    x = synth.normal_f32(2000 + batch, (batch, n_in))
+    out = host(qd.q8_0_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q8_0_gemv {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(256, 512), (3072, 8192), (77, 3072), (9, 288)])
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_q8_0_gemv_residual(qd, n_out, n_in, batch):
+    raw = q8_weights(3000 + n_in, n_out, n_in)
+    x = synth.normal_f32(3001, (batch, n_in))
+    r = synth.normal_f32(3002, (batch, n_out))
+    out = host(qd.q8_0_gemv_residual(dev(raw), n_in, n_out, dev(x), dev(r)))
+    ref, S = oracle.q8_0_gemv_residual(raw, n_in, n_out, x, r)
+    check_f32(out, ref, S, "residual")
+
+
+def test_q8_0_gemv_residual_in_place(qd):
+    n_out, n_in, batch = 1000, 3072, 2
+    raw = q8_weights(3100, n_out, n_in)
+    x = synth.normal_f32(3101, (batch, n_in))
+    r = synth.normal_f32(3102, (batch, n_out))
+    rd = dev(r)
+    qd.q8_0_gemv_residual(dev(raw), n_in, n_out, dev(x), rd, out=rd)
+    ref, S = oracle.q8_0_gemv_residual(raw, n_in, n_out, x, r)
+    check_f32(host(rd), ref, S, "residual in place")
+
+
+@pytest.mark.parametrize("n_in,n_q,n_kv", [(3072, 3072, 1024), (512, 100, 20), (96, 5, 5), (288, 64, 1)])
+@pytest.mark.parametrize("batch", [1, 2, 5, 8])
+def test_q8_0_qkv(qd, n_in, n_q, n_kv, batch):
+    wq = q8_weights(4000, n_q, n_in)
+    wk = q8_weights(4001, n_kv, n_in)
+    wv = q8_weights(4002, n_kv, n_in)
+    x = synth.normal_f32(4003 + batch, (batch, n_in))
+    q, k, v = qd.q8_0_qkv(dev(wq), dev(wk), dev(wv), n_in, n_q, n_kv, dev(x))
+    (rq, rk, rv), (sq, sk, sv) = oracle.q8_0_qkv(wq, wk, wv, n_in, n_q, n_kv, x)
+    check_f32(host(q), rq, sq, "q")
+    check_f32(host(k), rk, sk, "k")
+    check_f32(host(v), rv, sv, "v")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(8192, 3072), (100, 512), (7, 96), (33, 288)])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 8])
+def test_q8_0_swiglu(qd, n_out, n_in, batch):
+    if n_out == 8192 and batch == 3:
+        pytest.skip("covered by the smaller shapes")
+    wg = q8_weights(5000 + n_in, n_out, n_in)
+    wu = q8_weights(5001 + n_in, n_out, n_in)
+    x = synth.normal_f32(5002 + batch, (batch, n_in))
+    out = host(qd.q8_0_swiglu(dev(wg), dev(wu), n_in, n_out, dev(x)))
+    r = oracle.q8_0_swiglu(wg, wu, n_in, n_out, x)
+    tol = swiglu_tol(r)
+    err = np.abs(out.astype(np.float64) - r["out"])
+    assert np.all(err <= tol), f"worst err/tol {np.max(err / tol):.3g}"
+
+
+# ----------------------------------------------------------- Q4_K GEMV --
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (13, 768), (8192, 3072), (3072, 8192), (50, 2560)])
+@pytest.mark.parametrize("batch", [1, 2, 5, 8])
+def test_q4k_gemv(qd, n_out, n_in, batch):
+    if n_out * n_in > 10_000_000 and batch not in (1, 8):
+        pytest.skip("large shapes run at batch 1 and 8")
+    raw = synth.q4k_weights(6000 + n_in, n_out, n_in)
+    x = synth.normal_f32(6001 + batch, (batch, n_in))
+    out = host(qd.q4k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q4k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q4k {n_out}x{n_in} b{batch}")
+
+
+# --------------------------------------------------------- batched GEMM --
+
+@pytest.mark.parametrize("n_out,n_in,batch", [(16, 32, 1), (130, 96, 3), (256, 512, 128),
+                                              (200, 288, 130), (128, 3072, 129), (300, 64, 512)])
+def test_q8_0_gemm_batched(qd, n_out, n_in, batch):
+    raw = q8_weights(7000 + n_in, n_out, n_in)
+    x = synth.normal_f32(7001 + batch, (batch, n_in))
+    out = host(qd.q8_0_gemm_batched(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, "gemm q8_0", rel=BF16_REL, abs_=0.0)
+
+
+@pytest.mark.parametrize("n_out,n_in,batch", [(16, 32, 1), (130, 96, 3), (256, 512, 128),
+                                              (200, 288, 130), (300, 64, 512)])
+def test_f32_gemm_batched(qd, n_out, n_in, batch):
+    w = synth.normal_f32(7100 + n_in, (n_out, n_in), 0.02)
+    x = synth.normal_f32(7101 + batch, (batch, n_in))
+    out = host(qd.f32_gemm_batched(dev(w), n_in, n_out, dev(x)))
+    ref, S = oracle.f32_gemm(w, n_in, n_out, x)
+    check_f32(out, ref, S, "gemm f32", rel=BF16_REL, abs_=0.0)
+
+
+# --------------------------------------------------- library behaviour --
+
+def test_non_default_stream(qd):
+    n_out, n_in = 512, 3072
+    raw = q8_weights(8000, n_out, n_in)
+    x = synth.normal_f32(8001, (2, n_in))
+    s = torch.cuda.Stream()
+    wd, xd = dev(raw), dev(x)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = torch.empty((2, n_out), device="cuda")
+        qd.q8_0_gemv(wd, n_in, n_out, xd, out=out, stream=s)
+    s.synchronize()
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(out.cpu().numpy(), ref, S, "stream")
+
+
+def test_cache_prepare_release_clear_and_reuse(qd):
+    qd.clear_cache()
+    assert qd.cache_len() == 0
+    n_out, n_in = 64, 512
+    a = q8_weights(8100, n_out, n_in)
+    b = q8_weights(8101, n_out, n_in)
+    x = synth.normal_f32(8102, (1, n_in))
+    buf = dev(a)
+    qd.prepare(buf, qd.TYPE_Q8_0, n_in, n_out)
+    assert qd.cache_len() == 1
+    qd.prepare(buf, qd.TYPE_Q8_0, n_in, n_out)      # idempotent
+    assert qd.cache_len() == 1
+    out = host(qd.q8_0_gemv(buf, n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(a, n_in, n_out, x)
+    check_f32(out, ref, S, "prepared")
+    # new bytes behind the same pointer after release: must be re-read
+    qd.release(buf)
+    assert qd.cache_len() == 0
+    buf.copy_(dev(b))
+    out = host(qd.q8_0_gemv(buf, n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(b, n_in, n_out, x)
+    check_f32(out, ref, S, "after release")
+    with pytest.raises(qd.QdecError):
+        qd.release(dev(a))                            # never cached
+    qd.clear_cache()
+    assert qd.cache_len() == 0
+
+
+def test_stale_pointer_needs_release(qd):
+    """Documented contract: new bytes behind a cached pointer are not seen until
+    qdec_release; after release the new bytes are repacked."""
+    n_out, n_in = 32, 256
+    a = q8_weights(8150, n_out, n_in)
+    b = q8_weights(8151, n_out, n_in)
+    x = synth.normal_f32(8152, (1, n_in))
+    buf, xd = dev(a), dev(x)
+    qd.q8_0_gemv(buf, n_in, n_out, xd)
+    buf.copy_(dev(b))
+    stale = host(qd.q8_0_gemv(buf, n_in, n_out, xd))
+    ref_a, S_a = oracle.q8_0_gemv(a, n_in, n_out, x)
+    check_f32(stale, ref_a, S_a, "cached copy still used")
+    qd.release(buf)
+    fresh = host(qd.q8_0_gemv(buf, n_in, n_out, xd))
+    ref_b, S_b = oracle.q8_0_gemv(b, n_in, n_out, x)
+    check_f32(fresh, ref_b, S_b, "after release")
+
+
+def test_fail_alloc_hook(qd, monkeypatch):
+    monkeypatch.setenv("QDEC_FAIL_ALLOC", "1")
+    raw = dev(q8_weights(8200, 8, 64))
+    with pytest.raises(qd.QdecError) as ei:
+        qd.prepare(raw, qd.TYPE_Q8_0, 64, 8)
+    assert ei.value.status == qd.QDEC_ENOMEM
+
+
+def test_launch_counter_witness(qd):
+    raw = dev(q8_weights(8300, 32, 64))
+    x = dev(synth.normal_f32(8301, (1, 64)))
+    before = qd.launch_count()
+    qd.q8_0_gemv(raw, 64, 32, x)
+    qd.q8_0_gemv(raw, 64, 32, x)
+    sync()
+    assert qd.launch_count() >= before + 2
