@@ -13,8 +13,8 @@ Infinity Cache), so the bytes come from HBM as in a real decode.
 value = algorithmic bytes per step (GGML weight bytes + x + out + residual)
         / wall time per step, in GB/s, inputs resident in HBM.
 roofline = the dominant kernel's algorithmic bytes per launch / its mean
-        launch duration from HIP events recorded around each of its launches
-        inside the timed steps, against 8 TB/s.
+        launch duration (HIP events around `steps` back-to-back launches on
+        the launch stream), against 8 TB/s.
 cpu_baseline = the CPU oracle (single thread) on a bounded sample of steps.
 """
 from __future__ import annotations
@@ -82,17 +82,150 @@ def cpu_baseline(w, x, budget_s=12.0):
                       f"single-threaded C oracle, f64 accumulation"}
 
 
+def suite(args):
+    """Every workload configuration through the library, one line of JSON each
+    (to stdout): mean kernel time from HIP events around each launch, over
+    rotated weight copies (>= 512 MB per workload), GB/s of algorithmic bytes
+    and, for the batched GEMMs, TFLOP/s."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_ggml_amd as qd
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def copies_for(nbytes):
+        return max(2, -(-(512 << 20) // max(nbytes, 1)))
+
+    def timed(name, launches, nbytes, flops=None, iters=100, warm=20, extra=None):
+        n = len(launches)
+        for i in range(warm):
+            launches[i % n]()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for i, (s0, s1) in enumerate(ev):
+            s0.record(stream)
+            launches[i % n]()
+            s1.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        rec = {"workload": name, "mean_us": round(float(us.mean()), 3), "median_us": round(float(np.median(us)), 3),
+               "bytes": int(nbytes), "gbs": round(nbytes / (us.mean() * 1e-6) / 1e9, 1),
+               "pct_hbm": round(100 * nbytes / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        if flops:
+            rec["tflops"] = round(flops / (us.mean() * 1e-6) / 1e12, 2)
+        if extra:
+            rec.update(extra)
+        print(json.dumps(rec), flush=True)
+
+    def q8_dev(cfg, idx, n_out, n_in, ncopies):
+        raw = torch.from_numpy(synth.q8_0_weights(synth.seed(cfg, idx), n_out, n_in)[0]).to(dev)
+        out = []
+        for _ in range(ncopies):
+            c = raw.clone()
+            qd.prepare(c, qd.TYPE_Q8_0, n_in, n_out)
+            out.append(c)
+        return out
+
+    def xdev(seed, shape):
+        return torch.from_numpy(synth.normal_f32(seed, shape)).to(dev)
+
+    # config 0
+    w0 = q8_dev(0, 0, 256, 512, 4)
+    x0, o0 = xdev(synth.seed(0, 1), (1, 512)), torch.empty((1, 256), device=dev)
+    timed("c0 q8_0_gemv 256x512 b1", [lambda w=w: qd.q8_0_gemv(w, 512, 256, x0, out=o0) for w in w0],
+          q8_bytes(256, 512) + 512 * 4 + 256 * 4)
+    # config 1
+    nqkv = q8_bytes(5120, 3072)
+    L = copies_for(nqkv)
+    wq, wk, wv = q8_dev(1, 0, 3072, 3072, L), q8_dev(1, 1, 1024, 3072, L), q8_dev(1, 2, 1024, 3072, L)
+    xq = xdev(synth.seed(1, 5), (1, 3072))
+    oq, ok, ov = (torch.empty((1, n), device=dev) for n in (3072, 1024, 1024))
+    timed("c1 q8_0_qkv 3072+1024+1024 x 3072 b1",
+          [lambda i=i: qd.q8_0_qkv(wq[i], wk[i], wv[i], 3072, 3072, 1024, xq, oq, ok, ov) for i in range(L)],
+          nqkv + 3072 * 4 + 5120 * 4)
+    del wq, wk, wv
+    L = copies_for(q8_bytes(8192, 3072))
+    wup = q8_dev(1, 3, 8192, 3072, L)
+    xu, ou = xdev(synth.seed(1, 6), (1, 3072)), torch.empty((1, 8192), device=dev)
+    timed("c1 q8_0_gemv up 8192x3072 b1", [lambda w=w: qd.q8_0_gemv(w, 3072, 8192, xu, out=ou) for w in wup],
+          q8_bytes(8192, 3072) + 3072 * 4 + 8192 * 4)
+    wdn = q8_dev(1, 4, 3072, 8192, L)
+    xd, rd, od = xdev(synth.seed(1, 7), (1, 8192)), xdev(synth.seed(1, 8), (1, 3072)), torch.empty((1, 3072), device=dev)
+    timed("c1 q8_0_gemv_residual down 3072x8192 b1",
+          [lambda w=w: qd.q8_0_gemv_residual(w, 8192, 3072, xd, rd, out=od) for w in wdn],
+          q8_bytes(3072, 8192) + 8192 * 4 + 3072 * 8)
+    # config 2 (gate/up rotate in pairs; down reuses the config-1 rotation)
+    Lg = copies_for(2 * q8_bytes(8192, 3072))
+    wg = q8_dev(2, 0, 8192, 3072, Lg)
+    wu2 = q8_dev(2, 1, 8192, 3072, Lg)
+    for b in (1, 2, 4, 8):
+        x2, m2 = xdev(synth.seed(2, 3) + b, (b, 3072)), torch.empty((b, 8192), device=dev)
+        timed(f"c2 q8_0_swiglu 2x8192x3072 b{b}",
+              [lambda i=i: qd.q8_0_swiglu(wg[i], wu2[i], 3072, 8192, x2, out=m2) for i in range(Lg)],
+              2 * q8_bytes(8192, 3072) + b * 3072 * 4 + b * 8192 * 4)
+        r2, o2 = xdev(synth.seed(2, 4) + b, (b, 3072)), torch.empty((b, 3072), device=dev)
+        timed(f"c2 q8_0_gemv_residual down 3072x8192 b{b}",
+              [lambda w=w: qd.q8_0_gemv_residual(w, 8192, 3072, m2, r2, out=o2) for w in wdn],
+              q8_bytes(3072, 8192) + b * 8192 * 4 + b * 3072 * 8)
+    del wg, wu2
+    # config 3: batched GEMM (Q8_0 weights reuse up/down rotations; dense f32 separate)
+    for B in (128, 512):
+        for nm, ws, n_out, n_in in (("up 8192x3072", wup, 8192, 3072), ("down 3072x8192", wdn, 3072, 8192)):
+            x3, o3 = xdev(synth.seed(3, 2) + B, (B, n_in)), torch.empty((B, n_out), device=dev)
+            timed(f"c3 q8_0_gemm_batched {nm} B{B}",
+                  [lambda w=w: qd.q8_0_gemm_batched(w, n_in, n_out, x3, out=o3) for w in ws],
+                  q8_bytes(n_out, n_in) + B * n_in * 4 + B * n_out * 4, flops=2.0 * B * n_out * n_in)
+    del wup, wdn
+    for nm, n_out, n_in in (("up 8192x3072", 8192, 3072), ("down 3072x8192", 3072, 8192)):
+        wf = torch.from_numpy(synth.normal_f32(synth.seed(3, 10), (n_out, n_in), 0.02)).to(dev)
+        wfs = [wf] + [wf.clone() for _ in range(copies_for(wf.numel() * 4) - 1)]
+        for B in (128, 512):
+            x3, o3 = xdev(synth.seed(3, 12) + B, (B, n_in)), torch.empty((B, n_out), device=dev)
+            timed(f"c3 f32_gemm_batched {nm} B{B}",
+                  [lambda w=w: qd.f32_gemm_batched(w, n_in, n_out, x3, out=o3) for w in wfs],
+                  n_out * n_in * 4 + B * n_in * 4 + B * n_out * 4, flops=2.0 * B * n_out * n_in)
+        del wfs, wf
+    # config 4
+    for n_out, n_in in ((8192, 3072), (3072, 8192)):
+        raw = torch.from_numpy(synth.q4k_weights(synth.seed(4, 0 if n_out == 8192 else 1), n_out, n_in)).to(dev)
+        nb4 = n_out * (n_in // 256) * 144
+        ws = []
+        for _ in range(copies_for(nb4)):
+            c = raw.clone()
+            qd.prepare(c, qd.TYPE_Q4_K, n_in, n_out)
+            ws.append(c)
+        x4, o4 = xdev(synth.seed(4, 2), (1, n_in)), torch.empty((1, n_out), device=dev)
+        timed(f"c4 q4k_gemv {n_out}x{n_in} b1", [lambda w=w: qd.q4k_gemv(w, n_in, n_out, x4, out=o4) for w in ws],
+              nb4 + n_in * 4 + n_out * 4)
+        del ws, raw
+    wvoc = q8_dev(4, 3, 128256, 3072, 2)
+    xv, ov = xdev(synth.seed(4, 4), (1, 3072)), torch.empty((1, 128256), device=dev)
+    timed("c4 q8_0_gemv vocab 128256x3072 b1", [lambda w=w: qd.q8_0_gemv(w, 3072, 128256, xv, out=ov) for w in wvoc],
+          q8_bytes(128256, 3072) + 3072 * 4 + 128256 * 4, iters=40)
+    # launch cost of an empty kernel (the analogue of an empty submit round trip)
+    timed("empty kernel", [lambda: qd.empty_kernel()], 0)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", action="store_true",
+                    help="time every workload configuration (one JSON line each) instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is a "
               "single-GPU weight-streaming kernel and no multi-GPU build exists", file=sys.stderr)
         sys.exit(2)
+
+    if args.suite:
+        suite(args)
+        return
 
     import numpy as np
     import torch
@@ -127,29 +260,22 @@ def main():
     torch.cuda.synchronize()
 
     names = ("qkv", "up", "down_residual")
-    events = {n: [] for n in names}
 
-    def step(i, record):
+    def single(name, i):
         L = layers[i % LAYERS]
-        calls = (
-            ("qkv", lambda: qd.q8_0_qkv(L["wq"], L["wk"], L["wv"], N_IN, N_Q, N_KV, xs["x_qkv"],
-                                        q_out, k_out, v_out, stream=stream)),
-            ("up", lambda: qd.q8_0_gemv(L["up"], N_IN, N_FF, xs["x_up"], out=up_out, stream=stream)),
-            ("down_residual", lambda: qd.q8_0_gemv_residual(L["down"], N_FF, N_IN, xs["x_down"],
-                                                            xs["r_down"], out=down_out, stream=stream)),
-        )
-        for name, fn in calls:
-            if record:
-                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s.record(stream)
-                fn()
-                e.record(stream)
-                events[name].append((s, e))
-            else:
-                fn()
+        if name == "qkv":
+            qd.q8_0_qkv(L["wq"], L["wk"], L["wv"], N_IN, N_Q, N_KV, xs["x_qkv"], q_out, k_out, v_out, stream=stream)
+        elif name == "up":
+            qd.q8_0_gemv(L["up"], N_IN, N_FF, xs["x_up"], out=up_out, stream=stream)
+        else:
+            qd.q8_0_gemv_residual(L["down"], N_FF, N_IN, xs["x_down"], xs["r_down"], out=down_out, stream=stream)
+
+    def step(i):
+        for name in names:
+            single(name, i)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
 
     # One HIP graph per layer (its three launches), captured on torch's capture
@@ -160,13 +286,13 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             stream = torch.cuda.current_stream()
-            step(i, False)
+            step(i)
         graphs.append(g)
     g_all = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_all):
         stream = torch.cuda.current_stream()
         for i in range(LAYERS):
-            step(i, False)
+            step(i)
     stream = torch.cuda.current_stream()
     for _ in range(3):
         g_all.replay()
@@ -188,22 +314,30 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t0
     assert qd.launch_count() - launches0 == 3 * args.steps, "not every product ran in libqdec"
 
-    # timed region 2: the same steps with HIP events around every launch
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, True)
-    torch.cuda.synchronize()
+    # timed region 2: each product alone, `steps` launches back to back over the
+    # rotated layers, bracketed by HIP events on the launch stream: the mean
+    # launch duration of that kernel (launch gaps included, so slightly above
+    # the profiler's kernel duration).
     per_kernel = {}
     sb = step_bytes()
     for n in names:
-        us = np.array([s.elapsed_time(e) * 1e3 for s, e in events[n]])
-        per_kernel[n] = {"mean_us": round(float(us.mean()), 3), "median_us": round(float(np.median(us)), 3),
-                         "bytes": sb[n], "gbs": round(sb[n] / (us.mean() * 1e-6) / 1e9, 1)}
+        fns = [lambda i=i, n=n: single(n, i) for i in range(LAYERS)]
+        for i in range(LAYERS):
+            fns[i]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fns[i % LAYERS]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        per_kernel[n] = {"mean_us": round(us, 3), "bytes": sb[n], "gbs": round(sb[n] / (us * 1e-6) / 1e9, 1)}
     dom = max(names, key=lambda n: per_kernel[n]["mean_us"])
     achieved = per_kernel[dom]["gbs"]
 

@@ -13,6 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import weakref
 
 import torch
 
@@ -77,6 +78,34 @@ def _check(status: int):
         raise QdecError(status, lib.qdec_last_error().decode(errors="replace"))
 
 
+# The library caches a repacked copy per weight pointer and trusts the caller to
+# release it before the bytes behind the pointer change.  Torch frees and reuses
+# device addresses freely, so the binding releases a weight's copies when the
+# tensor object that was passed in is garbage-collected.
+_tracked: dict[int, weakref.finalize] = {}
+
+
+def _release_quietly(ptr: int):
+    f = _tracked.get(ptr)
+    if f is not None and not f.alive:
+        _tracked.pop(ptr, None)
+    lib.qdec_release(ptr)
+
+
+def _track(*weights):
+    """After a successful call: release each weight's repacked copies when the
+    tensor object dies."""
+    for t in weights:
+        if t is None or isinstance(t, int):
+            continue
+        ptr = t.data_ptr()
+        f = _tracked.get(ptr)
+        if f is None or not f.alive:
+            f = weakref.finalize(t, _release_quietly, ptr)
+            f.atexit = False
+            _tracked[ptr] = f
+
+
 def _ptr(t) -> int | None:
     if t is None:
         return None
@@ -110,6 +139,7 @@ def q8_0_gemv(w, n_in, n_out, x, out=None, stream=None):
     batch = _batch(x, n_in)
     out = _f32_out(out, batch, n_out, x)
     _check(lib.q8_0_gemv(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    _track(w)
     return out
 
 
@@ -118,6 +148,7 @@ def q8_0_gemv_residual(w, n_in, n_out, x, residual, out=None, stream=None):
     out = _f32_out(out, batch, n_out, x)
     _check(lib.q8_0_gemv_residual(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(residual), _ptr(out),
                                   _stream(stream)))
+    _track(w)
     return out
 
 
@@ -128,6 +159,7 @@ def q8_0_qkv(wq, wk, wv, n_in, n_q, n_kv, x, q_out=None, k_out=None, v_out=None,
     v_out = _f32_out(v_out, batch, n_kv, x)
     _check(lib.q8_0_qkv(_ptr(wq), _ptr(wk), _ptr(wv), n_in, n_q, n_kv, batch, _ptr(x), _ptr(q_out),
                         _ptr(k_out), _ptr(v_out), _stream(stream)))
+    _track(wq, wk, wv)
     return q_out, k_out, v_out
 
 
@@ -136,6 +168,7 @@ def q8_0_swiglu(w_gate, w_up, n_in, n_out, x, out=None, stream=None):
     out = _f32_out(out, batch, n_out, x)
     _check(lib.q8_0_swiglu(_ptr(w_gate), _ptr(w_up), n_in, n_out, batch, _ptr(x), _ptr(out),
                            _stream(stream)))
+    _track(w_gate, w_up)
     return out
 
 
@@ -143,6 +176,7 @@ def q4k_gemv(w, n_in, n_out, x, out=None, stream=None):
     batch = _batch(x, n_in)
     out = _f32_out(out, batch, n_out, x)
     _check(lib.q4k_gemv(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    _track(w)
     return out
 
 
@@ -150,6 +184,7 @@ def q8_0_gemm_batched(w, n_in, n_out, x, out=None, stream=None):
     batch = _batch(x, n_in)
     out = _f32_out(out, batch, n_out, x)
     _check(lib.q8_0_gemm_batched(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    _track(w)
     return out
 
 
@@ -162,13 +197,21 @@ def f32_gemm_batched(w, n_in, n_out, x, out=None, stream=None):
 
 def prepare(w, qtype, n_in, n_out, stream=None):
     _check(lib.qdec_prepare(_ptr(w), int(qtype), n_in, n_out, _stream(stream)))
+    _track(w)
 
 
 def release(w):
-    _check(lib.qdec_release(_ptr(w)))
+    ptr = _ptr(w)
+    f = _tracked.pop(ptr, None)
+    if f is not None:
+        f.detach()
+    _check(lib.qdec_release(ptr))
 
 
 def clear_cache():
+    for f in list(_tracked.values()):
+        f.detach()
+    _tracked.clear()
     lib.qdec_clear_cache()
 
 
@@ -180,6 +223,7 @@ def q8_0_dequantize(w, n_in, n_out, out=None, stream=None):
     if out is None:
         out = torch.empty((n_out, n_in), dtype=torch.float32, device=w.device)
     _check(lib.q8_0_dequantize(_ptr(w), n_in, n_out, _ptr(out), _stream(stream)))
+    _track(w)
     return out
 
 
@@ -187,6 +231,7 @@ def q4k_dequantize(w, n_in, n_out, out=None, stream=None):
     if out is None:
         out = torch.empty((n_out, n_in), dtype=torch.float32, device=w.device)
     _check(lib.q4k_dequantize(_ptr(w), n_in, n_out, _ptr(out), _stream(stream)))
+    _track(w)
     return out
 
 

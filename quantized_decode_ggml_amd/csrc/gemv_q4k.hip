@@ -3,23 +3,27 @@
 // layout), batch 1..8.
 //
 // Super-block (256 weights, 144 bytes; the Q4_K workload definition that
-// accompanies the pages): fp16 d, fp16 dmin, 12 bytes of eight 6-bit scales
-// and mins (GGML K-quant packing), 128 nibble bytes.  In 64-element chunk p the
-// low nibbles of qs[32p..32p+31] are sub-block 2p and the high nibbles
-// sub-block 2p+1.  w = d*sc*q - dmin*m.
+// accompanies the pages): fp16 d, fp16 dmin, eight 6-bit scales and mins, 128
+// nibble bytes.  In 64-element chunk p the low nibbles of qs[32p..32p+31] are
+// sub-block 2p and the high nibbles sub-block 2p+1.  w = d*sc*q - dmin*m.  The
+// repacked copy holds the nibbles, d|dmin, and the scales/mins unpacked to
+// bytes (one word per sub-block pair), so no lane decodes the 6-bit packing.
 //
-// Work mapping: as the Q8_0 kernel, with a 16-byte chunk of nibbles per lane
-// (32 weights: 16 of sub-block 2p and 16 of sub-block 2p+1).  Per chunk the
-// dot product is taken per sub-block in the factored form
+// Work mapping: as the Q8_0 fast path, with an 8-byte chunk of nibbles per
+// lane (16 weights: 8 of sub-block 2p, 8 of sub-block 2p+1), so a row of n_in
+// weights is n_in/16 chunks and lane j of a wave takes chunks j, j+64, ...; K
+// is split over KS waves of the workgroup and each wave computes R rows.  Per
+// chunk the dot product is taken per sub-block in the factored form
 //     sum_t w_t x_t = (d*sc) * sum_t q_t x_t - (dmin*m) * sum_t x_t,
-// where both products d*sc and dmin*m are exact in f32.  sum_t x_t depends only
-// on the lane's columns, so it is computed once per chunk and reused for the R
-// rows of the tile.
+// where d*sc and dmin*m are exact in f32.  sum_t x_t depends only on the lane's
+// columns, so it is formed once per wave when x stays in registers.
 #include "qdec_internal.h"
 
 namespace qdec {
 
 namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline float fp16_bits_to_f32(uint16_t h)
 {
@@ -28,45 +32,229 @@ __device__ inline float fp16_bits_to_f32(uint16_t h)
     return static_cast<float>(v);
 }
 
-__device__ inline uint32_t scale_byte(const uint4& m, int idx)
-{
-    const uint32_t word = idx < 4 ? m.y : (idx < 8 ? m.z : m.w);
-    return (word >> (8 * (idx & 3))) & 0xffu;
-}
-
-// 6-bit scale and min of sub-block s (GGML K-quant packing): sub-blocks 0-3
-// use the low 6 bits of scale bytes s and s+4; sub-blocks 4-7 take their low 4
-// bits from byte s+4 (scale: low nibble, min: high nibble) and their high 2
-// bits from the top of bytes s-4 (scale) and s (min).
-__device__ inline void scale_min(const uint4& m, int s, float& sc, float& mn)
-{
-    uint32_t a, b;
-    if (s < 4) {
-        a = scale_byte(m, s) & 63u;
-        b = scale_byte(m, s + 4) & 63u;
-    } else {
-        const uint32_t lo = scale_byte(m, s + 4);
-        a = (lo & 15u) | ((scale_byte(m, s - 4) >> 6) << 4);
-        b = (lo >> 4) | ((scale_byte(m, s) >> 6) << 4);
-    }
-    sc = (float)a;
-    mn = (float)b;
-}
-
 struct Q4KArgs {
     const uint8_t* qs;
-    const uint4* meta;
+    const uint32_t* dm;
+    const uint32_t* sm;
     float* out;
     const float* x;
     int64_t n_in;
     int64_t n_out;
     int batch;
-    int lpr_log2;
-    int nch;  // 16-byte nibble chunks per row = n_in / 32
+    int lpr_log2;  // general path: lanes per row group
+    int nch;       // 8-byte nibble chunks per row = n_in / 16
 };
 
-template <int B, int R, int NCH>
-__global__ __launch_bounds__(256) void q4k_gemv_kernel(Q4KArgs a)
+__device__ inline u32x2 stream_load8(const uint8_t* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+__device__ inline uint32_t stream_load4(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
+// x values of chunk c: 8 for the low-nibble sub-block, 8 for the high one.
+struct XChunk {
+    float lo[8], hi[8];
+    float slo, shi;  // their sums
+};
+
+__device__ inline int64_t chunk_x_offset(int c)
+{
+    const int sb = c >> 4, cc = c & 15;
+    return (int64_t)sb * 256 + 64 * (cc >> 2) + 8 * (cc & 3);
+}
+
+__device__ inline void load_xchunk(const float* xrow, int c, XChunk& xc)
+{
+    const float4* pl = reinterpret_cast<const float4*>(xrow + chunk_x_offset(c));
+    const float4* ph = reinterpret_cast<const float4*>(xrow + chunk_x_offset(c) + 32);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float4 v = pl[k], u = ph[k];
+        xc.lo[4 * k] = v.x; xc.lo[4 * k + 1] = v.y; xc.lo[4 * k + 2] = v.z; xc.lo[4 * k + 3] = v.w;
+        xc.hi[4 * k] = u.x; xc.hi[4 * k + 1] = u.y; xc.hi[4 * k + 2] = u.z; xc.hi[4 * k + 3] = u.w;
+    }
+}
+
+__device__ inline void sum_xchunk(XChunk& xc)
+{
+    float a = xc.lo[0], b = xc.hi[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) {
+        a += xc.lo[t];
+        b += xc.hi[t];
+    }
+    xc.slo = a;
+    xc.shi = b;
+}
+
+// Contribution of one 8-byte chunk (nibbles q, header words dm and sm) for x.
+__device__ inline float chunk_dot(u32x2 q, uint32_t dm, uint32_t sm, const XChunk& xc, float acc)
+{
+    const float d = fp16_bits_to_f32((uint16_t)(dm & 0xffff));
+    const float dmin = fp16_bits_to_f32((uint16_t)(dm >> 16));
+    const float f_lo = d * (float)(sm & 0xff), f_hi = d * (float)((sm >> 8) & 0xff);
+    const float g_lo = dmin * (float)((sm >> 16) & 0xff), g_hi = dmin * (float)(sm >> 24);
+    const uint32_t w[2] = {q.x, q.y};
+    float tl = 0.0f, th = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t lo = w[k] & 0x0f0f0f0fu;
+        const uint32_t hi = (w[k] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            tl = __builtin_fmaf((float)((lo >> (8 * t)) & 0xffu), xc.lo[4 * k + t], tl);
+            th = __builtin_fmaf((float)((hi >> (8 * t)) & 0xffu), xc.hi[4 * k + t], th);
+        }
+    }
+    acc = __builtin_fmaf(f_lo, tl, acc);
+    acc = __builtin_fmaf(-g_lo, xc.slo, acc);
+    acc = __builtin_fmaf(f_hi, th, acc);
+    acc = __builtin_fmaf(-g_hi, xc.shi, acc);
+    return acc;
+}
+
+template <int CTRL>
+__device__ inline float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave (DPP within 16-lane rows, then the four row
+// sums through scalar registers); the result is in every lane.
+__device__ inline float wave_sum(float v)
+{
+    v += dpp<0x128>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0xB1>(v);
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Fast path: n_in a multiple of 1024; CH chunk columns per lane, KS waves per
+// row group, R rows per wave, B batch rows.
+template <int B, int R, int CH, int KS>
+__global__ __launch_bounds__(256) void q4k_gemv_fast(Q4KArgs a)
+{
+    constexpr int GROUPS = 4 / KS;
+    constexpr bool XREG = B * CH <= 4;
+    __shared__ float part[KS > 1 ? 4 : 1][R][B];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = w / KS, ks = w % KS;
+    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * R;
+    const int cbase = ks * CH;
+    const int64_t nsb = a.n_in >> 8;
+
+    const float* xrow[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) xrow[b] = a.x + (int64_t)(b < a.batch ? b : a.batch - 1) * a.n_in;
+
+    XChunk xr[XREG ? CH : 1][XREG ? B : 1];
+    if constexpr (XREG) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+#pragma unroll
+            for (int b = 0; b < B; ++b) load_xchunk(xrow[b], lane + 64 * (cbase + k), xr[k][b]);
+    }
+
+    const uint8_t* qrow[R];
+    const uint32_t* dmrow[R];
+    const uint32_t* smrow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t rw = row0 + r;
+        const int64_t rr = rw < a.n_out ? rw : a.n_out - 1;
+        qrow[r] = a.qs + rr * (a.n_in >> 1);
+        dmrow[r] = a.dm + rr * nsb;
+        smrow[r] = a.sm + rr * nsb * 4;
+    }
+    uint32_t dmv[CH][R], smv[CH][R];
+    u32x2 qv[CH][R];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int c = lane + 64 * (cbase + k);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            dmv[k][r] = stream_load4(dmrow[r] + (c >> 4));
+            smv[k][r] = stream_load4(smrow[r] + ((c >> 4) << 2) + ((c & 15) >> 2));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+#pragma unroll
+        for (int r = 0; r < R; ++r) qv[k][r] = stream_load8(qrow[r] + (int64_t)(lane + 64 * (cbase + k)) * 8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    if constexpr (XREG) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+#pragma unroll
+            for (int b = 0; b < B; ++b) sum_xchunk(xr[k][b]);
+    }
+
+    float acc[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            XChunk xc;
+            if constexpr (XREG) {
+                xc = xr[XREG ? k : 0][XREG ? b : 0];
+            } else {
+                load_xchunk(xrow[b], lane + 64 * (cbase + k), xc);
+                sum_xchunk(xc);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r][b] = chunk_dot(qv[k][r], dmv[k][r], smv[k][r], xc, acc[r][b]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = wave_sum(acc[r][b]);
+
+    if constexpr (KS > 1) {
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int b = 0; b < B; ++b) part[w][r][b] = acc[r][b];
+        }
+        __syncthreads();
+        if (ks != 0) return;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                float v = part[w][r][b];
+#pragma unroll
+                for (int k = 1; k < KS; ++k) v += part[w + k][r][b];
+                acc[r][b] = v;
+            }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            if (lane == r * B + b && b < a.batch && row0 + r < a.n_out)
+                a.out[(int64_t)b * a.n_out + row0 + r] = acc[r][b];
+}
+
+// General path: row groups of LPR lanes, bounds-checked chunk loop.
+template <int B>
+__global__ __launch_bounds__(256) void q4k_gemv_general(Q4KArgs a)
 {
     const int lpr = 1 << a.lpr_log2;
     const int lane = threadIdx.x & 63;
@@ -74,133 +262,59 @@ __global__ __launch_bounds__(256) void q4k_gemv_kernel(Q4KArgs a)
     const int j = lane & (lpr - 1);
     const int groups = 64 >> a.lpr_log2;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const int64_t row0 = wave * groups * R;
     const int64_t nsb = a.n_in >> 8;
-
-    const uint8_t* qrow[R];
-    const uint4* mrow[R];
-    int64_t rowid[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t row = row0 + (int64_t)r * groups + g;
-        rowid[r] = row;
-        const int64_t rr = row < a.n_out ? row : a.n_out - 1;
-        qrow[r] = a.qs + rr * (a.n_in >> 1);
-        mrow[r] = a.meta + rr * nsb;
-    }
+    const int64_t row = wave * groups + g;
+    const int64_t rr = row < a.n_out ? row : a.n_out - 1;
+    const uint8_t* qrow = a.qs + rr * (a.n_in >> 1);
+    const uint32_t* dmrow = a.dm + rr * nsb;
+    const uint32_t* smrow = a.sm + rr * nsb * 4;
     const float* xrow[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) xrow[b] = a.x + (int64_t)(b < a.batch ? b : a.batch - 1) * a.n_in;
-
-    float acc[R][B];
+    float acc[B];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-
-    const int nk = NCH > 0 ? NCH : (a.nch + lpr - 1) >> a.lpr_log2;
-#pragma unroll
-    for (int kc = 0; kc < (NCH > 0 ? NCH : 1); ++kc) {
-        for (int kk = 0; kk < (NCH > 0 ? 1 : nk); ++kk) {
-            const int c = j + ((NCH > 0 ? kc : kk) << a.lpr_log2);
-            if (NCH == 0 && c >= a.nch) break;
-            const int sb = c >> 3;
-            const int cc = c & 7;
-            const int p = cc >> 1, h = cc & 1;
-            uint4 qv[R], mv[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                qv[r] = *reinterpret_cast<const uint4*>(qrow[r] + (int64_t)c * 16);
-                mv[r] = mrow[r][sb];
-            }
-            // per-row sub-block factors (independent of the batch row)
-            float f_lo[R], g_lo[R], f_hi[R], g_hi[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float d = fp16_bits_to_f32((uint16_t)(mv[r].x & 0xffff));
-                const float dmin = fp16_bits_to_f32((uint16_t)(mv[r].x >> 16));
-                float sc, mn;
-                scale_min(mv[r], 2 * p, sc, mn);
-                f_lo[r] = d * sc;
-                g_lo[r] = dmin * mn;
-                scale_min(mv[r], 2 * p + 1, sc, mn);
-                f_hi[r] = d * sc;
-                g_hi[r] = dmin * mn;
-            }
-            const int64_t xoff = (int64_t)sb * 256 + 64 * p + 16 * h;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float xl[16], xh[16];
-                const float4* pl = reinterpret_cast<const float4*>(xrow[b] + xoff);
-                const float4* ph = reinterpret_cast<const float4*>(xrow[b] + xoff + 32);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float4 v = pl[k], u = ph[k];
-                    xl[4 * k] = v.x; xl[4 * k + 1] = v.y; xl[4 * k + 2] = v.z; xl[4 * k + 3] = v.w;
-                    xh[4 * k] = u.x; xh[4 * k + 1] = u.y; xh[4 * k + 2] = u.z; xh[4 * k + 3] = u.w;
-                }
-                float sl = xl[0], sh = xh[0];
-#pragma unroll
-                for (int t = 1; t < 16; ++t) {
-                    sl += xl[t];
-                    sh += xh[t];
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint32_t w4[4] = {qv[r].x, qv[r].y, qv[r].z, qv[r].w};
-                    float tl = 0.0f, th = 0.0f;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t lo = w4[k] & 0x0f0f0f0fu;
-                        const uint32_t hi = (w4[k] >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            tl = __builtin_fmaf((float)((lo >> (8 * t)) & 0xffu), xl[4 * k + t], tl);
-                            th = __builtin_fmaf((float)((hi >> (8 * t)) & 0xffu), xh[4 * k + t], th);
-                        }
-                    }
-                    float v = acc[r][b];
-                    v = __builtin_fmaf(f_lo[r], tl, v);
-                    v = __builtin_fmaf(-g_lo[r], sl, v);
-                    v = __builtin_fmaf(f_hi[r], th, v);
-                    v = __builtin_fmaf(-g_hi[r], sh, v);
-                    acc[r][b] = v;
-                }
-            }
-        }
-    }
-
-    for (int off = lpr >> 1; off > 0; off >>= 1) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] += __shfl_xor(acc[r][b], off);
-    }
-    if (j != 0) return;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (rowid[r] >= a.n_out) continue;
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    for (int c = j; c < a.nch; c += lpr) {
+        const uint32_t dm = stream_load4(dmrow + (c >> 4));
+        const uint32_t sm = stream_load4(smrow + ((c >> 4) << 2) + ((c & 15) >> 2));
+        const u32x2 q = stream_load8(qrow + (int64_t)c * 8);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            if (b >= a.batch) break;
-            a.out[(int64_t)b * a.n_out + rowid[r]] = acc[r][b];
+            XChunk xc;
+            load_xchunk(xrow[b], c, xc);
+            sum_xchunk(xc);
+            acc[b] = chunk_dot(q, dm, sm, xc, acc[b]);
         }
     }
+    for (int off = lpr >> 1; off > 0; off >>= 1) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] += __shfl_xor(acc[b], off);
+    }
+    if (j != 0 || row >= a.n_out) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+        if (b < a.batch) a.out[(int64_t)b * a.n_out + row] = acc[b];
 }
 
 using KernelFn = void (*)(Q4KArgs);
 
 template <int B, int R>
-KernelFn pick_nch(int n)
+KernelFn pick_split(int nch64)
 {
-    switch (n) {
-        case 1: return q4k_gemv_kernel<B, R, 1>;
-        case 2: return q4k_gemv_kernel<B, R, 2>;
-        case 3: return q4k_gemv_kernel<B, R, 3>;
-        case 4: return q4k_gemv_kernel<B, R, 4>;
-        default: return q4k_gemv_kernel<B, R, 0>;
+    switch (nch64) {
+        case 1: return q4k_gemv_fast<B, R, 1, 1>;
+        case 2: return q4k_gemv_fast<B, R, 2, 1>;
+        case 3: return q4k_gemv_fast<B, R, 3, 1>;
+        case 4: return q4k_gemv_fast<B, R, 2, 2>;
+        case 6: return q4k_gemv_fast<B, R, 3, 2>;
+        case 8: return q4k_gemv_fast<B, R, 2, 4>;
+        case 12: return q4k_gemv_fast<B, R, 3, 4>;
+        case 16: return q4k_gemv_fast<B, R, 4, 4>;
+        default: return nullptr;
     }
 }
+
+int split_ks(int nch64) { return nch64 <= 3 ? 1 : (nch64 <= 6 ? 2 : 4); }
 
 }  // namespace
 
@@ -209,43 +323,58 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
 {
     Q4KArgs a{};
     a.qs = w.qs;
-    a.meta = w.meta;
+    a.dm = w.dm;
+    a.sm = w.sm;
     a.out = out;
     a.x = x;
     a.n_in = n_in;
     a.n_out = n_out;
     a.batch = (int)batch;
-    a.nch = (int)(n_in / 32);
-    // Largest power-of-two lane count (<= 64) that divides the chunk count, so
-    // that row groups cover whole rows without a ragged tail when possible.
-    int lpr_log2 = 6;
-    while (lpr_log2 > 3 && (a.nch % (1 << lpr_log2)) != 0) --lpr_log2;
-    if (a.nch % (1 << lpr_log2) != 0) lpr_log2 = 6;
-    int nch_per_lane = a.nch % (1 << lpr_log2) == 0 ? a.nch >> lpr_log2 : 0;
-    if (nch_per_lane > 4) nch_per_lane = 0;
-    a.lpr_log2 = lpr_log2;
-    const int groups = 64 >> lpr_log2;
-
+    a.nch = (int)(n_in / 16);
     const int bt = a.batch <= 1 ? 1 : a.batch <= 2 ? 2 : a.batch <= 4 ? 4 : 8;
-    int r = 4;
-    while (r > 1 && n_out / ((int64_t)groups * r) < 1024 * (r == 4 ? 2 : 1)) r >>= 1;
-    KernelFn fn;
-    int r_eff = r;
-    switch (bt) {
-        case 1: fn = r == 4 ? pick_nch<1, 4>(nch_per_lane) : r == 2 ? pick_nch<1, 2>(nch_per_lane)
-                                                                   : pick_nch<1, 1>(nch_per_lane);
-            break;
-        case 2: fn = r >= 2 ? pick_nch<2, 2>(nch_per_lane) : pick_nch<2, 1>(nch_per_lane);
-            r_eff = r >= 2 ? 2 : 1;
-            break;
-        case 4: fn = r >= 2 ? pick_nch<4, 2>(nch_per_lane) : pick_nch<4, 1>(nch_per_lane);
-            r_eff = r >= 2 ? 2 : 1;
-            break;
-        default: fn = pick_nch<8, 1>(nch_per_lane); r_eff = 1; break;
+    const int nch64 = a.nch % 64 == 0 ? a.nch / 64 : 0;
+    KernelFn fn = nullptr;
+    int64_t blocks = 0;
+    if (nch64 > 0) {
+        const int ks = split_ks(nch64);
+        const int groups = 4 / ks;
+        int r = 4;
+        while (r > 1 && n_out / ((int64_t)groups * r) < 512) r >>= 1;
+        int r_eff = r;
+        switch (bt) {
+            case 1:
+                fn = r == 4 ? pick_split<1, 4>(nch64) : (r == 2 ? pick_split<1, 2>(nch64) : pick_split<1, 1>(nch64));
+                break;
+            case 2:
+                fn = r >= 2 ? pick_split<2, 2>(nch64) : pick_split<2, 1>(nch64);
+                r_eff = r >= 2 ? 2 : 1;
+                break;
+            case 4:
+                fn = r >= 2 ? pick_split<4, 2>(nch64) : pick_split<4, 1>(nch64);
+                r_eff = r >= 2 ? 2 : 1;
+                break;
+            default:
+                fn = pick_split<8, 1>(nch64);
+                r_eff = 1;
+                break;
+        }
+        const int64_t rows_per_block = (int64_t)groups * r_eff;
+        blocks = (n_out + rows_per_block - 1) / rows_per_block;
     }
-    const int64_t rows_per_wave = (int64_t)groups * r_eff;
-    const int64_t waves = (n_out + rows_per_wave - 1) / rows_per_wave;
-    hipLaunchKernelGGL(fn, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+    if (!fn) {
+        int lpr_log2 = 6;
+        while (lpr_log2 > 1 && (1 << lpr_log2) > a.nch) --lpr_log2;
+        a.lpr_log2 = lpr_log2;
+        switch (bt) {
+            case 1: fn = q4k_gemv_general<1>; break;
+            case 2: fn = q4k_gemv_general<2>; break;
+            case 4: fn = q4k_gemv_general<4>; break;
+            default: fn = q4k_gemv_general<8>; break;
+        }
+        const int64_t rows_per_wave = 64 >> lpr_log2;
+        blocks = ((n_out + rows_per_wave - 1) / rows_per_wave + 3) / 4;
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, s, a);
     count_launch();
     return hipGetLastError();
 }

@@ -238,21 +238,51 @@ __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
             for (int b = 0; b < B; ++b) acc[r][m][b] = 0.0f;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
+        if constexpr (B == 1) {
+            // one batch row: convert and multiply in one pass
             float xv[16];
             if constexpr (XREG) {
 #pragma unroll
-                for (int t = 0; t < 16; ++t) xv[t] = xr[XREG ? k : 0][XREG ? b : 0][t];
+                for (int t = 0; t < 16; ++t) xv[t] = xr[XREG ? k : 0][0][t];
             } else {
-                load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xv);
+                load_x16(xrow[0] + (int64_t)(lane + 64 * (cbase + k)) * 16, xv);
             }
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
-                    acc[r][m][b] = __builtin_fmaf(fp16_bits_to_f32(dv[k][r][m]), dot16(qv[k][r][m], xv),
-                                                  acc[r][m][b]);
+                    acc[r][m][0] = __builtin_fmaf(fp16_bits_to_f32(dv[k][r][m]), dot16(qv[k][r][m], xv),
+                                                  acc[r][m][0]);
+        } else {
+            // several batch rows: convert each weight once, then B dot products
+            float qf[R][NM][16];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    const uint32_t wd[4] = {qv[k][r][m].x, qv[k][r][m].y, qv[k][r][m].z, qv[k][r][m].w};
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) qf[r][m][t] = (float)(int8_t)((wd[t >> 2] >> (8 * (t & 3))) & 0xff);
+                }
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                float xv[16];
+                if constexpr (XREG) {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) xv[t] = xr[XREG ? k : 0][XREG ? b : 0][t];
+                } else {
+                    load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xv);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        float t = qf[r][m][0] * xv[0];
+#pragma unroll
+                        for (int i = 1; i < 16; ++i) t = __builtin_fmaf(qf[r][m][i], xv[i], t);
+                        acc[r][m][b] = __builtin_fmaf(fp16_bits_to_f32(dv[k][r][m]), t, acc[r][m][b]);
+                    }
+            }
         }
     }
 #pragma unroll
@@ -373,33 +403,34 @@ KernelFn pick_split(int nch64)
 
 int split_ks(int nch64) { return nch64 <= 3 ? 1 : (nch64 <= 6 ? 2 : 4); }
 
-// R actually instantiated for (mode, bt, requested r).
+// R actually instantiated for (mode, requested r): SwiGLU streams two
+// matrices per row, so it takes at most two rows.
 int fast_r(GemvMode mode, int bt, int r)
 {
-    if (mode == kSwiGLU) return bt == 1 ? (r >= 2 ? 2 : 1) : 1;
-    if (bt == 1) return r;
-    if (bt == 8) return 1;
-    return r >= 2 ? 2 : 1;
+    (void)bt;
+    if (mode == kSwiGLU) return r >= 2 ? 2 : 1;
+    return r;
+}
+
+template <int MODE, int B>
+KernelFn pick_rows(int r, int nch64)
+{
+    if constexpr (MODE == kSwiGLU) {
+        return r >= 2 ? pick_split<MODE, B, 2>(nch64) : pick_split<MODE, B, 1>(nch64);
+    } else {
+        return r == 4 ? pick_split<MODE, B, 4>(nch64)
+                      : (r == 2 ? pick_split<MODE, B, 2>(nch64) : pick_split<MODE, B, 1>(nch64));
+    }
 }
 
 template <int MODE>
 KernelFn pick_fast(int bt, int r, int nch64)
 {
-    if constexpr (MODE == kSwiGLU) {
-        switch (bt) {
-            case 1: return r >= 2 ? pick_split<MODE, 1, 2>(nch64) : pick_split<MODE, 1, 1>(nch64);
-            case 2: return pick_split<MODE, 2, 1>(nch64);
-            case 4: return pick_split<MODE, 4, 1>(nch64);
-            default: return pick_split<MODE, 8, 1>(nch64);
-        }
-    } else {
-        switch (bt) {
-            case 1: return r == 4 ? pick_split<MODE, 1, 4>(nch64)
-                                  : (r == 2 ? pick_split<MODE, 1, 2>(nch64) : pick_split<MODE, 1, 1>(nch64));
-            case 2: return r >= 2 ? pick_split<MODE, 2, 2>(nch64) : pick_split<MODE, 2, 1>(nch64);
-            case 4: return r >= 2 ? pick_split<MODE, 4, 2>(nch64) : pick_split<MODE, 4, 1>(nch64);
-            default: return pick_split<MODE, 8, 1>(nch64);
-        }
+    switch (bt) {
+        case 1: return pick_rows<MODE, 1>(r, nch64);
+        case 2: return pick_rows<MODE, 2>(r, nch64);
+        case 4: return pick_rows<MODE, 4>(r, nch64);
+        default: return pick_rows<MODE, 8>(r, nch64);
     }
 }
 

@@ -17,10 +17,14 @@ namespace qdec {
 // Total bytes = n_out*n_in*17/16 (the GGML size) plus plane alignment.
 //
 // Repacked Q4_K matrix:
-//   qs plane   : n_out rows x n_in/2 bytes of nibbles, in GGML order within each
-//                super-block (128 bytes per super-block).
-//   meta plane : n_out rows x (n_in/256) 16-byte headers = the first 16 bytes of
-//                the GGML super-block (fp16 d, fp16 dmin, 12 packed scale bytes).
+//   qs plane : n_out rows x n_in/2 bytes of nibbles, in GGML order within each
+//              super-block (128 bytes per super-block).
+//   dm plane : n_out rows x (n_in/256) words, d | dmin << 16 (fp16 bits).
+//   sm plane : n_out rows x (n_in/256) x 4 words; word p holds the unpacked
+//              6-bit scales and mins of sub-blocks 2p and 2p+1:
+//              sc[2p] | sc[2p+1] << 8 | m[2p] << 16 | m[2p+1] << 24.
+//   (148 bytes per 256 weights instead of 144: the scales are unpacked once
+//   here so the GEMV does not decode the 6-bit packing per lane.)
 struct Q8View {
     const int8_t* q;
     const uint16_t* d;
@@ -28,7 +32,8 @@ struct Q8View {
 
 struct Q4KView {
     const uint8_t* qs;
-    const uint4* meta;
+    const uint32_t* dm;
+    const uint32_t* sm;
 };
 
 constexpr int64_t kAlign = 256;
@@ -49,14 +54,18 @@ inline Q8View q8_view(const void* base, int64_t n_in, int64_t n_out)
 
 inline int64_t q4k_plane_bytes(int64_t n_in, int64_t n_out)
 {
-    return align_up(n_out * (n_in / 2), kAlign) + align_up(n_out * (n_in / 256) * 16, kAlign);
+    const int64_t nsb = n_out * (n_in / 256);
+    return align_up(n_out * (n_in / 2), kAlign) + align_up(nsb * 4, kAlign) + align_up(nsb * 16, kAlign);
 }
 
 inline Q4KView q4k_view(const void* base, int64_t n_in, int64_t n_out)
 {
     const char* p = static_cast<const char*>(base);
-    return Q4KView{reinterpret_cast<const uint8_t*>(p),
-                   reinterpret_cast<const uint4*>(p + align_up(n_out * (n_in / 2), kAlign))};
+    const int64_t nsb = n_out * (n_in / 256);
+    const int64_t off_dm = align_up(n_out * (n_in / 2), kAlign);
+    const int64_t off_sm = off_dm + align_up(nsb * 4, kAlign);
+    return Q4KView{reinterpret_cast<const uint8_t*>(p), reinterpret_cast<const uint32_t*>(p + off_dm),
+                   reinterpret_cast<const uint32_t*>(p + off_sm)};
 }
 
 // ------------------------------------------------------------- launchers --

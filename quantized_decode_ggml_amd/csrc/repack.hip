@@ -8,9 +8,10 @@
 //   Q4_K block, 144 bytes: fp16 d | fp16 dmin | 12 scale bytes | 128 nibble bytes
 //                                                          w = d*sc*q - dmin*m
 // The repack ("call once at plan build", preload_q4k_soa_weights on that page)
-// only moves bytes: the q bytes and nibbles go to one plane, the per-block
-// headers to another, so every row starts on a 16-byte boundary and the hot
-// kernels read each row with aligned 16-byte loads.
+// splits each block into planes: the q bytes and nibbles go to one plane, the
+// scales to others, so every row starts on a 16-byte boundary and the hot
+// kernels read rows with aligned wide loads.  It moves bytes, except that the
+// Q4_K 6-bit scales and mins are unpacked to one byte each.
 #include "qdec_internal.h"
 
 namespace qdec {
@@ -49,11 +50,28 @@ __global__ __launch_bounds__(256) void repack_q8_0_kernel(const uint16_t* __rest
     dp[blk] = src[0];
 }
 
-// One thread per Q4_K super-block (72 halfwords).
+// 6-bit scale and min of sub-block s from the 12 packed bytes (GGML K-quant
+// packing): sub-blocks 0-3 use the low 6 bits of bytes s and s+4; sub-blocks
+// 4-7 take their low 4 bits from byte s+4 (scale: low nibble, min: high
+// nibble) and their high 2 bits from the top of bytes s-4 (scale) and s (min).
+__device__ inline void unpack_scale_min(const uint8_t (&b)[12], int s, uint32_t& sc, uint32_t& mn)
+{
+    if (s < 4) {
+        sc = b[s] & 63u;
+        mn = b[s + 4] & 63u;
+    } else {
+        sc = (b[s + 4] & 15u) | ((uint32_t)(b[s - 4] >> 6) << 4);
+        mn = (uint32_t)(b[s + 4] >> 4) | ((uint32_t)(b[s] >> 6) << 4);
+    }
+}
+
+// One thread per Q4_K super-block (72 halfwords): nibbles to the qs plane,
+// d|dmin to the dm plane, unpacked scales and mins to the sm plane.
 __global__ __launch_bounds__(256) void repack_q4k_kernel(const uint16_t* __restrict__ raw,
                                                          int64_t nblocks,
                                                          uint8_t* __restrict__ qsp,
-                                                         uint4* __restrict__ meta)
+                                                         uint32_t* __restrict__ dmp,
+                                                         uint32_t* __restrict__ smp)
 {
     const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blk >= nblocks) return;
@@ -62,7 +80,17 @@ __global__ __launch_bounds__(256) void repack_q4k_kernel(const uint16_t* __restr
 #pragma unroll
     for (int k = 0; k < 36; ++k)
         words[k] = (uint32_t)src[2 * k] | ((uint32_t)src[2 * k + 1] << 16);
-    meta[blk] = make_uint4(words[0], words[1], words[2], words[3]);
+    dmp[blk] = words[0];
+    uint8_t sb[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) sb[k] = (uint8_t)(words[1 + k / 4] >> (8 * (k % 4)));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t sc0, m0, sc1, m1;
+        unpack_scale_min(sb, 2 * p, sc0, m0);
+        unpack_scale_min(sb, 2 * p + 1, sc1, m1);
+        smp[blk * 4 + p] = sc0 | (sc1 << 8) | (m0 << 16) | (m1 << 24);
+    }
     // n_in/2 bytes per row and 128 per super-block: super-block blk's nibbles
     // land at byte blk*128 of the qs plane.
     uint4* dst = reinterpret_cast<uint4*>(qsp + blk * 128);
@@ -92,26 +120,6 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(Q8View w, int64_t n_i
     (void)n_in;
 }
 
-__device__ inline uint32_t byte_of(uint4 m, int idx)
-{
-    // idx indexes the 12 scale bytes that follow d and dmin in the header.
-    const uint32_t word = idx < 4 ? m.y : (idx < 8 ? m.z : m.w);
-    return (word >> (8 * (idx & 3))) & 0xffu;
-}
-
-// 6-bit scale and min of sub-block s (GGML K-quant packing).
-__device__ inline void q4k_scale_min(uint4 m, int s, uint32_t& sc, uint32_t& mn)
-{
-    if (s < 4) {
-        sc = byte_of(m, s) & 63u;
-        mn = byte_of(m, s + 4) & 63u;
-    } else {
-        const uint32_t lo = byte_of(m, s + 4);
-        sc = (lo & 15u) | ((byte_of(m, s - 4) >> 6) << 4);
-        mn = (lo >> 4) | ((byte_of(m, s) >> 6) << 4);
-    }
-}
-
 // One thread per 16 nibble bytes (32 weights: 16 in sub-block 2p, 16 in 2p+1).
 __global__ __launch_bounds__(256) void dequant_q4k_kernel(Q4KView w, int64_t n_in, int64_t nchunks,
                                                           float* __restrict__ out)
@@ -121,14 +129,12 @@ __global__ __launch_bounds__(256) void dequant_q4k_kernel(Q4KView w, int64_t n_i
     const int64_t sbg = c >> 3;          // global super-block index
     const int cc = (int)(c & 7);
     const int p = cc >> 1, h = cc & 1;
-    const uint4 m = w.meta[sbg];
-    const float d = fp16_bits_to_f32((uint16_t)(m.x & 0xffff));
-    const float dmin = fp16_bits_to_f32((uint16_t)(m.x >> 16));
-    uint32_t sc0, m0, sc1, m1;
-    q4k_scale_min(m, 2 * p, sc0, m0);
-    q4k_scale_min(m, 2 * p + 1, sc1, m1);
-    const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
-    const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
+    const uint32_t dm = w.dm[sbg];
+    const float d = fp16_bits_to_f32((uint16_t)(dm & 0xffff));
+    const float dmin = fp16_bits_to_f32((uint16_t)(dm >> 16));
+    const uint32_t sm = w.sm[sbg * 4 + p];
+    const float a0 = d * (float)(sm & 0xff), b0 = dmin * (float)((sm >> 16) & 0xff);
+    const float a1 = d * (float)((sm >> 8) & 0xff), b1 = dmin * (float)(sm >> 24);
     const uint4 qv = *reinterpret_cast<const uint4*>(w.qs + c * 16);
     const uint32_t words[4] = {qv.x, qv.y, qv.z, qv.w};
     // flattened element index of the first low-nibble weight
@@ -180,8 +186,8 @@ hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, vo
     const Q4KView v = q4k_view(dst, n_in, n_out);
     const int64_t nblocks = (n_in / 256) * n_out;
     hipLaunchKernelGGL(repack_q4k_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t*>(raw), nblocks,
-                       const_cast<uint8_t*>(v.qs), const_cast<uint4*>(v.meta));
+                       reinterpret_cast<const uint16_t*>(raw), nblocks, const_cast<uint8_t*>(v.qs),
+                       const_cast<uint32_t*>(v.dm), const_cast<uint32_t*>(v.sm));
     count_launch();
     return hipGetLastError();
 }
