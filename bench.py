@@ -13,8 +13,8 @@ Infinity Cache), so the bytes come from HBM as in a real decode.
 value = algorithmic bytes per step (GGML weight bytes + x + out + residual)
         / wall time per step, in GB/s, inputs resident in HBM.
 roofline = the dominant kernel's algorithmic bytes per launch / its mean
-        launch duration (HIP events around `steps` back-to-back launches on
-        the launch stream), against 8 TB/s.
+        launch duration (HIP events around a replayed graph of `steps`
+        launches of that kernel), against 8 TB/s.
 cpu_baseline = the CPU oracle (single thread) on a bounded sample of steps.
 """
 from __future__ import annotations
@@ -84,9 +84,9 @@ def cpu_baseline(w, x, budget_s=12.0):
 
 def suite(args):
     """Every workload configuration through the library, one line of JSON each
-    (to stdout): mean kernel time from HIP events around each launch, over
-    rotated weight copies (>= 512 MB per workload), GB/s of algorithmic bytes
-    and, for the batched GEMMs, TFLOP/s."""
+    (to stdout): mean launch duration of graph-replayed launches on rotated
+    weight copies (>= 512 MB per workload), GB/s of algorithmic bytes and, for
+    the batched GEMMs, TFLOP/s."""
     import numpy as np
     import torch
 
@@ -100,22 +100,34 @@ def suite(args):
         return max(2, -(-(512 << 20) // max(nbytes, 1)))
 
     def timed(name, launches, nbytes, flops=None, iters=100, warm=20, extra=None):
+        """Mean launch duration: `iters` launches (rotating over the weight
+        copies) captured into one HIP graph, replayed, bracketed by HIP events
+        on the replay stream; host launch costs stay out of the device timeline."""
+        nonlocal stream
         n = len(launches)
         for i in range(warm):
             launches[i % n]()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-        for i, (s0, s1) in enumerate(ev):
-            s0.record(stream)
-            launches[i % n]()
-            s1.record(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            stream = torch.cuda.current_stream()
+            for i in range(iters):
+                launches[i % n]()
+        stream = torch.cuda.current_stream()
+        g.replay()
         torch.cuda.synchronize()
-        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-        rec = {"workload": name, "mean_us": round(float(us.mean()), 3), "median_us": round(float(np.median(us)), 3),
-               "bytes": int(nbytes), "gbs": round(nbytes / (us.mean() * 1e-6) / 1e9, 1),
-               "pct_hbm": round(100 * nbytes / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        rec = {"workload": name, "mean_us": round(us, 3), "bytes": int(nbytes),
+               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+               "pct_hbm": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
         if flops:
-            rec["tflops"] = round(flops / (us.mean() * 1e-6) / 1e12, 2)
+            rec["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
         if extra:
             rec.update(extra)
         print(json.dumps(rec), flush=True)
@@ -319,23 +331,27 @@ def main():
     wall_eager = time.perf_counter() - t0
     assert qd.launch_count() - launches0 == 3 * args.steps, "not every product ran in libqdec"
 
-    # timed region 2: each product alone, `steps` launches back to back over the
-    # rotated layers, bracketed by HIP events on the launch stream: the mean
-    # launch duration of that kernel (launch gaps included, so slightly above
-    # the profiler's kernel duration).
+    # timed region 2: each product alone, `steps` launches over the rotated
+    # layers captured into one HIP graph and replayed, bracketed by HIP events
+    # on the replay stream: the mean launch duration of that kernel (launch
+    # gaps included, so slightly above the profiler's kernel duration).
     per_kernel = {}
     sb = step_bytes()
     for n in names:
-        fns = [lambda i=i, n=n: single(n, i) for i in range(LAYERS)]
-        for i in range(LAYERS):
-            fns[i]()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            stream = torch.cuda.current_stream()
+            for i in range(args.steps):
+                single(n, i)
+        stream = torch.cuda.current_stream()
+        g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
-            fns[i % LAYERS]()
+        g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
+        del g
         us = e0.elapsed_time(e1) * 1e3 / args.steps
         per_kernel[n] = {"mean_us": round(us, 3), "bytes": sb[n], "gbs": round(sb[n] / (us * 1e-6) / 1e9, 1)}
     dom = max(names, key=lambda n: per_kernel[n]["mean_us"])

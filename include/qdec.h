@@ -36,6 +36,8 @@
  *     copy is keyed by (device, pointer, type, n_in, n_out); the caller promises
  *     that the bytes behind a cached pointer do not change until qdec_release
  *     or qdec_clear_cache ("immutable", [cuda_lane] preload_resident_blob).
+ *     Inside HIP stream capture no copy can be made (QDEC_EINVAL): prepare or
+ *     use every weight once before capturing.
  *   - Return value: QDEC_OK (0) or a negative qdec_status.  Invalid arguments
  *     are rejected with QDEC_EINVAL before any HIP call; a failed allocation
  *     returns QDEC_ENOMEM; a failed launch or HIP call returns QDEC_EHIP.

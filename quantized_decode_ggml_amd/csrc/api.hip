@@ -87,9 +87,17 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     const Key key{dev, reinterpret_cast<uintptr_t>(w), type, n_in, n_out};
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &capture) != hipSuccess) {
+        (void)hipGetLastError();
+        capture = hipStreamCaptureStatusNone;
+    }
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_cache.find(key);
     if (it == g_cache.end()) {
+        // a repack allocates device memory, which a captured graph cannot do
+        if (capture != hipStreamCaptureStatusNone)
+            return fail(QDEC_EINVAL, "weight %p has no repacked copy: call qdec_prepare before graph capture", w);
         if (fail_alloc_hook()) return fail(QDEC_ENOMEM, "repack allocation refused (QDEC_FAIL_ALLOC=1)");
         Entry ent;
         ent.bytes = type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out) : q4k_plane_bytes(n_in, n_out);
@@ -113,7 +121,12 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
     }
     Entry& ent = it->second;
     if (!ent.done) {
-        if (hipEventQuery(ent.ready) == hipSuccess) {
+        if (capture != hipStreamCaptureStatusNone) {
+            // no cross-stream waits inside a capture: finish the repack on the host
+            e = hipEventSynchronize(ent.ready);
+            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            ent.done = true;
+        } else if (hipEventQuery(ent.ready) == hipSuccess) {
             ent.done = true;
         } else if (s != ent.made_on) {
             e = hipStreamWaitEvent(s, ent.ready, 0);

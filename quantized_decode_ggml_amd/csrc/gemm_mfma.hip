@@ -15,11 +15,19 @@
 // single-token path; bf16 keeps the f32 exponent range, and the error per
 // product is at most about 2*2^-9 relative.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C; each of its
-// four waves computes 64 x 64 with 4 x 4 MFMA 16x16x32 tiles.  K advances 64
-// at a time (two Q8_0 blocks).  Both operands are staged in LDS as bf16 rows
-// (K contiguous, padded by 8 elements against bank conflicts), double-buffered:
-// the global loads of step k+1 are in flight while step k runs on MFMA.
+// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C over a slice
+// of K; each of its four waves computes 64 x 64 with 4 x 4 MFMA 16x16x32
+// tiles.  K advances 64 at a time (two Q8_0 blocks).  Both operands are staged
+// in LDS as bf16 rows (K contiguous, padded by 8 elements against bank
+// conflicts), double-buffered: the global loads of step k+1 are in flight
+// while step k runs on MFMA.
+//
+// Parallelism: with few output tiles (the prefill batch is 128 or 512 rows) K
+// is split into S slices so that the grid has at least about two workgroups
+// per CU; the slices add their partial tiles into the output with
+// fire-and-forget f32 atomics (a fill kernel zeroes the output first).  The
+// workgroup order places the slices of one output tile and neighbouring tiles
+// on the same XCD, whose L2 then serves the shared x rows.
 #include "qdec_internal.h"
 
 namespace qdec {
@@ -40,6 +48,10 @@ struct GemmArgs {
     const float* wf;       // dense f32 W (N x K) or nullptr
     float* out;            // M x N f32
     int64_t M, N, K;
+    int64_t mtiles, ntiles;
+    int64_t kslice;        // K per split (multiple of BK)
+    int splits;
+    int xcd_remap;         // 1: remap block ids so consecutive tiles share an XCD
 };
 
 __device__ inline float fp16_bits_to_f32(uint16_t h)
@@ -62,14 +74,14 @@ __device__ inline bf16x4 to_bf16x4(float4 v)
 // Global -> register staging of one 128 x 64 f32 tile (rows r0.., cols k0..):
 // 2048 float4, 8 per thread, consecutive threads on consecutive float4s.
 __device__ inline void load_f32_tile(const float* __restrict__ src, int64_t rows, int64_t K,
-                                     int64_t r0, int64_t k0, float4 (&reg)[8])
+                                     int64_t kend, int64_t r0, int64_t k0, float4 (&reg)[8])
 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int idx = threadIdx.x + 256 * i;
         const int row = idx >> 4, c4 = idx & 15;
         const int64_t gr = r0 + row, gk = k0 + c4 * 4;
-        reg[i] = (gr < rows && gk < K) ? *reinterpret_cast<const float4*>(src + gr * K + gk)
+        reg[i] = (gr < rows && gk < kend) ? *reinterpret_cast<const float4*>(src + gr * K + gk)
                                        : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
@@ -91,11 +103,11 @@ struct QTileReg {
     uint16_t d;
 };
 
-__device__ inline void load_q8_tile(const GemmArgs& a, int64_t n0, int64_t k0, QTileReg& reg)
+__device__ inline void load_q8_tile(const GemmArgs& a, int64_t kend, int64_t n0, int64_t k0, QTileReg& reg)
 {
     const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
     const int64_t gn = n0 + row, gk = k0 + half * 32;
-    if (gn < a.N && gk < a.K) {
+    if (gn < a.N && gk < kend) {
         const uint4* p = reinterpret_cast<const uint4*>(a.q + gn * a.K + gk);
         reg.q0 = p[0];
         reg.q1 = p[1];
@@ -131,8 +143,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
     __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BN * LDK];
 
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    // block id -> (k slice, n tile, m tile), k fastest; with xcd_remap the ids
+    // that the dispatcher sends to one XCD (id % 8) get consecutive tiles
+    int64_t id = blockIdx.x;
+    if (a.xcd_remap) {
+        const int64_t per_xcd = (int64_t)gridDim.x / 8;
+        id = (id % 8) * per_xcd + id / 8;
+    }
+    const int64_t slice = id % a.splits;
+    const int64_t tile = id / a.splits;
+    const int64_t n0 = (tile % a.ntiles) * BN;
+    const int64_t m0 = (tile / a.ntiles) * BM;
+    const int64_t kbeg = slice * a.kslice;
+    const int64_t kend = kbeg + a.kslice < a.K ? kbeg + a.kslice : a.K;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -146,11 +169,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
     float4 xr[8];
     float4 wr[8];
     QTileReg qr;
-    const int64_t nk = (a.K + BK - 1) / BK;
+    const int64_t nk = (kend - kbeg + BK - 1) / BK;
 
-    load_f32_tile(a.x, a.M, a.K, m0, 0, xr);
-    if (QUANT) load_q8_tile(a, n0, 0, qr);
-    else load_f32_tile(a.wf, a.N, a.K, n0, 0, wr);
+    load_f32_tile(a.x, a.M, a.K, kend, m0, kbeg, xr);
+    if (QUANT) load_q8_tile(a, kend, n0, kbeg, qr);
+    else load_f32_tile(a.wf, a.N, a.K, kend, n0, kbeg, wr);
     store_f32_tile(As[0], xr);
     if (QUANT) store_q8_tile(Bs[0], qr);
     else store_f32_tile(Bs[0], wr);
@@ -160,10 +183,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
         const int cur = (int)(kt & 1);
         const bool more = kt + 1 < nk;
         if (more) {
-            const int64_t k0 = (kt + 1) * BK;
-            load_f32_tile(a.x, a.M, a.K, m0, k0, xr);
-            if (QUANT) load_q8_tile(a, n0, k0, qr);
-            else load_f32_tile(a.wf, a.N, a.K, n0, k0, wr);
+            const int64_t k0 = kbeg + (kt + 1) * BK;
+            load_f32_tile(a.x, a.M, a.K, kend, m0, k0, xr);
+            if (QUANT) load_q8_tile(a, kend, n0, k0, qr);
+            else load_f32_tile(a.wf, a.N, a.K, kend, n0, k0, wr);
         }
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
@@ -200,10 +223,61 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-                if (m < a.M) a.out[m * a.N + n] = acc[i][j][e];
+                if (m >= a.M) continue;
+                if (a.splits == 1) a.out[m * a.N + n] = acc[i][j][e];
+                else unsafeAtomicAdd(a.out + m * a.N + n, acc[i][j][e]);
             }
         }
     }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, int64_t n4, float* __restrict__ tail,
+                                                   int64_t ntail)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < ntail) tail[t] = 0.f;
+}
+
+// Grid plan: K slices so that tiles * slices reaches about 512 workgroups,
+// each slice at least 512 deep (8 K steps) and a multiple of BK.
+GemmArgs plan(int64_t M, int64_t N, int64_t K)
+{
+    GemmArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.mtiles = (M + BM - 1) / BM;
+    a.ntiles = (N + BN - 1) / BN;
+    const int64_t tiles = a.mtiles * a.ntiles;
+    int splits = 1;
+    while (tiles * splits < 512 && K / (splits * 2) >= 512) splits *= 2;
+    a.kslice = ((K + splits - 1) / splits + BK - 1) / BK * BK;
+    a.splits = (int)((K + a.kslice - 1) / a.kslice);
+    a.xcd_remap = (tiles * a.splits) % 8 == 0 ? 1 : 0;
+    return a;
+}
+
+hipError_t launch(GemmArgs& a, bool quant, hipStream_t s)
+{
+    if (a.splits > 1) {
+        const int64_t n = a.M * a.N;
+        const int64_t n4 = n / 4;
+        const int64_t ntail = n - n4 * 4;
+        int64_t blocks = (n4 + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        if (blocks < 1) blocks = 1;
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<float4*>(a.out), n4, a.out + n4 * 4, ntail);
+        count_launch();
+    }
+    const dim3 grid((unsigned)(a.mtiles * a.ntiles * a.splits));
+    if (quant) hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, dim3(256), 0, s, a);
+    count_launch();
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -211,21 +285,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                             float* out, hipStream_t s)
 {
-    GemmArgs a{x, w.q, w.d, nullptr, out, batch, n_out, n_in};
-    const dim3 grid((unsigned)((n_out + BN - 1) / BN), (unsigned)((batch + BM - 1) / BM));
-    hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, dim3(256), 0, s, a);
-    count_launch();
-    return hipGetLastError();
+    GemmArgs a = plan(batch, n_out, n_in);
+    a.x = x;
+    a.q = w.q;
+    a.d = w.d;
+    a.out = out;
+    return launch(a, true, s);
 }
 
 hipError_t launch_f32_gemm(const float* wf, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, hipStream_t s)
 {
-    GemmArgs a{x, nullptr, nullptr, wf, out, batch, n_out, n_in};
-    const dim3 grid((unsigned)((n_out + BN - 1) / BN), (unsigned)((batch + BM - 1) / BM));
-    hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, dim3(256), 0, s, a);
-    count_launch();
-    return hipGetLastError();
+    GemmArgs a = plan(batch, n_out, n_in);
+    a.x = x;
+    a.wf = wf;
+    a.out = out;
+    return launch(a, false, s);
 }
 
 }  // namespace qdec
