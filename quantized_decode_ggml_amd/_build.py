@@ -26,9 +26,13 @@ def hipcc() -> str:
 
 
 # No fast-math anywhere; packed f32 instructions are disabled on the device.
+# MFMA accumulators are kept in ordinary VGPRs: with the AGPR form the register
+# allocator rotates the loop-carried accumulators through v_accvgpr copies on
+# every K step, and each copy waits for the MFMA that produced its source.
 CXXFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-fvisibility=hidden", "-DQDEC_BUILDING",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

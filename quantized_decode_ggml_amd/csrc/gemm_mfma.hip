@@ -23,11 +23,13 @@
 // while step k runs on MFMA.
 //
 // Parallelism: with few output tiles (the prefill batch is 128 or 512 rows) K
-// is split into S slices so that the grid has at least about two workgroups
-// per CU; the slices add their partial tiles into the output with
-// fire-and-forget f32 atomics (a fill kernel zeroes the output first).  The
-// workgroup order places the slices of one output tile and neighbouring tiles
-// on the same XCD, whose L2 then serves the shared x rows.
+// is split into S slices so that the grid has at least one workgroup per CU;
+// the slices add their partial tiles into the output with fire-and-forget f32
+// atomics (a fill kernel zeroes the output first).  Each atomic costs far more
+// than a store, so S stays at the smallest value that fills the CUs.  Block
+// ids go to the XCDs round-robin, which spreads the m-tiles that share a
+// weight tile over all L2s (measured faster than grouping consecutive tiles
+// on one XCD).
 #include "qdec_internal.h"
 
 namespace qdec {
@@ -51,7 +53,6 @@ struct GemmArgs {
     int64_t mtiles, ntiles;
     int64_t kslice;        // K per split (multiple of BK)
     int splits;
-    int xcd_remap;         // 1: remap block ids so consecutive tiles share an XCD
 };
 
 __device__ inline float fp16_bits_to_f32(uint16_t h)
@@ -143,13 +144,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
     __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BN * LDK];
 
-    // block id -> (k slice, n tile, m tile), k fastest; with xcd_remap the ids
-    // that the dispatcher sends to one XCD (id % 8) get consecutive tiles
-    int64_t id = blockIdx.x;
-    if (a.xcd_remap) {
-        const int64_t per_xcd = (int64_t)gridDim.x / 8;
-        id = (id % 8) * per_xcd + id / 8;
-    }
+    // block id -> (k slice, n tile, m tile), k fastest
+    const int64_t id = blockIdx.x;
     const int64_t slice = id % a.splits;
     const int64_t tile = id / a.splits;
     const int64_t n0 = (tile % a.ntiles) * BN;
@@ -241,8 +237,8 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, int64
     if (t < ntail) tail[t] = 0.f;
 }
 
-// Grid plan: K slices so that tiles * slices reaches about 512 workgroups,
-// each slice at least 512 deep (8 K steps) and a multiple of BK.
+// Grid plan: K slices so that tiles * slices reaches 256 workgroups (one per
+// CU), each slice at least 512 deep (8 K steps) and a multiple of BK.
 GemmArgs plan(int64_t M, int64_t N, int64_t K)
 {
     GemmArgs a{};
@@ -253,10 +249,9 @@ GemmArgs plan(int64_t M, int64_t N, int64_t K)
     a.ntiles = (N + BN - 1) / BN;
     const int64_t tiles = a.mtiles * a.ntiles;
     int splits = 1;
-    while (tiles * splits < 512 && K / (splits * 2) >= 512) splits *= 2;
+    while (tiles * splits < 256 && K / (splits * 2) >= 512) splits *= 2;
     a.kslice = ((K + splits - 1) / splits + BK - 1) / BK * BK;
     a.splits = (int)((K + a.kslice - 1) / a.kslice);
-    a.xcd_remap = (tiles * a.splits) % 8 == 0 ? 1 : 0;
     return a;
 }
 
