@@ -20,7 +20,10 @@
 // (x 2 matrices for SwiGLU) at once, so each x value in registers serves R
 // rows.  Per wave the order is: x of its columns (registers), every fp16 scale,
 // every q chunk, then the arithmetic, so the loads return in use order while
-// later ones are still in flight.  Lane sums are folded with DPP row
+// later ones are still in flight.  With several batch rows whose x does not
+// fit in registers, the workgroup first copies x into LDS (direct
+// global->LDS loads, before the weight loads) when it fits in 48 KB; wider
+// cases read x from L2 chunk by chunk.  Lane sums are folded with DPP row
 // operations and lane reads into scalar registers (no LDS), the KS wave
 // partials through LDS.
 //
@@ -172,16 +175,46 @@ __device__ inline void store_row(const Q8GemvArgs& a, int64_t rw, int b, float v
     }
 }
 
+// x staged in LDS (batch > 1): the batch x n_in activations are copied into
+// LDS once per workgroup by direct global->LDS loads issued before any weight
+// load, so they never queue behind the weight stream.  Layout: the flattened
+// x as 16-float chunks c, the four float4 of chunk c stored in the order
+// q ^ ((c >> 1) & 3), which spreads the 64-byte per-lane reads of eight
+// neighbouring lanes over distinct LDS banks.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline int xs_slot(int c, int q) { return 4 * c + (q ^ ((c >> 1) & 3)); }
+
+__device__ inline void lds_x16(const float* xs, int c, float (&xv)[16])
+{
+    const float4* xp = reinterpret_cast<const float4*>(xs);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 v = xp[xs_slot(c, q)];
+        xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+    }
+}
+
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // vmcnt N (low 4 bits + high 2 bits); expcnt and lgkmcnt left at their maxima
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
 // Fast path.  MODE: GemvMode.  B: batch rows handled (>= the real batch;
 // padding rows use the last real x row and are never stored).  R: rows per
 // wave.  CH: chunk columns per lane in this wave.  KS: waves per row group.
-template <int MODE, int B, int R, int CH, int KS>
+// XL: x staged in LDS (dynamic shared memory of batch * n_in floats).
+template <int MODE, int B, int R, int CH, int KS, bool XL>
 __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
 {
     constexpr int NM = (MODE == kSwiGLU) ? 2 : 1;   // weight matrices per output row
     constexpr int GROUPS = 4 / KS;                   // row groups per workgroup
-    constexpr bool XREG = B * CH <= 4;               // x in registers (<= 64 VGPRs)
+    constexpr bool XREG = !XL && B * CH <= 4;        // x in registers (<= 64 VGPRs)
     __shared__ float part[KS > 1 ? 4 : 1][R][NM][B];
+    extern __shared__ __attribute__((aligned(16))) float xs[];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -193,6 +226,20 @@ __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
 #pragma unroll
     for (int b = 0; b < B; ++b) xrow[b] = a.x + (int64_t)(b < a.batch ? b : a.batch - 1) * a.n_in;
 
+    if constexpr (XL) {
+        // batch * n_in / 4 float4 slots, a multiple of 256 on this path; slot s
+        // of the layout holds global float4 4c + (j ^ ((c >> 1) & 3)), c = s / 4
+        const int nper = (int)(((int64_t)a.batch * a.n_in) >> 10);
+        for (int i = 0; i < nper; ++i) {
+            const int sb = i * 256 + w * 64;
+            const int c = (sb + lane) >> 2, j = (sb + lane) & 3;
+            const float* src = a.x + (int64_t)(4 * c + (j ^ ((c >> 1) & 3))) * 4;
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(xs + sb * 4), 16, 0, 0);
+        }
+        // the vmcnt wait below counts only the weight loads issued after these
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
     float xr[XREG ? CH : 1][XREG ? B : 1][16];
     if constexpr (XREG) {
 #pragma unroll
@@ -228,6 +275,13 @@ __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
     // are not marked restrict, so this fence pins them).
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XL) {
+        // this wave's x slots have landed once at most the weight loads remain;
+        // the barrier makes every wave's slots visible
+        wait_vmcnt<2 * CH * R * NM>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     float acc[R][NM][B];
 #pragma unroll
@@ -270,6 +324,9 @@ __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
                 if constexpr (XREG) {
 #pragma unroll
                     for (int t = 0; t < 16; ++t) xv[t] = xr[XREG ? k : 0][XREG ? b : 0][t];
+                } else if constexpr (XL) {
+                    const int bb = b < a.batch ? b : a.batch - 1;
+                    lds_x16(xs, bb * (int)(a.n_in >> 4) + lane + 64 * (cbase + k), xv);
                 } else {
                     load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xv);
                 }
@@ -385,18 +442,18 @@ using KernelFn = void (*)(Q8GemvArgs);
 // Fast-path instantiations: (CH, KS) from the chunk count per row; R from the
 // row count; B from the batch.  Register use grows with R*NM*B, so wide
 // batches and SwiGLU take fewer rows per wave.
-template <int MODE, int B, int R>
+template <int MODE, int B, int R, bool XL>
 KernelFn pick_split(int nch64)
 {
     switch (nch64) {
-        case 1: return q8_0_gemv_fast<MODE, B, R, 1, 1>;
-        case 2: return q8_0_gemv_fast<MODE, B, R, 2, 1>;
-        case 3: return q8_0_gemv_fast<MODE, B, R, 3, 1>;
-        case 4: return q8_0_gemv_fast<MODE, B, R, 2, 2>;
-        case 6: return q8_0_gemv_fast<MODE, B, R, 3, 2>;
-        case 8: return q8_0_gemv_fast<MODE, B, R, 2, 4>;
-        case 12: return q8_0_gemv_fast<MODE, B, R, 3, 4>;
-        case 16: return q8_0_gemv_fast<MODE, B, R, 4, 4>;
+        case 1: return q8_0_gemv_fast<MODE, B, R, 1, 1, XL>;
+        case 2: return q8_0_gemv_fast<MODE, B, R, 2, 1, XL>;
+        case 3: return q8_0_gemv_fast<MODE, B, R, 3, 1, XL>;
+        case 4: return q8_0_gemv_fast<MODE, B, R, 2, 2, XL>;
+        case 6: return q8_0_gemv_fast<MODE, B, R, 3, 2, XL>;
+        case 8: return q8_0_gemv_fast<MODE, B, R, 2, 4, XL>;
+        case 12: return q8_0_gemv_fast<MODE, B, R, 3, 4, XL>;
+        case 16: return q8_0_gemv_fast<MODE, B, R, 4, 4, XL>;
         default: return nullptr;
     }
 }
@@ -412,27 +469,35 @@ int fast_r(GemvMode mode, int bt, int r)
     return r;
 }
 
-template <int MODE, int B>
+template <int MODE, int B, bool XL>
 KernelFn pick_rows(int r, int nch64)
 {
     if constexpr (MODE == kSwiGLU) {
-        return r >= 2 ? pick_split<MODE, B, 2>(nch64) : pick_split<MODE, B, 1>(nch64);
+        return r >= 2 ? pick_split<MODE, B, 2, XL>(nch64) : pick_split<MODE, B, 1, XL>(nch64);
     } else {
-        return r == 4 ? pick_split<MODE, B, 4>(nch64)
-                      : (r == 2 ? pick_split<MODE, B, 2>(nch64) : pick_split<MODE, B, 1>(nch64));
+        return r == 4 ? pick_split<MODE, B, 4, XL>(nch64)
+                      : (r == 2 ? pick_split<MODE, B, 2, XL>(nch64) : pick_split<MODE, B, 1, XL>(nch64));
     }
 }
 
 template <int MODE>
-KernelFn pick_fast(int bt, int r, int nch64)
+KernelFn pick_fast(int bt, int r, int nch64, bool xl)
 {
     switch (bt) {
-        case 1: return pick_rows<MODE, 1>(r, nch64);
-        case 2: return pick_rows<MODE, 2>(r, nch64);
-        case 4: return pick_rows<MODE, 4>(r, nch64);
-        default: return pick_rows<MODE, 8>(r, nch64);
+        case 1: return pick_rows<MODE, 1, false>(r, nch64);
+        case 2: return xl ? pick_rows<MODE, 2, true>(r, nch64) : pick_rows<MODE, 2, false>(r, nch64);
+        case 4: return xl ? pick_rows<MODE, 4, true>(r, nch64) : pick_rows<MODE, 4, false>(r, nch64);
+        default: return xl ? pick_rows<MODE, 8, true>(r, nch64) : pick_rows<MODE, 8, false>(r, nch64);
     }
 }
+
+// Largest x staged in LDS (bytes): up to 48 KB three workgroups still fit on a
+// CU; beyond that the lost occupancy costs more than the L2 reads of x save
+// (measured on the 8-row 3072-wide and 2-row 8192-wide cases).  Larger batch
+// x width products read x from L2.
+constexpr int64_t kXldsMax = 48 * 1024;
+
+static_assert(kXldsMax <= 64 * 1024, "dynamic LDS above 64 KB would need a per-function opt-in");
 
 template <int MODE>
 KernelFn pick_general(int bt)
@@ -484,17 +549,19 @@ hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
     const int nch64 = a.nch % 64 == 0 ? a.nch / 64 : 0;
     KernelFn fn = nullptr;
     int64_t blocks = 0;
+    bool xl = false;
     if (nch64 > 0) {
         const int ks = split_ks(nch64);
         const int groups = 4 / ks;
         // largest R in {4, 2, 1} that still gives >= 512 workgroups
         int r = 4;
         while (r > 1 && a.total_rows / ((int64_t)groups * r) < 512) r >>= 1;
+        xl = bt > 1 && (int64_t)a.batch * a.n_in * 4 <= kXldsMax;
         switch (p.mode) {
-            case kPlain: fn = pick_fast<kPlain>(bt, r, nch64); break;
-            case kResidual: fn = pick_fast<kResidual>(bt, r, nch64); break;
-            case kQKV: fn = pick_fast<kQKV>(bt, r, nch64); break;
-            default: fn = pick_fast<kSwiGLU>(bt, r, nch64); break;
+            case kPlain: fn = pick_fast<kPlain>(bt, r, nch64, xl); break;
+            case kResidual: fn = pick_fast<kResidual>(bt, r, nch64, xl); break;
+            case kQKV: fn = pick_fast<kQKV>(bt, r, nch64, xl); break;
+            default: fn = pick_fast<kSwiGLU>(bt, r, nch64, xl); break;
         }
         const int64_t rows_per_block = (int64_t)groups * fast_r(p.mode, bt, r);
         blocks = (a.total_rows + rows_per_block - 1) / rows_per_block;
@@ -513,7 +580,8 @@ hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
         const int64_t waves = (a.total_rows + rows_per_wave - 1) / rows_per_wave;
         blocks = (waves + 3) / 4;
     }
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    const size_t lds = xl ? (size_t)a.batch * (size_t)a.n_in * 4 : 0;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), lds, s, a);
     count_launch();
     return hipGetLastError();
 }
