@@ -14,7 +14,9 @@ value = algorithmic bytes per step (GGML weight bytes + x + out + residual)
         / wall time per step, in GB/s, inputs resident in HBM.
 roofline = the dominant kernel's algorithmic bytes per launch / its mean
         launch duration (HIP events around a replayed graph of `steps`
-        launches of that kernel), against 8 TB/s.
+        launches of that kernel), against 8 TB/s; traffic = the HBM bytes the
+        profiler counted for one launch of it (profiles/, null once the GEMV
+        sources differ from the ones profiled).
 cpu_baseline = the CPU oracle (single thread) on a bounded sample of steps.
 """
 from __future__ import annotations
@@ -61,6 +63,29 @@ def make_inputs():
         "r_down": synth.normal_f32(synth.seed(cfg, 8), (1, N_IN)),
     }
     return w, x
+
+
+def measured_traffic(kernel_role):
+    """HBM bytes per launch of one decode-layer kernel, as counted by the
+    profiler (profiles/q8_0_decode_layer_traffic.json), or None when the
+    kernel sources changed after the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "q8_0_decode_layer_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        for rel, digest in rec["source_sha256"].items():
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None, None
+        k = rec["kernels"][kernel_role]
+    except (OSError, KeyError, ValueError):
+        return None, None
+    return k["hbm_bytes"], {"fetch_KiB": k["FETCH_SIZE_KiB"], "write_KiB": k["WRITE_SIZE_KiB"],
+                            "fetch_scale": rec["calibration"]["fetch_scale"],
+                            "write_scale": rec["calibration"]["write_scale"],
+                            "algorithmic_bytes": k["algorithmic_bytes"],
+                            "source": "profiles/q8_0_decode_layer_traffic.json"}
 
 
 def cpu_baseline(w, x, budget_s=12.0):
@@ -229,6 +254,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true",
                     help="time every workload configuration (one JSON line each) instead of the step")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a 64 MiB device copy (untimed), the known-size reference that "
+                         "scales the profiler's HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is a "
@@ -270,6 +298,15 @@ def main():
     down_out = torch.empty((1, N_IN), device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    if args.calibrate:
+        # 64 MiB read + 64 MiB written by qdec_copy_kernel, three times
+        nbytes = 64 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            qd.copy(dst, src, nbytes)
+        torch.cuda.synchronize()
+        del src, dst
 
     names = ("qkv", "up", "down_residual")
 
@@ -356,6 +393,7 @@ def main():
         per_kernel[n] = {"mean_us": round(us, 3), "bytes": sb[n], "gbs": round(sb[n] / (us * 1e-6) / 1e9, 1)}
     dom = max(names, key=lambda n: per_kernel[n]["mean_us"])
     achieved = per_kernel[dom]["gbs"]
+    traffic, traffic_detail = measured_traffic(dom)
 
     total_bytes = sum(sb.values())
     ms_per_step = wall / args.steps * 1e3
@@ -386,7 +424,8 @@ def main():
             "eager_ms_per_step": round(wall_eager / args.steps * 1e3, 5),
         },
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch", "traffic_detail": traffic_detail},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w_host, x_host)
