@@ -127,14 +127,19 @@ def suite(args):
     def timed(name, launches, nbytes, flops=None, iters=100, warm=20, extra=None):
         """Mean launch duration: `iters` launches (rotating over the weight
         copies) captured into one HIP graph, replayed, bracketed by HIP events
-        on the replay stream; host launch costs stay out of the device timeline."""
+        on the replay stream; host launch costs stay out of the device timeline.
+        Warm-up and capture use one dedicated stream, so per-stream library
+        state (the batched GEMV workspace) exists before the capture starts."""
         nonlocal stream
         n = len(launches)
-        for i in range(warm):
-            launches[i % n]()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            for i in range(warm):
+                launches[i % n]()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=cs):
             stream = torch.cuda.current_stream()
             for i in range(iters):
                 launches[i % n]()

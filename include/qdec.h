@@ -36,8 +36,16 @@
  *     copy is keyed by (device, pointer, type, n_in, n_out); the caller promises
  *     that the bytes behind a cached pointer do not change until qdec_release
  *     or qdec_clear_cache ("immutable", [cuda_lane] preload_resident_blob).
- *     Inside HIP stream capture no copy can be made (QDEC_EINVAL): prepare or
- *     use every weight once before capturing.
+ *     Inside HIP stream capture no copy can be made or waited for
+ *     (QDEC_EINVAL): call qdec_prepare, which returns once the copy is
+ *     complete, for every weight before capturing.
+ *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in of
+ *     1024..8192 in the supported steps) splits x into a library-owned device
+ *     buffer, one per (device, stream), made on the first such call on that
+ *     stream and freed by qdec_clear_cache.  Calls on one stream share it in
+ *     stream order; calls on different streams never share one.  A stream
+ *     capture cannot allocate it, so a capture on a stream that has none takes
+ *     the VALU kernels (same results to the f32 tolerance).
  *   - Return value: QDEC_OK (0) or a negative qdec_status.  Invalid arguments
  *     are rejected with QDEC_EINVAL before any HIP call; a failed allocation
  *     returns QDEC_ENOMEM; a failed launch or HIP call returns QDEC_EHIP.
@@ -132,15 +140,16 @@ QDEC_API int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64
 /* -------------------------------------------------------- repack cache -- */
 
 /* Repack w now (load time, not timed), type QDEC_TYPE_Q8_0 or QDEC_TYPE_Q4_K
- * ([cuda_lane] preload_q4k_soa_weights).  Idempotent. */
+ * ([cuda_lane] preload_q4k_soa_weights), and wait on the host until the copy
+ * is complete.  Idempotent. */
 QDEC_API int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream);
 
 /* Free every repacked copy made from w (all types and shapes) on the current
  * device.  Returns QDEC_EINVAL if there was none.  Waits for the device. */
 QDEC_API int qdec_release(const void* w);
 
-/* Free every repacked copy on every device ([cuda_lane] clear_weight_cache,
- * "tests / model swap").  Waits for the devices. */
+/* Free every repacked copy and every workspace on every device ([cuda_lane]
+ * clear_weight_cache, "tests / model swap").  Waits for the devices. */
 QDEC_API void qdec_clear_cache(void);
 
 /* Number of repacked copies currently held ([cuda_lane] weight_cache_len). */

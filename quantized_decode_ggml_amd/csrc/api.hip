@@ -80,9 +80,29 @@ void destroy(Entry& e)
     e = Entry{};
 }
 
-// Returns the repacked copy of w, making it on first use.
-int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s, const void** out)
+int64_t copy_bytes(int type, int64_t n_in, int64_t n_out)
 {
+    return type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out)
+         : type == kTypeQ8_0Tiled ? q8t_plane_bytes(n_in, n_out)
+                                  : q4k_plane_bytes(n_in, n_out);
+}
+
+hipError_t launch_copy_of(int type, const void* w, int64_t n_in, int64_t n_out, void* dst, hipStream_t s)
+{
+    const uint8_t* raw = static_cast<const uint8_t*>(w);
+    return type == QDEC_TYPE_Q8_0 ? launch_repack_q8_0(raw, n_in, n_out, dst, s)
+         : type == kTypeQ8_0Tiled ? launch_repack_q8_0_tiled(raw, n_in, n_out, dst, s)
+                                  : launch_repack_q4k(raw, n_in, n_out, dst, s);
+}
+
+// Returns the repacked copy of w, making it on first use.  With `wait` the
+// host waits until the copy is complete (qdec_prepare).  With `optional`, a
+// copy that a stream capture cannot make or wait for is reported as absent
+// (*out = nullptr, QDEC_OK) instead of as an error.
+int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s, const void** out,
+             bool wait = false, bool optional = false)
+{
+    *out = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -96,20 +116,20 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
     auto it = g_cache.find(key);
     if (it == g_cache.end()) {
         // a repack allocates device memory, which a captured graph cannot do
-        if (capture != hipStreamCaptureStatusNone)
+        if (capture != hipStreamCaptureStatusNone) {
+            if (optional) return QDEC_OK;
             return fail(QDEC_EINVAL, "weight %p has no repacked copy: call qdec_prepare before graph capture", w);
+        }
         if (fail_alloc_hook()) return fail(QDEC_ENOMEM, "repack allocation refused (QDEC_FAIL_ALLOC=1)");
         Entry ent;
-        ent.bytes = type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out) : q4k_plane_bytes(n_in, n_out);
+        ent.bytes = copy_bytes(type, n_in, n_out);
         e = hipMalloc(&ent.buf, (size_t)ent.bytes);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(QDEC_ENOMEM, "hipMalloc(%lld bytes) for a repacked copy: %s",
                         (long long)ent.bytes, hipGetErrorString(e));
         }
-        e = type == QDEC_TYPE_Q8_0
-                ? launch_repack_q8_0(static_cast<const uint8_t*>(w), n_in, n_out, ent.buf, s)
-                : launch_repack_q4k(static_cast<const uint8_t*>(w), n_in, n_out, ent.buf, s);
+        e = launch_copy_of(type, w, n_in, n_out, ent.buf, s);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&ent.ready, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventRecord(ent.ready, s);
         if (e != hipSuccess) {
@@ -122,7 +142,12 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
     Entry& ent = it->second;
     if (!ent.done) {
         if (capture != hipStreamCaptureStatusNone) {
-            // no cross-stream waits inside a capture: finish the repack on the host
+            // an event wait or query would invalidate the capture
+            if (optional) return QDEC_OK;
+            return fail(QDEC_EINVAL, "weight %p: its repack may still be running; call qdec_prepare for it "
+                                     "before graph capture", w);
+        }
+        if (wait) {
             e = hipEventSynchronize(ent.ready);
             if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
             ent.done = true;
@@ -133,6 +158,49 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
             if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
         }
     }
+    *out = ent.buf;
+    return QDEC_OK;
+}
+
+// ------------------------------------------------------------ workspaces --
+// Scratch for the split activations of the matrix-core GEMV, one buffer per
+// (device, stream): calls on one stream are ordered, so they can share it;
+// calls on different streams never do.  A buffer grows on demand outside
+// stream capture; a capturing stream whose buffer is missing or too small gets
+// none, and the caller then takes the VALU kernels.
+std::map<std::pair<int, uintptr_t>, Entry> g_ws;
+
+int stream_workspace(hipStream_t s, int64_t bytes, void** out)
+{
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &capture) != hipSuccess) {
+        (void)hipGetLastError();
+        capture = hipStreamCaptureStatusNone;
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    Entry& ent = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
+    if (ent.bytes >= bytes) {
+        *out = ent.buf;
+        return QDEC_OK;
+    }
+    if (capture != hipStreamCaptureStatusNone) return QDEC_OK;
+    if (fail_alloc_hook()) return fail(QDEC_ENOMEM, "workspace allocation refused (QDEC_FAIL_ALLOC=1)");
+    if (ent.buf) {
+        (void)hipDeviceSynchronize();   // the old buffer may still be read by queued kernels
+        destroy(ent);
+    }
+    e = hipMalloc(&ent.buf, (size_t)bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        ent = Entry{};
+        return fail(QDEC_ENOMEM, "hipMalloc(%lld bytes) for a workspace: %s", (long long)bytes,
+                    hipGetErrorString(e));
+    }
+    ent.bytes = bytes;
     *out = ent.buf;
     return QDEC_OK;
 }
@@ -202,6 +270,21 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
     p.residual = residual;
     p.n_in = n_in;
     p.batch = batch;
+    if (q8_mfma_supported(p)) {
+        // tiled copies and a workspace; inside a capture either may be missing,
+        // and the VALU kernels then run instead
+        Q8TView tiles[3] = {};
+        bool have = true;
+        for (int k = 0; k < nw && have; ++k) {
+            const void* tb = nullptr;
+            QDEC_TRY(repacked(ws[k], kTypeQ8_0Tiled, n_in, rows[k], s, &tb, false, true));
+            if (tb) tiles[k] = q8t_view(tb, n_in, rows[k]);
+            else have = false;
+        }
+        void* wsp = nullptr;
+        if (have) QDEC_TRY(stream_workspace(s, q8_mfma_workspace_bytes(n_in), &wsp));
+        if (have && wsp) return finish(launch_q8_0_gemv_mfma(p, tiles, wsp, s), fn);
+    }
     return finish(launch_q8_0_gemv(p, s), fn);
 }
 
@@ -329,7 +412,11 @@ int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream
     QDEC_TRY(check_dims(fn, n_in, n_out, 1, type == QDEC_TYPE_Q8_0 ? 32 : 256, 0));
     QDEC_TRY(check_ptr(fn, "weight", w, 2));
     const void* buf = nullptr;
-    return repacked(w, type, n_in, n_out, stream, &buf);
+    QDEC_TRY(repacked(w, type, n_in, n_out, stream, &buf, true));
+    // Q8_0 weights also get the fragment-tiled copy of the batched matrix-core
+    // GEMV, so that graphs captured later can use it
+    if (type == QDEC_TYPE_Q8_0) QDEC_TRY(repacked(w, kTypeQ8_0Tiled, n_in, n_out, stream, &buf, true));
+    return QDEC_OK;
 }
 
 int qdec_release(const void* w)
@@ -364,13 +451,23 @@ void qdec_clear_cache(void)
         destroy(kv.second);
     }
     g_cache.clear();
+    for (auto& kv : g_ws) {
+        if (have_dev) (void)hipSetDevice(kv.first.first);
+        (void)hipDeviceSynchronize();
+        destroy(kv.second);
+    }
+    g_ws.clear();
     if (have_dev) (void)hipSetDevice(cur);
 }
 
 int64_t qdec_cache_len(void)
 {
+    // one per (weight, public type, shape): the tiled copy a Q8_0 weight also
+    // gets for the batched matrix-core GEMV is not counted separately
     std::lock_guard<std::mutex> lock(g_mu);
-    return (int64_t)g_cache.size();
+    int64_t n = 0;
+    for (const auto& kv : g_cache) n += kv.first.type != kTypeQ8_0Tiled;
+    return n;
 }
 
 int q8_0_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream)

@@ -30,6 +30,17 @@ struct Q8View {
     const uint16_t* d;
 };
 
+// Fragment-tiled Q8_0 matrix (the matrix-core GEMV's copy): rows in groups of
+// 16, the last group padded with zero rows; for group G and Q8_0 block b the
+// 512-byte q tile at byte (G*nb + b)*512 holds, at byte 8*l, the 8 weights
+// of row 16G + l%16 at k = 32b + 8*(l/16) .. +7 (the bf16 MFMA B-operand order
+// of lane l), and the d plane holds at element (G*nb + b)*16 + r the scale of
+// row 16G + r.  One wave load of a tile is 512 contiguous bytes.
+struct Q8TView {
+    const int8_t* q;
+    const uint16_t* d;
+};
+
 struct Q4KView {
     const uint8_t* qs;
     const uint32_t* dm;
@@ -51,6 +62,25 @@ inline Q8View q8_view(const void* base, int64_t n_in, int64_t n_out)
     return Q8View{reinterpret_cast<const int8_t*>(p),
                   reinterpret_cast<const uint16_t*>(p + align_up(n_out * n_in, kAlign))};
 }
+
+inline int64_t q8t_groups(int64_t n_out) { return (n_out + 15) / 16; }
+
+inline int64_t q8t_plane_bytes(int64_t n_in, int64_t n_out)
+{
+    const int64_t tiles = q8t_groups(n_out) * (n_in / 32);
+    return align_up(tiles * 512, kAlign) + align_up(tiles * 32, kAlign);
+}
+
+inline Q8TView q8t_view(const void* base, int64_t n_in, int64_t n_out)
+{
+    const char* p = static_cast<const char*>(base);
+    const int64_t tiles = q8t_groups(n_out) * (n_in / 32);
+    return Q8TView{reinterpret_cast<const int8_t*>(p),
+                   reinterpret_cast<const uint16_t*>(p + align_up(tiles * 512, kAlign))};
+}
+
+// Cache type of the tiled copy (internal; the public types are the GGML ids).
+constexpr int kTypeQ8_0Tiled = 0x108;
 
 inline int64_t q4k_plane_bytes(int64_t n_in, int64_t n_out)
 {
@@ -76,6 +106,8 @@ hipError_t launch_repack_q8_0(const uint8_t* raw, int64_t n_in, int64_t n_out, v
                               hipStream_t s);
 hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
                              hipStream_t s);
+hipError_t launch_repack_q8_0_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
+                                    hipStream_t s);
 hipError_t launch_dequant_q8_0(Q8View w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
 hipError_t launch_dequant_q4k(Q4KView w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
 
@@ -96,6 +128,15 @@ struct Q8GemvProblem {
 };
 
 hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s);
+
+// Matrix-core path for 3..8 batch rows (gemv_q8_0_mfma.hip).  It reads the
+// fragment-tiled copies of the segments and needs a device workspace of
+// q8_mfma_workspace_bytes(n_in) bytes for the split activations, owned by
+// the caller and used in stream order.
+int64_t q8_mfma_workspace_bytes(int64_t n_in);
+bool q8_mfma_supported(const Q8GemvProblem& p);
+hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, void* workspace,
+                                 hipStream_t s);
 
 hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                            float* out, hipStream_t s);

@@ -99,6 +99,35 @@ __global__ __launch_bounds__(256) void repack_q4k_kernel(const uint16_t* __restr
         dst[k] = make_uint4(words[4 + 4 * k], words[5 + 4 * k], words[6 + 4 * k], words[7 + 4 * k]);
 }
 
+// One thread per (row, Q8_0 block) of the tiled copy, rows padded to a
+// multiple of 16 with zeros: the block's 32 weights go to the four 8-byte
+// slots of its tile that the lanes r, r+16, r+32, r+48 load, its scale to the
+// tile's scale slot r.
+__global__ __launch_bounds__(256) void repack_q8_0_tiled_kernel(const uint16_t* __restrict__ raw,
+                                                                int64_t n_out, int64_t nb,
+                                                                int64_t nthreads,
+                                                                uint2* __restrict__ qp,
+                                                                uint16_t* __restrict__ dp)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nthreads) return;
+    const int64_t row = t / nb, b = t % nb;
+    const int64_t g = row >> 4;
+    const int r = (int)(row & 15);
+    uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint16_t d = 0;
+    if (row < n_out) {
+        const uint16_t* src = raw + (row * nb + b) * (kQ8Bytes / 2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) words[k] = (uint32_t)src[1 + 2 * k] | ((uint32_t)src[2 + 2 * k] << 16);
+        d = src[0];
+    }
+    uint2* tile = qp + (g * nb + b) * 64;   // 64 slots of 8 bytes
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) tile[r + 16 * kg] = make_uint2(words[2 * kg], words[2 * kg + 1]);
+    dp[(g * nb + b) * 16 + r] = d;
+}
+
 // One thread per 16 weights of the repacked Q8_0 matrix.
 __global__ __launch_bounds__(256) void dequant_q8_0_kernel(Q8View w, int64_t n_in, int64_t nchunks,
                                                            float* __restrict__ out)
@@ -188,6 +217,18 @@ hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, vo
     hipLaunchKernelGGL(repack_q4k_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t*>(raw), nblocks, const_cast<uint8_t*>(v.qs),
                        const_cast<uint32_t*>(v.dm), const_cast<uint32_t*>(v.sm));
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_repack_q8_0_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
+                                    hipStream_t s)
+{
+    const Q8TView v = q8t_view(dst, n_in, n_out);
+    const int64_t nb = n_in / 32, nthreads = q8t_groups(n_out) * 16 * nb;
+    hipLaunchKernelGGL(repack_q8_0_tiled_kernel, dim3(grid_for(nthreads, 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(raw), n_out, nb, nthreads,
+                       reinterpret_cast<uint2*>(const_cast<int8_t*>(v.q)), const_cast<uint16_t*>(v.d));
     count_launch();
     return hipGetLastError();
 }

@@ -1,0 +1,219 @@
+"""GPU parity of the matrix-core Q8_0 GEMV path (3..8 batch rows): which path
+runs, every supported width, ragged rows and segments, activations over a wide
+dynamic range (the exact three-part bf16 split of x), graph capture with and
+without a prepared workspace, and a refused workspace allocation.
+
+Bar: the f32 bound, |gpu - oracle| <= 1e-5 * S + 1e-6 with S = sum_j |w x|
+from the oracle (SwiGLU: the propagated bound of helpers.swiglu_tol).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import check_f32, q8_weights, swiglu_tol, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# widths the matrix-core path takes (n_in / 32 blocks split over 4 or 8 waves)
+MFMA_WIDTHS = [1024, 2048, 3072, 4096, 6144, 8192]
+
+
+@pytest.fixture(scope="module")
+def qd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_decode_ggml_amd as q
+    return q
+
+
+@pytest.fixture(autouse=True)
+def fresh_cache(qd):
+    qd.clear_cache()      # also drops the per-stream workspaces
+    yield
+    qd.clear_cache()
+
+
+def dev(a):
+    return to_dev(a, torch)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def launches(qd, fn):
+    torch.cuda.synchronize()
+    before = qd.launch_count()
+    r = fn()
+    torch.cuda.synchronize()
+    return r, qd.launch_count() - before
+
+
+@pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 2), (3072, 4, 2),
+                                               (3072, 8, 2), (8192, 5, 2), (512, 4, 1), (2560, 8, 1)])
+def test_path_selection(qd, n_in, batch, expect):
+    """3..8 rows at a supported width: x split + matrix-core kernel (2 launches);
+    otherwise the VALU kernel (1 launch)."""
+    n_out = 48
+    raw = q8_weights(9000 + n_in, n_out, n_in)
+    x = synth.normal_f32(9001 + batch, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    out, n = launches(qd, lambda: qd.q8_0_gemv(w, n_in, n_out, xd))
+    assert n == expect
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(host(out), ref, S, f"path n_in={n_in} b{batch}")
+
+
+@pytest.mark.parametrize("n_in", MFMA_WIDTHS)
+@pytest.mark.parametrize("n_out", [16, 77])
+@pytest.mark.parametrize("batch", [3, 6, 8])
+def test_gemv_widths(qd, n_in, n_out, batch):
+    raw = q8_weights(9100 + n_in + n_out, n_out, n_in)
+    x = synth.normal_f32(9101 + batch, (batch, n_in))
+    out = host(qd.q8_0_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"mfma gemv {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("batch", [3, 8])
+def test_gemv_wide_dynamic_range(qd, batch):
+    """Activations spread over 2^-60..2^60 (per element), so the hi, mid and lo
+    parts of the split all carry weight; the bound is relative to S."""
+    n_out, n_in = 40, 2048
+    raw = q8_weights(9200, n_out, n_in)
+    rng = np.random.default_rng(9201)
+    x = (synth.normal_f32(9202, (batch, n_in)).astype(np.float64)
+         * np.exp2(rng.uniform(-60, 60, size=(batch, n_in)))).astype(np.float32)
+    out = host(qd.q8_0_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"wide range b{batch}")
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(100, 20), (48, 16), (3072, 1024)])
+@pytest.mark.parametrize("batch", [3, 7])
+def test_qkv_ragged_segments(qd, n_q, n_kv, batch):
+    """Segment boundaries inside a 16-row group of the matrix-core kernel."""
+    n_in = 1024 if n_q < 3072 else 3072
+    wq, wk, wv = (q8_weights(9300 + k, n, n_in) for k, n in enumerate((n_q, n_kv, n_kv)))
+    x = synth.normal_f32(9310 + batch, (batch, n_in))
+    (q, k, v), n = launches(qd, lambda: qd.q8_0_qkv(dev(wq), dev(wk), dev(wv), n_in, n_q, n_kv, dev(x)))
+    (rq, rk, rv), (sq, sk, sv) = oracle.q8_0_qkv(wq, wk, wv, n_in, n_q, n_kv, x)
+    check_f32(host(q), rq, sq, "q")
+    check_f32(host(k), rk, sk, "k")
+    check_f32(host(v), rv, sv, "v")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(77, 2048), (8192, 3072)])
+@pytest.mark.parametrize("batch", [4, 5, 8])
+def test_swiglu(qd, n_out, n_in, batch):
+    g = q8_weights(9400 + n_in, n_out, n_in)
+    u = q8_weights(9401 + n_in, n_out, n_in)
+    x = synth.normal_f32(9402 + batch, (batch, n_in))
+    out = host(qd.q8_0_swiglu(dev(g), dev(u), n_in, n_out, dev(x)))
+    r = oracle.q8_0_swiglu(g, u, n_in, n_out, x)
+    err = np.abs(out.astype(np.float64) - r["out"])
+    assert not np.isnan(out).any()
+    assert (err <= swiglu_tol(r)).all(), f"worst err/tol {np.max(err / swiglu_tol(r)):.3g}"
+
+
+@pytest.mark.parametrize("batch", [3, 8])
+def test_residual_in_place(qd, batch):
+    n_out, n_in = 3072, 8192
+    raw = q8_weights(9500, n_out, n_in)
+    x = synth.normal_f32(9501, (batch, n_in))
+    r = synth.normal_f32(9502, (batch, n_out))
+    buf = dev(r)
+    qd.q8_0_gemv_residual(dev(raw), n_in, n_out, dev(x), buf, out=buf)
+    ref, S = oracle.q8_0_gemv_residual(raw, n_in, n_out, x, r)
+    check_f32(host(buf), ref, S, f"residual in place b{batch}")
+
+
+def test_graph_capture_with_workspace(qd):
+    """Warm-up on the capture stream makes its workspace; the captured graph then
+    uses the matrix-core path (2 launches recorded) and every replay, with eager
+    work in between, matches the eager result bit for bit."""
+    n_out, n_in, batch = 1024, 3072, 4
+    raw = q8_weights(9600, n_out, n_in)
+    x = synth.normal_f32(9601, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        eager = qd.q8_0_gemv(w, n_in, n_out, xd)
+    s.synchronize()
+    eager = eager.cpu().numpy()
+    out = torch.empty((batch, n_out), device="cuda")
+    g = torch.cuda.CUDAGraph()
+    before = qd.launch_count()
+    with torch.cuda.graph(g, stream=s):
+        qd.q8_0_gemv(w, n_in, n_out, xd, out=out)
+    assert qd.launch_count() - before == 2
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    for k in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        got = host(out)
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {k}"
+        check_f32(got, ref, S, f"replay {k}")
+        qd.q8_0_gemv(w, n_in, n_out, xd)          # eager work between replays
+    del g
+
+
+def test_graph_capture_without_workspace_falls_back(qd):
+    """A capturing stream with no workspace cannot allocate one: the call takes
+    the VALU kernel (1 launch recorded) and stays within the bound."""
+    n_out, n_in, batch = 512, 3072, 8
+    raw = q8_weights(9700, n_out, n_in)
+    x = synth.normal_f32(9701, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    torch.cuda.synchronize()
+    out = torch.empty((batch, n_out), device="cuda")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    before = qd.launch_count()
+    with torch.cuda.graph(g, stream=s):
+        qd.q8_0_gemv(w, n_in, n_out, xd, out=out)
+    assert qd.launch_count() - before == 1
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    for k in range(2):
+        out.zero_()
+        g.replay()
+        check_f32(host(out), ref, S, f"fallback replay {k}")
+    del g
+
+
+def test_capture_with_pending_repack_is_rejected(qd):
+    """A weight used once (repack still possibly in flight) cannot be waited for
+    inside a capture: the call fails cleanly instead of breaking the capture."""
+    n_out, n_in = 64, 512
+    w = dev(q8_weights(9750, n_out, n_in))
+    x = dev(synth.normal_f32(9751, (1, n_in)))
+    qd.q8_0_gemv(w, n_in, n_out, x)                  # first use: repack enqueued, not waited for
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(qd.QdecError) as ei:
+        with torch.cuda.graph(g, stream=s):
+            qd.q8_0_gemv(w, n_in, n_out, x)
+    assert ei.value.status == qd.QDEC_EINVAL
+    assert "qdec_prepare" in str(ei.value)
+    del g
+    torch.cuda.synchronize()
+
+
+def test_workspace_allocation_refused(qd, monkeypatch):
+    n_out, n_in, batch = 64, 3072, 4
+    w = dev(q8_weights(9800, n_out, n_in))
+    x = dev(synth.normal_f32(9801, (batch, n_in)))
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)       # the repack itself is allowed
+    torch.cuda.synchronize()
+    monkeypatch.setenv("QDEC_FAIL_ALLOC", "1")
+    with pytest.raises(qd.QdecError) as ei:
+        qd.q8_0_gemv(w, n_in, n_out, x)
+    assert ei.value.status == qd.QDEC_ENOMEM
