@@ -64,6 +64,14 @@ __device__ inline Seg row_seg(const Q8GemvArgs& a, int64_t rr, int m)
     }
 }
 
+// Rows lo and hi lie in one segment (always true outside QKV).
+template <int MODE>
+__device__ inline bool same_segment(const Q8GemvArgs& a, int64_t lo, int64_t hi)
+{
+    if constexpr (MODE == kQKV) return (lo >= a.end0) == (hi >= a.end0) && (lo >= a.end1) == (hi >= a.end1);
+    else return true;
+}
+
 // Final value of output row `rw`, batch row b (v1 is the up product of SwiGLU).
 template <int MODE>
 __device__ inline void store_row(const Q8GemvArgs& a, int64_t rw, int b, float v0, float v1)

@@ -20,7 +20,12 @@
 // (x 2 matrices for SwiGLU) at once, so each x value in registers serves R
 // rows.  Per wave the order is: x of its columns (registers), every fp16 scale,
 // every q chunk, then the arithmetic, so the loads return in use order while
-// later ones are still in flight.  With several batch rows whose x does not
+// later ones are still in flight.  One batch row: one chunk column per wave
+// and one row group per workgroup, which keeps the arithmetic a wave still
+// owes after its last load short (the kernel's tail).  The scalar set-up
+// before the first weight load is kept to a few dozen instructions: the
+// scalar unit is shared by every wave of a compute unit, and all of them
+// start together.  With several batch rows whose x does not
 // fit in registers, the workgroup first copies x into LDS (direct
 // global->LDS loads, before the weight loads) when it fits in 48 KB; wider
 // cases read x from L2 chunk by chunk.  Lane sums are folded with DPP row
@@ -135,14 +140,17 @@ __device__ inline void wait_vmcnt()
 // Fast path.  MODE: GemvMode.  B: batch rows handled (>= the real batch;
 // padding rows use the last real x row and are never stored).  R: rows per
 // wave.  CH: chunk columns per lane in this wave.  KS: waves per row group.
-// XL: x staged in LDS (dynamic shared memory of batch * n_in floats).
-template <int MODE, int B, int R, int CH, int KS, bool XL>
-__global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
+// XL: x staged in LDS (dynamic shared memory of batch * n_in floats).  NW:
+// waves per workgroup (NW / KS row groups).
+template <int MODE, int B, int R, int CH, int KS, bool XL, int NW>
+__global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
 {
     constexpr int NM = (MODE == kSwiGLU) ? 2 : 1;   // weight matrices per output row
-    constexpr int GROUPS = 4 / KS;                   // row groups per workgroup
+    constexpr int GROUPS = NW / KS;                  // row groups per workgroup
+    static_assert(GROUPS * KS == NW, "whole row groups per workgroup");
+    static_assert(!XL || NW == 4, "the LDS copy of x assumes 256 threads");
     constexpr bool XREG = !XL && B * CH <= 4;        // x in registers (<= 64 VGPRs)
-    __shared__ float part[KS > 1 ? 4 : 1][R][NM][B];
+    __shared__ float part[KS > 1 ? NW : 1][R][NM][B];
     extern __shared__ __attribute__((aligned(16))) float xs[];
 
     const int lane = threadIdx.x & 63;
@@ -177,13 +185,26 @@ __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
             for (int b = 0; b < B; ++b) load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xr[k][b]);
     }
 
+    // Row pointers (scalar work shared by every wave of a CU, so kept short):
+    // when the R rows are all in range and in one segment they are consecutive
+    // rows of one plane; otherwise each row is mapped (and clamped) alone.
     Seg sg[R][NM];
+    if (row0 + R <= a.total_rows && same_segment<MODE>(a, row0, row0 + R - 1)) {
+        const int64_t nb = a.n_in >> 5;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t rw = row0 + r;
-        const int64_t rr = rw < a.total_rows ? rw : a.total_rows - 1;  // keep loads in bounds
+        for (int m = 0; m < NM; ++m) {
+            const Seg s0 = row_seg<MODE>(a, row0, m);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) sg[r][m] = row_seg<MODE>(a, rr, m);
+            for (int r = 0; r < R; ++r) sg[r][m] = Seg{s0.q + r * a.n_in, s0.d + r * nb};
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t rw = row0 + r;
+            const int64_t rr = rw < a.total_rows ? rw : a.total_rows - 1;  // keep loads in bounds
+#pragma unroll
+            for (int m = 0; m < NM; ++m) sg[r][m] = row_seg<MODE>(a, rr, m);
+        }
     }
     uint16_t dv[CH][R][NM];
     uint4 qv[CH][R][NM];
@@ -278,6 +299,8 @@ __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[r][m][b] = wave_sum(acc[r][m][b]);
 
+    // lane l < R*B ends up with the (row l / B, batch row l % B) value
+    float v0 = 0.0f, v1 = 0.0f;
     if constexpr (KS > 1) {
         if (lane == 0) {
 #pragma unroll
@@ -289,26 +312,26 @@ __global__ __launch_bounds__(256) void q8_0_gemv_fast(Q8GemvArgs a)
         }
         __syncthreads();
         if (ks != 0) return;
+        if (lane < R * B) {
+            const int r = lane / B, b = lane % B;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                v0 += part[w + k][r][0][b];
+                v1 += part[w + k][r][NM - 1][b];
+            }
+        }
+    } else {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    float v = part[w][r][m][b];
-#pragma unroll
-                    for (int k = 1; k < KS; ++k) v += part[w + k][r][m][b];
-                    acc[r][m][b] = v;
+            for (int b = 0; b < B; ++b)
+                if (lane == r * B + b) {
+                    v0 = acc[r][0][b];
+                    v1 = acc[r][NM - 1][b];
                 }
     }
-    // lane r*B + b stores the (row r, batch b) value
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            if (lane == r * B + b && b < a.batch && row0 + r < a.total_rows)
-                store_row<MODE>(a, row0 + r, b, acc[r][0][b], acc[r][NM - 1][b]);
-        }
+    const int rl = lane / B, bl = lane % B;
+    if (lane < R * B && bl < a.batch && row0 + rl < a.total_rows) store_row<MODE>(a, row0 + rl, bl, v0, v1);
 }
 
 // General path: row groups of LPR lanes, one row per group, bounds-checked loop.
@@ -368,21 +391,22 @@ __global__ __launch_bounds__(256) void q8_0_gemv_general(Q8GemvArgs a)
 
 using KernelFn = void (*)(Q8GemvArgs);
 
-// Fast-path instantiations: (CH, KS) from the chunk count per row; R from the
-// row count; B from the batch.  Register use grows with R*NM*B, so wide
-// batches and SwiGLU take fewer rows per wave.
+// Fast-path instantiations for two or more batch rows: (CH, KS) from the
+// chunk count per row, four waves per workgroup; R from the row count; B from
+// the batch.  Register use grows with R*NM*B, so wide batches and SwiGLU take
+// fewer rows per wave.
 template <int MODE, int B, int R, bool XL>
 KernelFn pick_split(int nch64)
 {
     switch (nch64) {
-        case 1: return q8_0_gemv_fast<MODE, B, R, 1, 1, XL>;
-        case 2: return q8_0_gemv_fast<MODE, B, R, 2, 1, XL>;
-        case 3: return q8_0_gemv_fast<MODE, B, R, 3, 1, XL>;
-        case 4: return q8_0_gemv_fast<MODE, B, R, 2, 2, XL>;
-        case 6: return q8_0_gemv_fast<MODE, B, R, 3, 2, XL>;
-        case 8: return q8_0_gemv_fast<MODE, B, R, 2, 4, XL>;
-        case 12: return q8_0_gemv_fast<MODE, B, R, 3, 4, XL>;
-        case 16: return q8_0_gemv_fast<MODE, B, R, 4, 4, XL>;
+        case 1: return q8_0_gemv_fast<MODE, B, R, 1, 1, XL, 4>;
+        case 2: return q8_0_gemv_fast<MODE, B, R, 2, 1, XL, 4>;
+        case 3: return q8_0_gemv_fast<MODE, B, R, 3, 1, XL, 4>;
+        case 4: return q8_0_gemv_fast<MODE, B, R, 2, 2, XL, 4>;
+        case 6: return q8_0_gemv_fast<MODE, B, R, 3, 2, XL, 4>;
+        case 8: return q8_0_gemv_fast<MODE, B, R, 2, 4, XL, 4>;
+        case 12: return q8_0_gemv_fast<MODE, B, R, 3, 4, XL, 4>;
+        case 16: return q8_0_gemv_fast<MODE, B, R, 4, 4, XL, 4>;
         default: return nullptr;
     }
 }
@@ -413,10 +437,70 @@ template <int MODE>
 KernelFn pick_fast(int bt, int r, int nch64, bool xl)
 {
     switch (bt) {
-        case 1: return pick_rows<MODE, 1, false>(r, nch64);
         case 2: return xl ? pick_rows<MODE, 2, true>(r, nch64) : pick_rows<MODE, 2, false>(r, nch64);
         case 4: return xl ? pick_rows<MODE, 4, true>(r, nch64) : pick_rows<MODE, 4, false>(r, nch64);
         default: return xl ? pick_rows<MODE, 8, true>(r, nch64) : pick_rows<MODE, 8, false>(r, nch64);
+    }
+}
+
+// One batch row.  A wave's arithmetic after its last weight load lands is the
+// kernel's tail (a single wave issues a signed-byte conversion only every ~13
+// cycles), so each wave takes one chunk column (two above 8192 columns) and a
+// workgroup is the KS waves of one row group; x is then read once per
+// workgroup.  Rows per wave: 8 weight rows up to four waves per group, 4
+// beyond, halved while the grid would hold fewer than 3072 waves (three per
+// SIMD).
+struct B1Shape { int ks, ch; };
+
+B1Shape b1_shape(int nch64)
+{
+    switch (nch64) {
+        case 1: return {1, 1};
+        case 2: return {2, 1};
+        case 3: return {3, 1};
+        case 4: return {4, 1};
+        case 6: return {6, 1};
+        case 8: return {8, 1};
+        case 12: return {6, 2};
+        case 16: return {8, 2};
+        default: return {0, 0};
+    }
+}
+
+int b1_rows(GemvMode mode, int ks, int64_t total_rows)
+{
+    const int nm = mode == kSwiGLU ? 2 : 1;
+    int r = (ks <= 4 ? 8 : 4) / nm;
+    while (r > 1 && (total_rows / r) * ks < 3072) r >>= 1;
+    return r;
+}
+
+template <int MODE, int R>
+KernelFn pick_b1_split(int nch64)
+{
+    switch (nch64) {
+        case 1: return q8_0_gemv_fast<MODE, 1, R, 1, 1, false, 1>;
+        case 2: return q8_0_gemv_fast<MODE, 1, R, 1, 2, false, 2>;
+        case 3: return q8_0_gemv_fast<MODE, 1, R, 1, 3, false, 3>;
+        case 4: return q8_0_gemv_fast<MODE, 1, R, 1, 4, false, 4>;
+        case 6: return q8_0_gemv_fast<MODE, 1, R, 1, 6, false, 6>;
+        case 8: return q8_0_gemv_fast<MODE, 1, R, 1, 8, false, 8>;
+        case 12: return q8_0_gemv_fast<MODE, 1, R, 2, 6, false, 6>;
+        case 16: return q8_0_gemv_fast<MODE, 1, R, 2, 8, false, 8>;
+        default: return nullptr;
+    }
+}
+
+template <int MODE>
+KernelFn pick_b1(int r, int nch64)
+{
+    if constexpr (MODE == kSwiGLU) {
+        return r >= 4 ? pick_b1_split<MODE, 4>(nch64)
+                      : (r == 2 ? pick_b1_split<MODE, 2>(nch64) : pick_b1_split<MODE, 1>(nch64));
+    } else {
+        return r >= 8 ? pick_b1_split<MODE, 8>(nch64)
+                      : (r == 4 ? pick_b1_split<MODE, 4>(nch64)
+                                : (r == 2 ? pick_b1_split<MODE, 2>(nch64) : pick_b1_split<MODE, 1>(nch64)));
     }
 }
 
@@ -450,14 +534,26 @@ hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
     const int nch64 = a.nch % 64 == 0 ? a.nch / 64 : 0;
     KernelFn fn = nullptr;
     int64_t blocks = 0;
+    int threads = 256;
     bool xl = false;
-    if (nch64 > 0) {
+    if (nch64 > 0 && bt == 1) {
+        const B1Shape sh = b1_shape(nch64);
+        const int r = b1_rows(p.mode, sh.ks, a.total_rows);
+        switch (p.mode) {
+            case kPlain: fn = pick_b1<kPlain>(r, nch64); break;
+            case kResidual: fn = pick_b1<kResidual>(r, nch64); break;
+            case kQKV: fn = pick_b1<kQKV>(r, nch64); break;
+            default: fn = pick_b1<kSwiGLU>(r, nch64); break;
+        }
+        threads = 64 * sh.ks;
+        blocks = (a.total_rows + r - 1) / r;
+    } else if (nch64 > 0) {
         const int ks = split_ks(nch64);
         const int groups = 4 / ks;
         // largest R in {4, 2, 1} that still gives >= 512 workgroups
         int r = 4;
         while (r > 1 && a.total_rows / ((int64_t)groups * r) < 512) r >>= 1;
-        xl = bt > 1 && (int64_t)a.batch * a.n_in * 4 <= kXldsMax;
+        xl = (int64_t)a.batch * a.n_in * 4 <= kXldsMax;
         switch (p.mode) {
             case kPlain: fn = pick_fast<kPlain>(bt, r, nch64, xl); break;
             case kResidual: fn = pick_fast<kResidual>(bt, r, nch64, xl); break;
@@ -482,7 +578,7 @@ hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
         blocks = (waves + 3) / 4;
     }
     const size_t lds = xl ? (size_t)a.batch * (size_t)a.n_in * 4 : 0;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), lds, s, a);
     count_launch();
     return hipGetLastError();
 }
