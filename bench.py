@@ -7,8 +7,9 @@ batch 1, all in libqdec kernels on one stream:
     FFN down    3072x8192 with residual, x[8192], r[3072]
 Weights are seeded synthetic Q8_0 (W ~ N(0, 0.02) quantised per 32-block),
 activations N(0, 1).  Consecutive steps read the weights of consecutive
-"layers": LAYERS distinct device copies (8 x 70 MB = 560 MB, twice the 256 MB
-Infinity Cache), so the bytes come from HBM as in a real decode.
+"layers": LAYERS distinct device copies (32 x 70 MB = 2.25 GB; even one product
+alone rotates over >= 512 MB, twice the 256 MB Infinity Cache), so the bytes
+come from HBM as in a real decode.
 
 value = algorithmic bytes per step (GGML weight bytes + x + out + residual)
         / wall time per step, in GB/s, inputs resident in HBM.
@@ -31,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-LAYERS = 8
+LAYERS = 32
 N_IN, N_Q, N_KV, N_FF = 3072, 3072, 1024, 8192
 
 

@@ -12,7 +12,8 @@
 // Work mapping: as the Q8_0 fast path, with an 8-byte chunk of nibbles per
 // lane (16 weights: 8 of sub-block 2p, 8 of sub-block 2p+1), so a row of n_in
 // weights is n_in/16 chunks and lane j of a wave takes chunks j, j+64, ...; K
-// is split over KS waves of the workgroup and each wave computes R rows.  Per
+// is split over KS waves of the workgroup and each wave computes R rows.  One
+// batch row: one chunk column per wave and one row group per workgroup.  Per
 // chunk the dot product is taken per sub-block in the factored form
 //     sum_t w_t x_t = (d*sc) * sum_t q_t x_t - (dmin*m) * sum_t x_t,
 // where d*sc and dmin*m are exact in f32.  sum_t x_t depends only on the lane's
@@ -138,12 +139,13 @@ __device__ inline float wave_sum(float v)
 
 // Fast path: n_in a multiple of 1024; CH chunk columns per lane, KS waves per
 // row group, R rows per wave, B batch rows.
-template <int B, int R, int CH, int KS>
-__global__ __launch_bounds__(256) void q4k_gemv_fast(Q4KArgs a)
+template <int B, int R, int CH, int KS, int NW>
+__global__ __launch_bounds__(64 * NW) void q4k_gemv_fast(Q4KArgs a)
 {
-    constexpr int GROUPS = 4 / KS;
+    constexpr int GROUPS = NW / KS;
+    static_assert(GROUPS * KS == NW, "whole row groups per workgroup");
     constexpr bool XREG = B * CH <= 4;
-    __shared__ float part[KS > 1 ? 4 : 1][R][B];
+    __shared__ float part[KS > 1 ? NW : 1][R][B];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -164,16 +166,31 @@ __global__ __launch_bounds__(256) void q4k_gemv_fast(Q4KArgs a)
             for (int b = 0; b < B; ++b) load_xchunk(xrow[b], lane + 64 * (cbase + k), xr[k][b]);
     }
 
+    // Row pointers: consecutive rows from the first when all R are in range
+    // (short scalar set-up; the scalar unit is shared by the whole CU),
+    // otherwise each row clamped alone.
     const uint8_t* qrow[R];
     const uint32_t* dmrow[R];
     const uint32_t* smrow[R];
+    if (row0 + R <= a.n_out) {
+        const uint8_t* q0 = a.qs + row0 * (a.n_in >> 1);
+        const uint32_t* dm0 = a.dm + row0 * nsb;
+        const uint32_t* sm0 = a.sm + row0 * nsb * 4;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t rw = row0 + r;
-        const int64_t rr = rw < a.n_out ? rw : a.n_out - 1;
-        qrow[r] = a.qs + rr * (a.n_in >> 1);
-        dmrow[r] = a.dm + rr * nsb;
-        smrow[r] = a.sm + rr * nsb * 4;
+        for (int r = 0; r < R; ++r) {
+            qrow[r] = q0 + r * (a.n_in >> 1);
+            dmrow[r] = dm0 + r * nsb;
+            smrow[r] = sm0 + r * nsb * 4;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t rw = row0 + r;
+            const int64_t rr = rw < a.n_out ? rw : a.n_out - 1;
+            qrow[r] = a.qs + rr * (a.n_in >> 1);
+            dmrow[r] = a.dm + rr * nsb;
+            smrow[r] = a.sm + rr * nsb * 4;
+        }
     }
     uint32_t dmv[CH][R], smv[CH][R];
     u32x2 qv[CH][R];
@@ -225,6 +242,8 @@ __global__ __launch_bounds__(256) void q4k_gemv_fast(Q4KArgs a)
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[r][b] = wave_sum(acc[r][b]);
 
+    // lane l < R*B ends up with the (row l / B, batch row l % B) value
+    float v = 0.0f;
     if constexpr (KS > 1) {
         if (lane == 0) {
 #pragma unroll
@@ -234,22 +253,19 @@ __global__ __launch_bounds__(256) void q4k_gemv_fast(Q4KArgs a)
         }
         __syncthreads();
         if (ks != 0) return;
+        if (lane < R * B) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) v += part[w + k][lane / B][lane % B];
+        }
+    } else {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float v = part[w][r][b];
-#pragma unroll
-                for (int k = 1; k < KS; ++k) v += part[w + k][r][b];
-                acc[r][b] = v;
-            }
+            for (int b = 0; b < B; ++b)
+                if (lane == r * B + b) v = acc[r][b];
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            if (lane == r * B + b && b < a.batch && row0 + r < a.n_out)
-                a.out[(int64_t)b * a.n_out + row0 + r] = acc[r][b];
+    const int rl = lane / B, bl = lane % B;
+    if (lane < R * B && bl < a.batch && row0 + rl < a.n_out) a.out[(int64_t)bl * a.n_out + row0 + rl] = v;
 }
 
 // General path: row groups of LPR lanes, bounds-checked chunk loop.
@@ -302,19 +318,55 @@ template <int B, int R>
 KernelFn pick_split(int nch64)
 {
     switch (nch64) {
-        case 1: return q4k_gemv_fast<B, R, 1, 1>;
-        case 2: return q4k_gemv_fast<B, R, 2, 1>;
-        case 3: return q4k_gemv_fast<B, R, 3, 1>;
-        case 4: return q4k_gemv_fast<B, R, 2, 2>;
-        case 6: return q4k_gemv_fast<B, R, 3, 2>;
-        case 8: return q4k_gemv_fast<B, R, 2, 4>;
-        case 12: return q4k_gemv_fast<B, R, 3, 4>;
-        case 16: return q4k_gemv_fast<B, R, 4, 4>;
+        case 1: return q4k_gemv_fast<B, R, 1, 1, 4>;
+        case 2: return q4k_gemv_fast<B, R, 2, 1, 4>;
+        case 3: return q4k_gemv_fast<B, R, 3, 1, 4>;
+        case 4: return q4k_gemv_fast<B, R, 2, 2, 4>;
+        case 6: return q4k_gemv_fast<B, R, 3, 2, 4>;
+        case 8: return q4k_gemv_fast<B, R, 2, 4, 4>;
+        case 12: return q4k_gemv_fast<B, R, 3, 4, 4>;
+        case 16: return q4k_gemv_fast<B, R, 4, 4, 4>;
         default: return nullptr;
     }
 }
 
 int split_ks(int nch64) { return nch64 <= 3 ? 1 : (nch64 <= 6 ? 2 : 4); }
+
+// One batch row: one chunk column per wave (two above 8192 columns) and one
+// row group per workgroup, as the Q8_0 path, so the arithmetic left after a
+// wave's last load stays short.
+struct B1Shape { int ks, ch; };
+
+B1Shape b1_shape(int nch64)
+{
+    switch (nch64) {
+        case 1: return {1, 1};
+        case 2: return {2, 1};
+        case 3: return {3, 1};
+        case 4: return {4, 1};
+        case 6: return {6, 1};
+        case 8: return {8, 1};
+        case 12: return {6, 2};
+        case 16: return {8, 2};
+        default: return {0, 0};
+    }
+}
+
+template <int R>
+KernelFn pick_b1_split(int nch64)
+{
+    switch (nch64) {
+        case 1: return q4k_gemv_fast<1, R, 1, 1, 1>;
+        case 2: return q4k_gemv_fast<1, R, 1, 2, 2>;
+        case 3: return q4k_gemv_fast<1, R, 1, 3, 3>;
+        case 4: return q4k_gemv_fast<1, R, 1, 4, 4>;
+        case 6: return q4k_gemv_fast<1, R, 1, 6, 6>;
+        case 8: return q4k_gemv_fast<1, R, 1, 8, 8>;
+        case 12: return q4k_gemv_fast<1, R, 2, 6, 6>;
+        case 16: return q4k_gemv_fast<1, R, 2, 8, 8>;
+        default: return nullptr;
+    }
+}
 
 }  // namespace
 
@@ -335,16 +387,25 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
     const int nch64 = a.nch % 64 == 0 ? a.nch / 64 : 0;
     KernelFn fn = nullptr;
     int64_t blocks = 0;
-    if (nch64 > 0) {
+    int threads = 256;
+    if (nch64 > 0 && bt == 1) {
+        // 4 rows per wave (a Q4_K chunk costs ~50 VALU operations, so fewer
+        // rows per wave than Q8_0; measured best of 2, 4 and 8 on the 8192x3072
+        // and 3072x8192 shapes), halved while the grid would hold fewer than
+        // 3072 waves
+        const B1Shape sh = b1_shape(nch64);
+        int r = 4;
+        while (r > 1 && (n_out / r) * sh.ks < 3072) r >>= 1;
+        fn = r == 4 ? pick_b1_split<4>(nch64) : (r == 2 ? pick_b1_split<2>(nch64) : pick_b1_split<1>(nch64));
+        threads = 64 * sh.ks;
+        blocks = (n_out + r - 1) / r;
+    } else if (nch64 > 0) {
         const int ks = split_ks(nch64);
         const int groups = 4 / ks;
         int r = 4;
         while (r > 1 && n_out / ((int64_t)groups * r) < 512) r >>= 1;
         int r_eff = r;
         switch (bt) {
-            case 1:
-                fn = r == 4 ? pick_split<1, 4>(nch64) : (r == 2 ? pick_split<1, 2>(nch64) : pick_split<1, 1>(nch64));
-                break;
             case 2:
                 fn = r >= 2 ? pick_split<2, 2>(nch64) : pick_split<2, 1>(nch64);
                 r_eff = r >= 2 ? 2 : 1;
@@ -374,7 +435,7 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
         const int64_t rows_per_wave = 64 >> lpr_log2;
         blocks = ((n_out + rows_per_wave - 1) / rows_per_wave + 3) / 4;
     }
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, s, a);
     count_launch();
     return hipGetLastError();
 }
