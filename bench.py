@@ -248,6 +248,14 @@ def suite(args):
     xv, ov = xdev(synth.seed(4, 4), (1, 3072)), torch.empty((1, 128256), device=dev)
     timed("c4 q8_0_gemv vocab 128256x3072 b1", [lambda w=w: qd.q8_0_gemv(w, 3072, 128256, xv, out=ov) for w in wvoc],
           q8_bytes(128256, 3072) + 3072 * 4 + 128256 * 4, iters=40)
+    # the same projection with the on-device top-k (logits kept, k candidates out)
+    for k in (1, 40):
+        ti = torch.empty((1, k), dtype=torch.int32, device=dev)
+        tv = torch.empty((1, k), device=dev)
+        timed(f"c4 q8_0_gemv_topk vocab 128256x3072 b1 k={k}",
+              [lambda w=w: qd.q8_0_gemv_topk(w, 3072, 128256, xv, k, logits=ov, top_idx=ti, top_val=tv)
+               for w in wvoc],
+              q8_bytes(128256, 3072) + 3072 * 4 + 128256 * 4, iters=40)
     # launch cost of an empty kernel (the analogue of an empty submit round trip)
     timed("empty kernel", [lambda: qd.empty_kernel()], 0)
 

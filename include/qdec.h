@@ -40,9 +40,10 @@
  *     (QDEC_EINVAL): call qdec_prepare, which returns once the copy is
  *     complete, for every weight before capturing.
  *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in of
- *     1024..8192 in the supported steps) splits x into a library-owned device
- *     buffer, one per (device, stream), made on the first such call on that
- *     stream and freed by qdec_clear_cache.  Calls on one stream share it in
+ *     1024..8192 in the supported steps) splits x, and q8_0_gemv_topk keeps
+ *     its candidate lists, in a library-owned device buffer, one per
+ *     (device, stream), made (or grown) on the first such call on that stream
+ *     and freed by qdec_clear_cache.  Calls on one stream share it in
  *     stream order; calls on different streams never share one.  A stream
  *     capture cannot allocate it, so a capture on a stream that has none takes
  *     the VALU kernels (same results to the f32 tolerance).
@@ -115,6 +116,27 @@ QDEC_API int q8_0_qkv(const void* wq, const void* wk, const void* wv, int64_t n_
  * Conditions as q8_0_gemv. */
 QDEC_API int q8_0_swiglu(const void* w_gate, const void* w_up, int64_t n_in, int64_t n_out,
                 int64_t batch, const float* x, float* out, hipStream_t stream);
+
+/* Largest k of q8_0_gemv_topk. */
+#define QDEC_TOPK_MAX 256
+
+/* Vocabulary projection with on-device top-k ([QTensorEngine]
+ * dispatch_output_topk_chunked, and dispatch_output_top1_chunked for k = 1):
+ * logits = W x exactly as q8_0_gemv computes them (same kernels, same bits),
+ * written to `logits` (device f32, batch x n_out, kept for a sampler), then,
+ * per batch row, the k largest logits: top_idx[b*k + r] (int32 vocabulary row)
+ * and top_val[b*k + r] = logits[b*n_out + top_idx[b*k + r]], r = 0 first.
+ * Order: larger logit first; equal logits by smaller index; -0 equals +0
+ * (NaN logits, possible only from non-finite inputs, rank by bit pattern).
+ * 1 <= k <= min(n_out, QDEC_TOPK_MAX); other conditions as q8_0_gemv.  The
+ * candidate lists of n_out > 4096 live in the stream's workspace (see
+ * Conventions): a capturing stream must already hold one of at least
+ * 2 * batch * ceil(n_out/4096) * k * 8 bytes (make the same call on it once
+ * before capturing), else QDEC_EINVAL.  logits, top_idx, top_val and x must
+ * not overlap. */
+QDEC_API int q8_0_gemv_topk(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
+                   const float* x, int64_t k, float* logits, int32_t* top_idx,
+                   float* top_val, hipStream_t stream);
 
 /* Q4_K dequant-GEMV ([cuda_lane] try_q4k_soa_gemv): as q8_0_gemv over Q4_K
  * weights; n_in % 256 == 0, 1 <= batch <= 8. */

@@ -63,6 +63,8 @@ def _load():
             lib.oracle_q8_0_swiglu.restype = ctypes.c_int
             lib.oracle_silu.argtypes = [ctypes.c_double]
             lib.oracle_silu.restype = ctypes.c_double
+            lib.oracle_topk.argtypes = [P, I, I, I, P, P]
+            lib.oracle_topk.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -183,3 +185,16 @@ def q8_0_swiglu(w_gate, w_up, n_in: int, n_out: int, x):
 
 def silu(z: float) -> float:
     return _load().oracle_silu(float(z))
+
+
+def topk(values, k: int):
+    """(idx int32, val f32), each (batch, k): the k largest values of each row,
+    largest first, equal values by smaller index.  values is (batch, n) f32."""
+    v = _f32(values)
+    v2 = v.reshape(-1, v.shape[-1]) if v.ndim > 1 else v.reshape(1, -1)
+    batch, n = v2.shape
+    idx = np.empty((batch, k), np.int32)
+    val = np.empty((batch, k), np.float32)
+    if _load().oracle_topk(_ptr(np.ascontiguousarray(v2)), n, batch, k, _ptr(idx), _ptr(val)) != 0:
+        raise ValueError(f"topk: k={k} outside [1, n={n}], or a NaN value")
+    return idx, val

@@ -304,3 +304,52 @@ int oracle_q8_0_swiglu(const uint8_t* w_gate, const uint8_t* w_up, int64_t n_in,
     free(gg); free(uu);
     return rc;
 }
+
+/* ---------------------------------------------------------------- top-k -- */
+
+/* Vocabulary top-k ([P3] dispatch_output_topk_chunked, and
+ * dispatch_output_top1_chunked for k = 1): the k largest logits of each batch
+ * row with their vocabulary ids, largest first.  The pages fix no order among
+ * equal logits; the reading used is "equal values by smaller index", so top-1
+ * is the first maximum (the usual argmax convention).  Values compare
+ * numerically, so -0 and +0 are equal; NaN has no place in that order and is
+ * rejected.  Written as a plain sort of (value, index) pairs with the C
+ * library's qsort, then the first k. */
+typedef struct {
+    float v;
+    int64_t i;
+} topk_item;
+
+static int topk_cmp(const void* pa, const void* pb)
+{
+    const topk_item* a = (const topk_item*)pa;
+    const topk_item* b = (const topk_item*)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+int oracle_topk(const float* v, int64_t n, int64_t batch, int64_t k, int32_t* idx, float* val)
+{
+    if (n < 1 || batch < 1 || k < 1 || k > n || n > INT32_MAX) return -1;
+    topk_item* it = (topk_item*)malloc((size_t)n * sizeof(topk_item));
+    if (!it) return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t i = 0; i < n; ++i) {
+            const float f = v[b * n + i];
+            if (isnan(f)) {
+                free(it);
+                return -1;
+            }
+            it[i].v = f;
+            it[i].i = i;
+        }
+        qsort(it, (size_t)n, sizeof(topk_item), topk_cmp);
+        for (int64_t r = 0; r < k; ++r) {
+            idx[b * k + r] = (int32_t)it[r].i;
+            val[b * k + r] = it[r].v;
+        }
+    }
+    free(it);
+    return 0;
+}

@@ -5,7 +5,7 @@ Argument marshalling only.  Every function takes torch tensors that live on the
 GPU, passes their device pointers and the current HIP stream to the C ABI of the
 same name, and raises QdecError on a non-zero status.  All arithmetic runs in
 the library's HIP kernels; there is no CPU path.  The library must have been
-built (``python -m quantized_decode_ggml_amd._build`` or
+built (``python quantized_decode_ggml_amd/_build.py`` or
 ``__graft_entry__.build()``); importing this package without it raises.
 """
 from __future__ import annotations
@@ -24,9 +24,10 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qdec.h")
 QDEC_OK, QDEC_EINVAL, QDEC_ENOMEM, QDEC_EHIP, QDEC_EUNSUPPORTED = 0, -1, -2, -3, -4
 TYPE_Q8_0, TYPE_Q4_K = 8, 12
 GEMV_MAX_BATCH = 8
+TOPK_MAX = 256
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it first (quantized_decode_ggml_amd._build.build())")
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python quantized_decode_ggml_amd/_build.py)")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -38,6 +39,7 @@ _SIGS = {
     "q8_0_qkv": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P],
     "q8_0_swiglu": [_P, _P, _I, _I, _I, _P, _P, _P],
     "q4k_gemv": [_P, _I, _I, _I, _P, _P, _P],
+    "q8_0_gemv_topk": [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P],
     "q8_0_gemm_batched": [_P, _I, _I, _I, _P, _P, _P],
     "f32_gemm_batched": [_P, _I, _I, _I, _P, _P, _P],
     "qdec_prepare": [_P, ctypes.c_int, _I, _I, _P],
@@ -170,6 +172,20 @@ def q8_0_swiglu(w_gate, w_up, n_in, n_out, x, out=None, stream=None):
                            _stream(stream)))
     _track(w_gate, w_up)
     return out
+
+
+def q8_0_gemv_topk(w, n_in, n_out, x, k, logits=None, top_idx=None, top_val=None, stream=None):
+    """Vocabulary projection plus on-device top-k: returns (top_idx int32
+    (batch, k), top_val f32 (batch, k), logits f32 (batch, n_out))."""
+    batch = _batch(x, n_in)
+    logits = _f32_out(logits, batch, n_out, x)
+    if top_idx is None:
+        top_idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
+    top_val = _f32_out(top_val, batch, k, x)
+    _check(lib.q8_0_gemv_topk(_ptr(w), n_in, n_out, batch, _ptr(x), k, _ptr(logits), _ptr(top_idx),
+                              _ptr(top_val), _stream(stream)))
+    _track(w)
+    return top_idx, top_val, logits
 
 
 def q4k_gemv(w, n_in, n_out, x, out=None, stream=None):

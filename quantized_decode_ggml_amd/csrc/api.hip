@@ -363,6 +363,42 @@ int q8_0_swiglu(const void* w_gate, const void* w_up, int64_t n_in, int64_t n_ou
                           stream);
 }
 
+int q8_0_gemv_topk(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, int64_t k,
+                   float* logits, int32_t* top_idx, float* top_val, hipStream_t stream)
+{
+    const char* fn = "q8_0_gemv_topk";
+    QDEC_TRY(check_dims(fn, n_in, n_out, batch, 32, QDEC_GEMV_MAX_BATCH));
+    if (k < 1 || k > QDEC_TOPK_MAX || k > n_out)
+        return fail(QDEC_EINVAL, "%s: k=%lld outside [1, min(n_out, %d)]", fn, (long long)k, QDEC_TOPK_MAX);
+    QDEC_TRY(check_ptr(fn, "top_idx", top_idx, 4));
+    QDEC_TRY(check_ptr(fn, "top_val", top_val, 4));
+    QDEC_TRY(check_ptr(fn, "logits", logits, 4));
+    const int64_t lb = batch * n_out * 4, tb = batch * k * 4;
+    if (overlaps(top_idx, tb, top_val, tb) || overlaps(top_idx, tb, logits, lb) || overlaps(top_val, tb, logits, lb) ||
+        overlaps(top_idx, tb, x, batch * n_in * 4) || overlaps(top_val, tb, x, batch * n_in * 4))
+        return fail(QDEC_EINVAL, "%s: top_idx, top_val, logits and x must not overlap", fn);
+    // the candidate buffers are checked before anything is launched
+    const int64_t need = topk_workspace_bytes(n_out, batch, (int)k);
+    if (need > 0) {
+        void* probe = nullptr;
+        QDEC_TRY(stream_workspace(stream, need, &probe));
+        if (!probe)
+            return fail(QDEC_EINVAL, "%s: no top-k workspace on this capturing stream: make one call on the "
+                        "stream before capturing it", fn);
+    }
+    const void* ws[1] = {w};
+    const int64_t rows[1] = {n_out};
+    float* outs[1] = {logits};
+    QDEC_TRY(q8_gemv_common(kPlain, fn, ws, 1, n_in, rows, batch, x, nullptr, outs, 1, stream));
+    // the projection may have grown the stream's workspace: fetch it again
+    void* wsp = nullptr;
+    if (need > 0) {
+        QDEC_TRY(stream_workspace(stream, need, &wsp));
+        if (!wsp) return fail(QDEC_EINVAL, "%s: top-k workspace vanished", fn);
+    }
+    return finish(launch_topk(logits, n_out, batch, (int)k, wsp, top_idx, top_val, stream), fn);
+}
+
 int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
              hipStream_t stream)
 {

@@ -146,6 +146,13 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
 hipError_t launch_f32_gemm(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, hipStream_t s);
 
+// Top-k of batch rows of n_out logits (1 <= k <= 256): the workspace holds two
+// candidate buffers of batch * ceil(n_out / 4096) * k 64-bit keys (none for
+// n_out <= 4096).
+int64_t topk_workspace_bytes(int64_t n_out, int64_t batch, int k);
+hipError_t launch_topk(const float* logits, int64_t n_out, int64_t batch, int k, void* workspace,
+                       int32_t* top_idx, float* top_val, hipStream_t s);
+
 hipError_t launch_empty(hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 

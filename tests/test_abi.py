@@ -49,6 +49,11 @@ def test_initial_state():
     lambda L: L.q8_0_dequantize(FAKE, 64, 8, FAKE * 2 + 4, None),         # out not 16-aligned
     lambda L: L.qdec_copy(FAKE, FAKE * 2, 24, None),                      # bytes % 16
     lambda L: L.qdec_release(None),
+    lambda L: L.q8_0_gemv_topk(FAKE, 64, 16, 1, FAKE, 0, FAKE * 2, FAKE * 3, FAKE * 4, None),    # k = 0
+    lambda L: L.q8_0_gemv_topk(FAKE, 64, 16, 1, FAKE, 17, FAKE * 2, FAKE * 3, FAKE * 4, None),   # k > n_out
+    lambda L: L.q8_0_gemv_topk(FAKE, 64, 400, 1, FAKE, 257, FAKE * 2, FAKE * 3, FAKE * 4, None), # k > 256
+    lambda L: L.q8_0_gemv_topk(FAKE, 64, 16, 1, FAKE, 4, FAKE * 2, FAKE * 2 + 8, FAKE * 4, None),  # idx in logits
+    lambda L: L.q8_0_gemv_topk(FAKE, 64, 16, 1, FAKE, 4, FAKE * 2, FAKE * 3, None, None),          # null top_val
 ])
 def test_invalid_arguments_rejected(call):
     before = qd.launch_count()

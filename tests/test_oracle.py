@@ -439,3 +439,75 @@ def test_swiglu_matches_gemvs():
     # silu(g) = g * sigmoid(g), with sigmoid from its tanh form (a different formula)
     sig = 0.5 * (1.0 + np.tanh(0.5 * g))
     assert np.allclose(r["out"], g * sig * u, rtol=1e-13, atol=1e-300)
+
+
+# ------------------------------------------------------------------ top-k --
+# Reading (the pages fix no order among equal logits): larger value first,
+# equal values by smaller index; -0 equals +0; NaN rejected.
+
+def _ranks_before(a, b, v):
+    """Does index a rank before index b? (stated order, written independently
+    of the oracle's comparator)"""
+    return v[a] > v[b] or (v[a] == v[b] and a < b)
+
+
+def test_topk_hand_example():
+    v = np.array([[1.0, 5.0, 3.0, 5.0, -2.0, 0.0]], np.float32)
+    idx, val = oracle.topk(v, 3)
+    assert idx.tolist() == [[1, 3, 2]]
+    assert val.tolist() == [[5.0, 5.0, 3.0]]
+    idx, _ = oracle.topk(v, 6)
+    assert idx.tolist() == [[1, 3, 2, 0, 5, 4]]
+
+
+def test_topk_first_maximum_is_argmax():
+    rng = np.random.default_rng(71)
+    v = rng.integers(-3, 4, size=(6, 50)).astype(np.float32)   # many ties
+    idx, val = oracle.topk(v, 1)
+    assert (idx[:, 0] == np.argmax(v, axis=1)).all()            # numpy returns the first maximum
+    assert (val[:, 0] == v.max(axis=1)).all()
+
+
+def test_topk_brute_force_small():
+    """Every selected index ranks before every unselected one, and the list is
+    in rank order; checked by pairwise comparison on tiny rows with ties."""
+    rng = np.random.default_rng(72)
+    for _ in range(200):
+        n = int(rng.integers(1, 9))
+        k = int(rng.integers(1, n + 1))
+        v = rng.choice(np.array([-1.5, 0.0, 2.0, 2.5], np.float32), size=(1, n))
+        idx, val = oracle.topk(v, k)
+        sel = idx[0].tolist()
+        assert len(set(sel)) == k
+        rest = [i for i in range(n) if i not in sel]
+        assert all(_ranks_before(a, b, v[0]) for a in sel for b in rest)
+        assert all(_ranks_before(sel[r], sel[r + 1], v[0]) for r in range(k - 1))
+        assert (val[0] == v[0][sel]).all()
+
+
+def test_topk_signed_zero_and_infinities():
+    v = np.array([[-0.0, 0.0, -0.0, np.inf, -np.inf]], np.float32)
+    idx, val = oracle.topk(v, 5)
+    assert idx.tolist() == [[3, 0, 1, 2, 4]]
+    assert np.signbit(val[0][1]) and not np.signbit(val[0][2])   # the values keep their own bits
+
+
+def test_topk_batch_rows_independent():
+    rng = np.random.default_rng(73)
+    v = rng.standard_normal((4, 300)).astype(np.float32)
+    idx, val = oracle.topk(v, 7)
+    for b in range(4):
+        i1, v1 = oracle.topk(v[b:b + 1], 7)
+        assert (i1[0] == idx[b]).all() and (v1[0] == val[b]).all()
+        assert (np.sort(v[b])[::-1][:7] == val[b]).all()
+
+
+def test_topk_rejects_bad_arguments():
+    v = np.zeros((1, 4), np.float32)
+    with pytest.raises(ValueError):
+        oracle.topk(v, 5)
+    with pytest.raises(ValueError):
+        oracle.topk(v, 0)
+    v[0, 2] = np.nan
+    with pytest.raises(ValueError):
+        oracle.topk(v, 1)

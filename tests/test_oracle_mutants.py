@@ -33,6 +33,9 @@ MUTANTS = {
     "qkv_k_reads_q": ("oracle_q8_0_gemv(wk, n_in, n_kv", "oracle_q8_0_gemv(wq, n_in, n_kv"),
     "fp16_bias": ("ldexpf((float)(1024 + f), e - 25)", "ldexpf((float)(1024 + f), e - 24)"),
     "fp16_subnormal_scale": ("ldexpf((float)f, -24)", "ldexpf((float)f, -25)"),
+    "topk_ties_larger_index_first": ("return (a->i < b->i) ? -1 : (a->i > b->i);", "return (a->i > b->i) ? -1 : (a->i < b->i);"),
+    "topk_smallest_first": ("if (a->v > b->v) return -1;\n    if (a->v < b->v) return 1;", "if (a->v < b->v) return -1;\n    if (a->v > b->v) return 1;"),
+    "topk_off_by_one": ("val[b * k + r] = it[r].v;", "val[b * k + r] = it[r + (r + 1 < n)].v;"),
 }
 
 
