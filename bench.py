@@ -214,6 +214,30 @@ def suite(args):
               [lambda w=w: qd.q8_0_gemv_residual(w, 8192, 3072, m2, r2, out=o2) for w in wdn],
               q8_bytes(3072, 8192) + b * 8192 * 4 + b * 3072 * 8)
     del wg, wu2
+    # chained pre-norm block at batch 1 (next-row f2): RMSNorm+QKV, O-proj+residual,
+    # RMSNorm+SwiGLU, down+residual; 4 launches per block, blocks rotate
+    E, NQ, NKV, FF = 3072, 3072, 1024, 8192
+    blk = q8_bytes(NQ + 2 * NKV, E) + q8_bytes(E, NQ) + 2 * q8_bytes(FF, E) + q8_bytes(E, FF)
+    Lb = copies_for(blk)
+    bw = {k: q8_dev(5, i, r, c, Lb) for i, (k, r, c) in enumerate(
+        (("q", NQ, E), ("k", NKV, E), ("v", NKV, E), ("o", E, NQ), ("g", FF, E), ("u", FF, E), ("d", E, FF)))}
+    g1 = torch.from_numpy((1.0 + 0.1 * synth.normal_f32(synth.seed(5, 10), (E,))).astype(np.float32)).to(dev)
+    g2 = torch.from_numpy((1.0 + 0.1 * synth.normal_f32(synth.seed(5, 11), (E,))).astype(np.float32)).to(dev)
+    hb = xdev(synth.seed(5, 12), (1, E))
+    qb, kb, vb = (torch.empty((1, n), device=dev) for n in (NQ, NKV, NKV))
+    sb = torch.empty((1, FF + E), device=dev)
+
+    def block(i):
+        qd.q8_0_rmsnorm_qkv(bw["q"][i], bw["k"][i], bw["v"][i], E, NQ, NKV, hb, g1, 1e-5, q_out=qb, k_out=kb,
+                            v_out=vb)
+        qd.q8_0_attn_out_ffn(bw["o"][i], bw["g"][i], bw["u"][i], bw["d"][i], E, NQ, FF, hb, qb, g2, 1e-5,
+                             scratch=sb)
+
+    # bytes: weights + activations read and written by the four products and the folded norms
+    act = 4 * (E + E + (NQ + 2 * NKV) + NQ + 2 * E + E + FF + FF + 2 * E)
+    timed("f2 pre-norm block b1 (norm+QKV, O+res, norm+SwiGLU, down+res; 4 launches)",
+          [lambda i=i: block(i) for i in range(Lb)], blk + act, iters=40)
+    del bw
     # config 3: batched GEMM (Q8_0 weights reuse up/down rotations; dense f32 separate)
     for B in (128, 512):
         for nm, ws, n_out, n_in in (("up 8192x3072", wup, 8192, 3072), ("down 3072x8192", wdn, 3072, 8192)):

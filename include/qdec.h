@@ -138,6 +138,46 @@ QDEC_API int q8_0_gemv_topk(const void* w, int64_t n_in, int64_t n_out, int64_t 
                    const float* x, int64_t k, float* logits, int32_t* top_idx,
                    float* top_val, hipStream_t stream);
 
+/* RMSNorm ([QTensorEngine] apply_output_norm_inplace, the pre-norm model's
+ * output_norm; the pages give no formula, the usual one is used):
+ * out[b][j] = x[b][j] / sqrt(mean_j x[b][j]^2 + eps) * w[j], any batch >= 1
+ * and n >= 1, 0 <= eps <= 1; the sum of squares and the root are taken in f64
+ * (no overflow for any f32 row), the products in f32.  out may be x (in place) but must not
+ * overlap it otherwise.  x, w, out are device f32. */
+QDEC_API int qdec_rmsnorm(const float* x, int64_t n, int64_t batch, const float* w, float eps,
+                 float* out, hipStream_t stream);
+
+/* Attention input of a pre-norm decode block: (q, k, v) = QKV(RMSNorm(h;
+ * norm_w, eps)) as q8_0_qkv over the normalised rows ([cuda_lane]
+ * try_q4k_soa_qkv, [QTensorEngine] dispatch_transformer_layer).  One batch row
+ * at n_in a multiple of 1024 (up to 16384) folds the norm into the product:
+ * out = r * (W (norm_w * h)), r = 1/sqrt(mean h^2 + eps), one launch, scratch
+ * unused (may be NULL).  Otherwise h is normalised into scratch (device f32,
+ * batch x n_in, 16-byte aligned) first.  norm_w: device f32 n_in, 16-byte
+ * aligned.  Other conditions as q8_0_qkv. */
+QDEC_API int q8_0_rmsnorm_qkv(const void* wq, const void* wk, const void* wv, int64_t n_in,
+                     int64_t n_q, int64_t n_kv, int64_t batch, const float* h,
+                     const float* norm_w, float eps, float* q_out, float* k_out,
+                     float* v_out, float* scratch, hipStream_t stream);
+
+/* The rest of a pre-norm decode block once attention has produced `attn`
+ * (batch x n_q; the attention core itself -- RoPE, KV cache, softmax -- is
+ * not part of this library):
+ *   h <- h + Wo attn                          (Wo: n_embd x n_q)
+ *   f  = SwiGLU(RMSNorm(h; ffn_norm, eps))    (gate, up: n_ff x n_embd)
+ *   h <- h + Wd f                             (Wd: n_embd x n_ff)
+ * three launches at one batch row (the norm folded into the SwiGLU product),
+ * four otherwise ([QTensorEngine] dispatch_transformer_layer,
+ * [cuda_lane] try_q4k_soa_fused_swiglu and try_q4k_soa_ffn_block_residual).
+ * h: device f32 batch x n_embd, updated in place.  scratch: device f32 of
+ * batch x (n_ff + n_embd) floats, 16-byte aligned, not overlapping h or attn
+ * (f, then the normalised h).  n_q, n_embd, n_ff multiples of 32;
+ * 1 <= batch <= 8. */
+QDEC_API int q8_0_attn_out_ffn(const void* wo, const void* w_gate, const void* w_up,
+                      const void* w_down, int64_t n_embd, int64_t n_q, int64_t n_ff,
+                      int64_t batch, float* h, const float* attn, const float* ffn_norm,
+                      float eps, float* scratch, hipStream_t stream);
+
 /* Q4_K dequant-GEMV ([cuda_lane] try_q4k_soa_gemv): as q8_0_gemv over Q4_K
  * weights; n_in % 256 == 0, 1 <= batch <= 8. */
 QDEC_API int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,

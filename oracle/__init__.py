@@ -65,6 +65,8 @@ def _load():
             lib.oracle_silu.restype = ctypes.c_double
             lib.oracle_topk.argtypes = [P, I, I, I, P, P]
             lib.oracle_topk.restype = ctypes.c_int
+            lib.oracle_rmsnorm.argtypes = [P, I, I, P, ctypes.c_double, P]
+            lib.oracle_rmsnorm.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -198,3 +200,33 @@ def topk(values, k: int):
     if _load().oracle_topk(_ptr(np.ascontiguousarray(v2)), n, batch, k, _ptr(idx), _ptr(val)) != 0:
         raise ValueError(f"topk: k={k} outside [1, n={n}], or a NaN value")
     return idx, val
+
+
+def rmsnorm(x, w, eps: float) -> np.ndarray:
+    """f64 (batch, n): x / sqrt(mean(x^2) + eps) * w per row (oracle.c)."""
+    wv = _f32(w).reshape(-1)
+    n = wv.size
+    xv = _f32(x).reshape(-1)
+    batch = xv.size // n
+    assert xv.size == batch * n and batch >= 1
+    out = np.empty((batch, n), np.float64)
+    if _load().oracle_rmsnorm(_ptr(xv), n, batch, _ptr(wv), float(eps), _ptr(out)) != 0:
+        raise ValueError("rmsnorm: bad arguments")
+    return out
+
+
+def q8_0_gemv_f64(w, n_in: int, n_out: int, y) -> tuple[np.ndarray, np.ndarray]:
+    """(out, S) for an f64 input y (batch, n_in), e.g. a normalised vector that
+    never exists in f32: out = deq(W) y and S = |deq(W)| |y|, with deq from
+    q8_0_dequantize (exact f32) and numpy's f64 matrix product as the step."""
+    y = np.asarray(y, np.float64).reshape(-1, n_in)
+    deq = q8_0_dequantize(w, n_in, n_out).astype(np.float64)
+    return y @ deq.T, np.abs(y) @ np.abs(deq).T
+
+
+def q8_0_swiglu_f64(w_gate, w_up, n_in: int, n_out: int, y) -> dict:
+    """As q8_0_swiglu for an f64 input y: dict with out, g, u, Sg, Su."""
+    g, sg = q8_0_gemv_f64(w_gate, n_in, n_out, y)
+    u, su = q8_0_gemv_f64(w_up, n_in, n_out, y)
+    silu_g = g / (1.0 + np.exp(-g))          # silu(z) = z / (1 + e^-z), as oracle_silu
+    return {"out": silu_g * u, "g": g, "u": u, "Sg": sg, "Su": su}

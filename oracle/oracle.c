@@ -353,3 +353,22 @@ int oracle_topk(const float* v, int64_t n, int64_t batch, int64_t k, int32_t* id
     free(it);
     return 0;
 }
+
+/* -------------------------------------------------------------- RMSNorm -- */
+
+/* RMSNorm ([P3] apply_output_norm_inplace: the output_norm of a pre-norm model,
+ * applied before the vocabulary projection; the same normalisation precedes a
+ * block's attention and FFN products).  The pages print no formula; the usual
+ * definition is used, in f64:
+ *   out[b][j] = x[b][j] / sqrt(mean_j x[b][j]^2 + eps) * w[j]. */
+int oracle_rmsnorm(const float* x, int64_t n, int64_t batch, const float* w, double eps, double* out)
+{
+    if (n < 1 || batch < 1 || !(eps >= 0.0)) return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < n; ++j) ss += (double)x[b * n + j] * (double)x[b * n + j];
+        const double r = 1.0 / sqrt(ss / (double)n + eps);
+        for (int64_t j = 0; j < n; ++j) out[b * n + j] = (double)x[b * n + j] * r * (double)w[j];
+    }
+    return 0;
+}

@@ -40,6 +40,9 @@ _SIGS = {
     "q8_0_swiglu": [_P, _P, _I, _I, _I, _P, _P, _P],
     "q4k_gemv": [_P, _I, _I, _I, _P, _P, _P],
     "q8_0_gemv_topk": [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P],
+    "qdec_rmsnorm": [_P, _I, _I, _P, ctypes.c_float, _P, _P],
+    "q8_0_rmsnorm_qkv": [_P, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P],
+    "q8_0_attn_out_ffn": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_float, _P, _P],
     "q8_0_gemm_batched": [_P, _I, _I, _I, _P, _P, _P],
     "f32_gemm_batched": [_P, _I, _I, _I, _P, _P, _P],
     "qdec_prepare": [_P, ctypes.c_int, _I, _I, _P],
@@ -186,6 +189,45 @@ def q8_0_gemv_topk(w, n_in, n_out, x, k, logits=None, top_idx=None, top_val=None
                               _ptr(top_val), _stream(stream)))
     _track(w)
     return top_idx, top_val, logits
+
+
+def rmsnorm(x, w, eps, out=None, stream=None):
+    """out = x / sqrt(mean(x^2) + eps) * w per row; out may be x (in place)."""
+    n = w.numel()
+    batch = _batch(x, n)
+    out = _f32_out(out, batch, n, x)
+    _check(lib.qdec_rmsnorm(_ptr(x), n, batch, _ptr(w), float(eps), _ptr(out), _stream(stream)))
+    return out
+
+
+def q8_0_rmsnorm_qkv(wq, wk, wv, n_in, n_q, n_kv, h, norm_w, eps, q_out=None, k_out=None, v_out=None,
+                     scratch=None, stream=None):
+    """(q, k, v) = QKV(RMSNorm(h)); scratch (batch x n_in) is made when the
+    norm cannot be folded (several batch rows) and none is given."""
+    batch = _batch(h, n_in)
+    q_out = _f32_out(q_out, batch, n_q, h)
+    k_out = _f32_out(k_out, batch, n_kv, h)
+    v_out = _f32_out(v_out, batch, n_kv, h)
+    if scratch is None and batch > 1:
+        scratch = torch.empty((batch, n_in), dtype=torch.float32, device=h.device)
+    _check(lib.q8_0_rmsnorm_qkv(_ptr(wq), _ptr(wk), _ptr(wv), n_in, n_q, n_kv, batch, _ptr(h), _ptr(norm_w),
+                                float(eps), _ptr(q_out), _ptr(k_out), _ptr(v_out), _ptr(scratch),
+                                _stream(stream)))
+    _track(wq, wk, wv)
+    return q_out, k_out, v_out
+
+
+def q8_0_attn_out_ffn(wo, w_gate, w_up, w_down, n_embd, n_q, n_ff, h, attn, ffn_norm, eps, scratch=None,
+                      stream=None):
+    """h += Wo attn; h += Wd SwiGLU(RMSNorm(h)), in place; returns h."""
+    batch = _batch(h, n_embd)
+    if scratch is None:
+        scratch = torch.empty((batch, n_ff + n_embd), dtype=torch.float32, device=h.device)
+    _check(lib.q8_0_attn_out_ffn(_ptr(wo), _ptr(w_gate), _ptr(w_up), _ptr(w_down), n_embd, n_q, n_ff, batch,
+                                 _ptr(h), _ptr(attn), _ptr(ffn_norm), float(eps), _ptr(scratch),
+                                 _stream(stream)))
+    _track(wo, w_gate, w_up, w_down)
+    return h
 
 
 def q4k_gemv(w, n_in, n_out, x, out=None, stream=None):

@@ -246,7 +246,8 @@ int finish(hipError_t e, const char* what)
 
 int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw, int64_t n_in,
                    const int64_t* rows, int64_t batch, const float* x, const float* residual,
-                   float* const* outs, int nout, hipStream_t s)
+                   float* const* outs, int nout, hipStream_t s, const float* norm_w = nullptr,
+                   float eps = 0.0f)
 {
     for (int k = 0; k < nw; ++k) QDEC_TRY(check_ptr(fn, "weight", ws[k], 2));
     QDEC_TRY(check_ptr(fn, "x", x, 16));
@@ -270,6 +271,13 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
     p.residual = residual;
     p.n_in = n_in;
     p.batch = batch;
+    if (norm_w) {
+        // callers pass a norm only where it folds into the one-row kernel
+        p.norm_w = norm_w;
+        p.eps = eps;
+        if (!q8_gemv_norm_fusable(p)) return fail(QDEC_EINVAL, "%s: RMSNorm cannot be folded here", fn);
+        return finish(launch_q8_0_gemv(p, s), fn);
+    }
     if (q8_mfma_supported(p)) {
         // tiled copies and a workspace; inside a capture either may be missing,
         // and the VALU kernels then run instead
@@ -286,6 +294,26 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
         if (have && wsp) return finish(launch_q8_0_gemv_mfma(p, tiles, wsp, s), fn);
     }
     return finish(launch_q8_0_gemv(p, s), fn);
+}
+
+// y = RMSNorm(x) feeding a Q8_0 product of `mode`: folded into the one-row
+// kernel where it can be, else normalised into `scratch` first.
+int q8_normed_product(GemvMode mode, const char* fn, const void* const* ws, int nw, int64_t n_in,
+                      const int64_t* rows, int64_t batch, const float* x, const float* norm_w, float eps,
+                      float* const* outs, int nout, float* scratch, hipStream_t s)
+{
+    QDEC_TRY(check_ptr(fn, "norm_w", norm_w, 16));
+    if (!(eps >= 0.0f) || eps > 1.0f) return fail(QDEC_EINVAL, "%s: eps=%g outside [0, 1]", fn, (double)eps);
+    Q8GemvProblem probe{};
+    probe.batch = batch;
+    probe.n_in = n_in;
+    if (q8_gemv_norm_fusable(probe))
+        return q8_gemv_common(mode, fn, ws, nw, n_in, rows, batch, x, nullptr, outs, nout, s, norm_w, eps);
+    QDEC_TRY(check_ptr(fn, "scratch", scratch, 16));
+    if (overlaps(scratch, batch * n_in * 4, x, batch * n_in * 4))
+        return fail(QDEC_EINVAL, "%s: scratch overlaps the input", fn);
+    QDEC_TRY(finish(launch_rmsnorm(x, n_in, batch, norm_w, eps, scratch, s), fn));
+    return q8_gemv_common(mode, fn, ws, nw, n_in, rows, batch, scratch, nullptr, outs, nout, s);
 }
 
 }  // namespace
@@ -397,6 +425,77 @@ int q8_0_gemv_topk(const void* w, int64_t n_in, int64_t n_out, int64_t batch, co
         if (!wsp) return fail(QDEC_EINVAL, "%s: top-k workspace vanished", fn);
     }
     return finish(launch_topk(logits, n_out, batch, (int)k, wsp, top_idx, top_val, stream), fn);
+}
+
+int qdec_rmsnorm(const float* x, int64_t n, int64_t batch, const float* w, float eps, float* out, hipStream_t stream)
+{
+    const char* fn = "qdec_rmsnorm";
+    if (n < 1 || n > INT32_MAX || batch < 1 || batch > INT32_MAX)
+        return fail(QDEC_EINVAL, "%s: n=%lld batch=%lld out of range", fn, (long long)n, (long long)batch);
+    if (!(eps >= 0.0f) || eps > 1.0f) return fail(QDEC_EINVAL, "%s: eps=%g outside [0, 1]", fn, (double)eps);
+    QDEC_TRY(check_ptr(fn, "x", x, 4));
+    QDEC_TRY(check_ptr(fn, "w", w, 4));
+    QDEC_TRY(check_ptr(fn, "out", out, 4));
+    if (out != x && overlaps(out, batch * n * 4, x, batch * n * 4))
+        return fail(QDEC_EINVAL, "%s: out overlaps x without being x", fn);
+    return finish(launch_rmsnorm(x, n, batch, w, eps, out, stream), fn);
+}
+
+int q8_0_rmsnorm_qkv(const void* wq, const void* wk, const void* wv, int64_t n_in, int64_t n_q, int64_t n_kv,
+                     int64_t batch, const float* h, const float* norm_w, float eps, float* q_out, float* k_out,
+                     float* v_out, float* scratch, hipStream_t stream)
+{
+    const char* fn = "q8_0_rmsnorm_qkv";
+    QDEC_TRY(check_dims(fn, n_in, n_q, batch, 32, QDEC_GEMV_MAX_BATCH));
+    if (n_kv < 1 || n_kv > n_q) return fail(QDEC_EINVAL, "%s: n_kv=%lld outside [1, n_q]", fn, (long long)n_kv);
+    const void* ws[3] = {wq, wk, wv};
+    const int64_t rows[3] = {n_q, n_kv, n_kv};
+    float* outs[3] = {q_out, k_out, v_out};
+    for (int a = 0; a < 3; ++a)
+        for (int b = a + 1; b < 3; ++b)
+            if (outs[a] && outs[b] && overlaps(outs[a], batch * rows[a] * 4, outs[b], batch * rows[b] * 4))
+                return fail(QDEC_EINVAL, "%s: outputs overlap", fn);
+    if (scratch)
+        for (int a = 0; a < 3; ++a)
+            if (outs[a] && overlaps(outs[a], batch * rows[a] * 4, scratch, batch * n_in * 4))
+                return fail(QDEC_EINVAL, "%s: an output overlaps scratch", fn);
+    return q8_normed_product(kQKV, fn, ws, 3, n_in, rows, batch, h, norm_w, eps, outs, 3, scratch, stream);
+}
+
+int q8_0_attn_out_ffn(const void* wo, const void* w_gate, const void* w_up, const void* w_down, int64_t n_embd,
+                      int64_t n_q, int64_t n_ff, int64_t batch, float* h, const float* attn, const float* ffn_norm,
+                      float eps, float* scratch, hipStream_t stream)
+{
+    const char* fn = "q8_0_attn_out_ffn";
+    QDEC_TRY(check_dims(fn, n_q, n_embd, batch, 32, QDEC_GEMV_MAX_BATCH));
+    QDEC_TRY(check_dims(fn, n_embd, n_ff, batch, 32, QDEC_GEMV_MAX_BATCH));
+    QDEC_TRY(check_dims(fn, n_ff, n_embd, batch, 32, QDEC_GEMV_MAX_BATCH));
+    QDEC_TRY(check_ptr(fn, "h", h, 16));
+    QDEC_TRY(check_ptr(fn, "scratch", scratch, 16));
+    const int64_t hb = batch * n_embd * 4, fb = batch * n_ff * 4;
+    if (overlaps(scratch, fb + hb, h, hb) || overlaps(scratch, fb + hb, attn, batch * n_q * 4))
+        return fail(QDEC_EINVAL, "%s: scratch overlaps h or attn", fn);
+    float* f = scratch;                 // batch x n_ff: SwiGLU output
+    float* hn = scratch + batch * n_ff; // batch x n_embd: normalised h (several batch rows)
+    // h += Wo attn
+    {
+        const void* ws[1] = {wo};
+        const int64_t rows[1] = {n_embd};
+        float* outs[1] = {h};
+        QDEC_TRY(q8_gemv_common(kResidual, fn, ws, 1, n_q, rows, batch, attn, h, outs, 1, stream));
+    }
+    // f = SwiGLU(RMSNorm(h))
+    {
+        const void* ws[2] = {w_gate, w_up};
+        const int64_t rows[2] = {n_ff, n_ff};
+        float* outs[1] = {f};
+        QDEC_TRY(q8_normed_product(kSwiGLU, fn, ws, 2, n_embd, rows, batch, h, ffn_norm, eps, outs, 1, hn, stream));
+    }
+    // h += Wd f
+    const void* ws[1] = {w_down};
+    const int64_t rows[1] = {n_embd};
+    float* outs[1] = {h};
+    return q8_gemv_common(kResidual, fn, ws, 1, n_ff, rows, batch, f, h, outs, 1, stream);
 }
 
 int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,

@@ -36,6 +36,8 @@ struct Q8GemvArgs {
     int batch;
     int lpr_log2;         // general path: lanes per row group = 1 << lpr_log2
     int nch;              // 16-byte chunks per row = n_in / 16
+    const float* norm_w;  // RMSNorm weights folded into a one-row product, or null
+    float eps;
 };
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -124,6 +126,8 @@ inline Q8GemvArgs make_q8_gemv_args(const Q8GemvProblem& p)
     a.total_rows = p.mode == kSwiGLU ? p.rows[0] : end;
     a.batch = (int)p.batch;
     a.nch = (int)(p.n_in / 16);
+    a.norm_w = p.norm_w;
+    a.eps = p.eps;
     return a;
 }
 

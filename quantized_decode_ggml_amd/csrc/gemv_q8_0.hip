@@ -151,6 +151,7 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
     static_assert(!XL || NW == 4, "the LDS copy of x assumes 256 threads");
     constexpr bool XREG = !XL && B * CH <= 4;        // x in registers (<= 64 VGPRs)
     __shared__ float part[KS > 1 ? NW : 1][R][NM][B];
+    __shared__ double part_ss[KS > 1 && B == 1 ? NW : 1];    // folded RMSNorm: sum of squares per wave
     extern __shared__ __attribute__((aligned(16))) float xs[];
 
     const int lane = threadIdx.x & 63;
@@ -183,6 +184,18 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
         for (int k = 0; k < CH; ++k)
 #pragma unroll
             for (int b = 0; b < B; ++b) load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xr[k][b]);
+    }
+    // One batch row may fold an RMSNorm of x into the product: the norm
+    // weights of the wave's columns are loaded with x (before the weight
+    // stream) and applied after the weight loads are issued.
+    constexpr bool NORM_OK = B == 1 && XREG;
+    const bool norm = NORM_OK && a.norm_w != nullptr;
+    float gr[NORM_OK ? CH : 1][16];
+    if constexpr (NORM_OK) {
+        if (norm) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) load_x16(a.norm_w + (int64_t)(lane + 64 * (cbase + k)) * 16, gr[k]);
+        }
     }
 
     // Row pointers (scalar work shared by every wave of a CU, so kept short):
@@ -231,6 +244,21 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
         wait_vmcnt<2 * CH * R * NM>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+    }
+    // folded RMSNorm: x <- norm_w * x, and this lane's share of sum x^2 (f64:
+    // no overflow for any f32 row, and the sum is exact to f64 rounding)
+    double ssq = 0.0;
+    if constexpr (NORM_OK) {
+        if (norm) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const float v = xr[k][0][t];
+                    ssq = __builtin_fma((double)v, (double)v, ssq);
+                    xr[k][0][t] = v * gr[k][t];
+                }
+        }
     }
 
     float acc[R][NM][B];
@@ -299,6 +327,12 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[r][m][b] = wave_sum(acc[r][m][b]);
 
+    if constexpr (NORM_OK) {
+        if (norm) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) ssq += __shfl_xor(ssq, off);
+        }
+    }
     // lane l < R*B ends up with the (row l / B, batch row l % B) value
     float v0 = 0.0f, v1 = 0.0f;
     if constexpr (KS > 1) {
@@ -309,6 +343,7 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
                 for (int m = 0; m < NM; ++m)
 #pragma unroll
                     for (int b = 0; b < B; ++b) part[w][r][m][b] = acc[r][m][b];
+            if constexpr (NORM_OK) part_ss[w] = ssq;
         }
         __syncthreads();
         if (ks != 0) return;
@@ -320,6 +355,14 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
                 v1 += part[w + k][r][NM - 1][b];
             }
         }
+        if constexpr (NORM_OK) {
+            if (norm) {
+                double t = 0.0;
+#pragma unroll
+                for (int k = 0; k < KS; ++k) t += part_ss[w + k];
+                ssq = t;
+            }
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -329,6 +372,13 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
                     v0 = acc[r][0][b];
                     v1 = acc[r][NM - 1][b];
                 }
+    }
+    if constexpr (NORM_OK) {
+        if (norm) {
+            const float rs = (float)(1.0 / sqrt(ssq / (double)a.n_in + (double)a.eps));
+            v0 *= rs;
+            v1 *= rs;
+        }
     }
     const int rl = lane / B, bl = lane % B;
     if (lane < R * B && bl < a.batch && row0 + rl < a.total_rows) store_row<MODE>(a, row0 + rl, bl, v0, v1);
@@ -525,8 +575,15 @@ KernelFn pick_general(int bt)
 
 }  // namespace
 
+bool q8_gemv_norm_fusable(const Q8GemvProblem& p)
+{
+    const int64_t nch = p.n_in / 16;
+    return p.batch == 1 && nch % 64 == 0 && b1_shape((int)(nch / 64)).ks > 0;
+}
+
 hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
 {
+    if (p.norm_w && !q8_gemv_norm_fusable(p)) return hipErrorInvalidValue;   // only the one-row shape folds a norm
     Q8GemvArgs a = make_q8_gemv_args(p);
 
     // Batch rounds up to 1, 2, 4 or 8 (padding rows are never stored).

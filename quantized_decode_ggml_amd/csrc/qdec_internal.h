@@ -125,9 +125,20 @@ struct Q8GemvProblem {
     const float* residual;
     int64_t n_in;
     int64_t batch;
+    // Optional RMSNorm of x folded into the product (one batch row on the
+    // fast path only, see q8_gemv_norm_fusable): the kernel computes
+    // r * sum_j W_ij (norm_w_j x_j), r = 1 / sqrt(mean_j x_j^2 + eps).
+    const float* norm_w;
+    float eps;
 };
 
 hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s);
+bool q8_gemv_norm_fusable(const Q8GemvProblem& p);
+
+// RMSNorm of `batch` rows of n floats: out = x / sqrt(mean(x^2) + eps) * w
+// (one workgroup per row; out may be x).
+hipError_t launch_rmsnorm(const float* x, int64_t n, int64_t batch, const float* w, float eps, float* out,
+                          hipStream_t s);
 
 // Matrix-core path for 3..8 batch rows (gemv_q8_0_mfma.hip).  It reads the
 // fragment-tiled copies of the segments and needs a device workspace of

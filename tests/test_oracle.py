@@ -511,3 +511,56 @@ def test_topk_rejects_bad_arguments():
     v[0, 2] = np.nan
     with pytest.raises(ValueError):
         oracle.topk(v, 1)
+
+
+# ---------------------------------------------------------------- RMSNorm --
+# Reading (the pages print no formula): out = x / sqrt(mean(x^2) + eps) * w.
+
+def test_rmsnorm_hand_example():
+    y = oracle.rmsnorm(np.array([[3.0, 4.0]], np.float32), np.array([1.0, 1.0], np.float32), 0.0)
+    rms = (12.5) ** 0.5
+    assert y[0, 0] == pytest.approx(3.0 / rms, rel=1e-15)
+    assert y[0, 1] == pytest.approx(4.0 / rms, rel=1e-15)
+    y = oracle.rmsnorm(np.array([[3.0, 4.0]], np.float32), np.array([2.0, -0.5], np.float32), 0.5)
+    r = 1.0 / (12.5 + 0.5) ** 0.5
+    assert y[0].tolist() == pytest.approx([3.0 * r * 2.0, 4.0 * r * -0.5], rel=1e-15)
+
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(81)
+    w = rng.standard_normal(64).astype(np.float32)
+    for c in (-3.5, 0.25, 1e10):
+        x = np.full((1, 64), c, np.float32)
+        assert oracle.rmsnorm(x, w, 0.0)[0] == pytest.approx(np.sign(c) * w.astype(np.float64), rel=1e-14)
+    assert (oracle.rmsnorm(np.zeros((2, 64), np.float32), w, 1e-5) == 0).all()
+
+
+def test_rmsnorm_unit_mean_square_and_scale_invariance():
+    rng = np.random.default_rng(82)
+    x = rng.standard_normal((3, 1000)).astype(np.float32)
+    ones = np.ones(1000, np.float32)
+    y = oracle.rmsnorm(x, ones, 0.0)
+    assert np.mean(y * y, axis=1) == pytest.approx([1.0, 1.0, 1.0], rel=1e-13)
+    y4 = oracle.rmsnorm(x * np.float32(4.0), ones, 0.0)
+    assert np.allclose(y4, y, rtol=1e-14, atol=0)
+    w = rng.standard_normal(1000).astype(np.float32)
+    assert np.allclose(oracle.rmsnorm(x, w, 1e-3), oracle.rmsnorm(x, ones, 1e-3) * w, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_eps_inside_the_root():
+    x = np.array([[1e-3, -1e-3]], np.float32)
+    y = oracle.rmsnorm(x, np.ones(2, np.float32), 1e-6)
+    r = 1.0 / (float(np.float32(1e-3)) ** 2 + 1e-6) ** 0.5
+    assert y[0, 0] == pytest.approx(float(np.float32(1e-3)) * r, rel=1e-14)
+
+
+def test_gemv_f64_input_matches_f32_path():
+    """For an input that is exactly an f32 vector, the f64-input product equals
+    the C oracle's product (a different summation, so to f64 rounding)."""
+    import synth
+    raw, _ = synth.q8_0_weights(83, 20, 96)
+    x = synth.normal_f32(84, (2, 96))
+    a, sa = oracle.q8_0_gemv(raw, 96, 20, x)
+    b, sb = oracle.q8_0_gemv_f64(raw, 96, 20, x.astype(np.float64))
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+    assert np.allclose(sa, sb, rtol=1e-13, atol=1e-15)

@@ -35,6 +35,9 @@ MUTANTS = {
     "fp16_subnormal_scale": ("ldexpf((float)f, -24)", "ldexpf((float)f, -25)"),
     "topk_ties_larger_index_first": ("return (a->i < b->i) ? -1 : (a->i > b->i);", "return (a->i > b->i) ? -1 : (a->i < b->i);"),
     "topk_smallest_first": ("if (a->v > b->v) return -1;\n    if (a->v < b->v) return 1;", "if (a->v < b->v) return -1;\n    if (a->v > b->v) return 1;"),
+    "rmsnorm_sum_not_mean": ("const double r = 1.0 / sqrt(ss / (double)n + eps);", "const double r = 1.0 / sqrt(ss + eps);"),
+    "rmsnorm_eps_outside_root": ("const double r = 1.0 / sqrt(ss / (double)n + eps);", "const double r = 1.0 / (sqrt(ss / (double)n) + eps);"),
+    "rmsnorm_weight_dropped": ("out[b * n + j] = (double)x[b * n + j] * r * (double)w[j];", "out[b * n + j] = (double)x[b * n + j] * r;"),
     "topk_off_by_one": ("val[b * k + r] = it[r].v;", "val[b * k + r] = it[r + (r + 1 < n)].v;"),
 }
 
