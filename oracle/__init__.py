@@ -52,7 +52,8 @@ def _load():
             lib.oracle_q4k_unpack_scales.argtypes = [P, P, P]
             lib.oracle_q8_0_dequantize.argtypes = [P, I, I, P]
             lib.oracle_q4k_dequantize.argtypes = [P, I, I, P]
-            for name in ("oracle_q8_0_gemv", "oracle_q4k_gemv", "oracle_f32_gemm"):
+            lib.oracle_q6k_dequantize.argtypes = [P, I, I, P]
+            for name in ("oracle_q8_0_gemv", "oracle_q4k_gemv", "oracle_q6k_gemv", "oracle_f32_gemm"):
                 getattr(lib, name).argtypes = [P, I, I, I, P, P, P]
                 getattr(lib, name).restype = ctypes.c_int
             lib.oracle_q8_0_gemv_residual.argtypes = [P, I, I, I, P, P, P, P]
@@ -143,6 +144,19 @@ def q8_0_gemv(w, n_in: int, n_out: int, x):
 
 def q4k_gemv(w, n_in: int, n_out: int, x):
     return _gemv(_load().oracle_q4k_gemv, w, n_in, n_out, x, _u8)
+
+
+def q6k_dequantize(w, n_in: int, n_out: int) -> np.ndarray:
+    """(n_out, n_in) f32 from raw GGML Q6_K bytes (210-byte super-blocks)."""
+    w = _u8(w)
+    assert n_in % 256 == 0 and w.size == n_out * (n_in // 256) * 210
+    out = np.empty((n_out, n_in), np.float32)
+    _load().oracle_q6k_dequantize(_ptr(w), n_in, n_out, _ptr(out))
+    return out
+
+
+def q6k_gemv(w, n_in: int, n_out: int, x):
+    return _gemv(_load().oracle_q6k_gemv, w, n_in, n_out, x, _u8)
 
 
 def f32_gemm(w, n_in: int, n_out: int, x):

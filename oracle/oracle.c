@@ -53,6 +53,8 @@
 #define Q8_0_ELEMS 32
 #define Q4K_BYTES 144
 #define Q4K_ELEMS 256
+#define Q6K_BYTES 210
+#define Q6K_ELEMS 256
 
 /* ---------------------------------------------------------------- fp16 -- */
 
@@ -170,6 +172,38 @@ void oracle_q4k_dequantize(const uint8_t* w, int64_t n_in, int64_t n_out, float*
     }
 }
 
+/* Q6_K ([P3] names Q6_K for the embedding and output tensors; no block layout
+ * is given there or in the workload definitions, so the reading is the public
+ * GGML K-quant layout).  210-byte super-blocks of 256 weights: 128 bytes ql
+ * (the low four bits of the 6-bit quants, two per byte), 64 bytes qh (the high
+ * two bits, four per byte), 16 int8 scales (one per 16 weights), then fp16 d.
+ * Weight e: half h = e / 128, group j = (e % 128) / 32, l = e % 32.  Its low
+ * four bits are the low nibble (j = 0, 1) or the high nibble (j = 2, 3) of
+ * ql[64h + 32(j % 2) + l]; its high two bits are bits 2j, 2j+1 of
+ * qh[32h + l]; its scale is scales[8h + 2j + l / 16]; w = d * sc * (q - 32).
+ * d*sc*(q-32) has at most 11 + 7 + 5 significant bits, so it is exact in f32. */
+void oracle_q6k_dequantize(const uint8_t* w, int64_t n_in, int64_t n_out, float* out)
+{
+    const int64_t nsb = n_in / Q6K_ELEMS;
+    for (int64_t i = 0; i < n_out; ++i) {
+        for (int64_t k = 0; k < nsb; ++k) {
+            const uint8_t* blk = w + (i * nsb + k) * Q6K_BYTES;
+            const uint8_t* ql = blk;
+            const uint8_t* qh = blk + 128;
+            const int8_t* sc = (const int8_t*)(blk + 192);
+            const float d = oracle_fp16_to_f32(load_le16(blk + 208));
+            for (int e = 0; e < Q6K_ELEMS; ++e) {
+                const int h = e / 128, j = (e % 128) / 32, l = e % 32;
+                const uint8_t lo_byte = ql[64 * h + 32 * (j % 2) + l];
+                const int lo = (j < 2) ? (lo_byte & 0x0f) : (lo_byte >> 4);
+                const int hi = (qh[32 * h + l] >> (2 * j)) & 3;
+                const int q = lo | (hi << 4);
+                out[i * n_in + k * Q6K_ELEMS + e] = d * (float)sc[8 * h + 2 * j + l / 16] * (float)(q - 32);
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------ dot products -- */
 
 /* out[b*n_out + i] = sum_j W[i][j] * x[b*n_in + j] in f64, and
@@ -238,6 +272,15 @@ int oracle_q4k_gemv(const uint8_t* w, int64_t n_in, int64_t n_out, int64_t batch
 }
 
 /* Dense f32 weights ([P2] try_cuda_batch_gemv): out[b][i] = sum_j W[i][j] x[b][j]. */
+/* Q6_K dequant-GEMV ([P1] the GEMV family over another GGML block type; the
+ * pages' output and embedding tensors are Q6_K): as oracle_q8_0_gemv. */
+int oracle_q6k_gemv(const uint8_t* w, int64_t n_in, int64_t n_out, int64_t batch,
+                    const float* x, double* out, double* s_abs)
+{
+    return quant_rows_dot(oracle_q6k_dequantize, (n_in / Q6K_ELEMS) * Q6K_BYTES, w, n_in,
+                          n_out, batch, x, out, s_abs);
+}
+
 int oracle_f32_gemm(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
                     const float* x, double* out, double* s_abs)
 {

@@ -76,6 +76,23 @@ def q4k_weights(seed: int, n_out: int, n_in: int, lo: float = 1e-4, hi: float = 
     return blk.reshape(-1)
 
 
+Q6K_BLOCK_BYTES, Q6K_BLOCK_ELEMS = 210, 256
+
+
+def q6k_weights(seed: int, n_out: int, n_in: int, lo: float = 1e-4, hi: float = 1e-3) -> np.ndarray:
+    """Random GGML Q6_K bytes (uint8, flat), row-major n_out x n_in: random
+    quant bytes, int8 scales in [-64, 63], fp16 d in [lo, hi]."""
+    assert n_in % Q6K_BLOCK_ELEMS == 0
+    nsb = n_in // Q6K_BLOCK_ELEMS
+    rng = np.random.default_rng(seed)
+    blk = np.empty((n_out, nsb, Q6K_BLOCK_BYTES), np.uint8)
+    blk[:, :, 0:192] = rng.integers(0, 256, (n_out, nsb, 192), dtype=np.uint8)
+    blk[:, :, 192:208] = rng.integers(-64, 64, (n_out, nsb, 16)).astype(np.int8).view(np.uint8)
+    d = rng.uniform(lo, hi, (n_out, nsb)).astype(np.float16)
+    blk[:, :, 208:210] = d.view(np.uint8).reshape(n_out, nsb, 2)
+    return blk.reshape(-1)
+
+
 def fnv1a64(raw: bytes | np.ndarray, n_in: int, n_out: int) -> int:
     """Content fingerprint for run logs: FNV-1a over the bytes, then n_in and
     n_out each folded in as a whole 64-bit word (the pages' weight_fingerprint

@@ -564,3 +564,89 @@ def test_gemv_f64_input_matches_f32_path():
     b, sb = oracle.q8_0_gemv_f64(raw, 96, 20, x.astype(np.float64))
     assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
     assert np.allclose(sa, sb, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------- Q6_K --
+# Layout reading (not on the pages): see tests/golden/q6k_blocks.json.
+
+def _q6k_block_from_fixture(b):
+    blk = np.zeros(210, np.uint8)
+    for k, v in b["ql"].items():
+        blk[int(k)] = v
+    for k, v in b["qh"].items():
+        blk[128 + int(k)] = v
+    blk[192:208] = np.array(b["scales"], np.int8).view(np.uint8)
+    blk[208:210] = np.frombuffer(bytes.fromhex(b["d_hex"]), np.uint8)
+    return blk
+
+
+def test_q6k_golden_blocks(golden_dir):
+    import json
+    import os
+    with open(os.path.join(golden_dir, "q6k_blocks.json")) as f:
+        fx = json.load(f)
+    for b in fx["blocks"]:
+        w = oracle.q6k_dequantize(_q6k_block_from_fixture(b), 256, 1)[0]
+        for e, v in b["expect"].items():
+            assert w[int(e)] == v, f"{b['name']} weight {e}: {w[int(e)]} != {v}"
+
+
+def _q6k_pack(q, sc, d16):
+    """Independent encoder, written per (h, l) byte rather than per weight:
+    q (256,) ints 0..63, sc (16,) ints, d16 (uint16 bits) -> 210 bytes."""
+    blk = np.zeros(210, np.uint8)
+    for h in range(2):
+        for l in range(32):
+            base = 128 * h + l
+            q0, q1, q2, q3 = (int(q[base + 32 * g]) for g in range(4))
+            blk[64 * h + l] = (q0 & 15) | ((q2 & 15) << 4)
+            blk[64 * h + 32 + l] = (q1 & 15) | ((q3 & 15) << 4)
+            blk[128 + 32 * h + l] = (q0 >> 4) | ((q1 >> 4) << 2) | ((q2 >> 4) << 4) | ((q3 >> 4) << 6)
+    blk[192:208] = np.asarray(sc, np.int8).view(np.uint8)
+    blk[208:210] = np.array([d16], np.uint16).view(np.uint8)
+    return blk
+
+
+def test_q6k_encoder_round_trip():
+    rng = np.random.default_rng(91)
+    for _ in range(20):
+        q = rng.integers(0, 64, 256)
+        sc = rng.integers(-128, 128, 16)
+        d = np.float16(rng.uniform(1e-3, 2.0))
+        blk = _q6k_pack(q, sc, int(d.view(np.uint16)))
+        w = oracle.q6k_dequantize(blk, 256, 1)[0].astype(np.float64)
+        e = np.arange(256)
+        group = 8 * (e // 128) + 2 * ((e % 128) // 32) + (e % 32) // 16
+        ref = float(d) * sc[group] * (q - 32)
+        assert np.array_equal(w, ref)          # exact: at most 23 significant bits
+
+
+def test_q6k_super_block_addressing_and_zero_scale():
+    rng = np.random.default_rng(92)
+    rows = []
+    for i in range(2):
+        row = []
+        for k in range(2):
+            d = np.float16(0.5 * (1 + i) + 0.25 * k)
+            row.append(_q6k_pack(np.full(256, 40), np.ones(16, int), int(d.view(np.uint16))))
+        rows.append(np.concatenate(row))
+    w = oracle.q6k_dequantize(np.concatenate(rows), 512, 2)
+    for i in range(2):
+        for k in range(2):
+            assert (w[i, 256 * k:256 * (k + 1)] == float(np.float16(0.5 * (1 + i) + 0.25 * k)) * 8).all()
+    blk = _q6k_pack(rng.integers(0, 64, 256), rng.integers(-128, 128, 16), 0)
+    assert (oracle.q6k_dequantize(blk, 256, 1) == 0).all()
+
+
+@pytest.mark.parametrize("n_out,n_in,batch", [(2, 256, 1), (3, 512, 2)])
+def test_q6k_gemv_exact_rational(n_out, n_in, batch):
+    import synth
+    raw = synth.q6k_weights(93 + n_out, n_out, n_in)
+    x = synth.normal_f32(94 + batch, (batch, n_in))
+    out, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+    W = oracle.q6k_dequantize(raw, n_in, n_out)
+    for b in range(batch):
+        for i in range(n_out):
+            ex = exact_dot(W[i], x[b])
+            assert out[b, i] == pytest.approx(float(ex), rel=1e-12, abs=1e-15)
+            assert S[b, i] == pytest.approx(float(sum(abs(Fraction(float(a)) * Fraction(float(c))) for a, c in zip(W[i], x[b]))), rel=1e-12)

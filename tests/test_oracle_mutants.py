@@ -35,6 +35,10 @@ MUTANTS = {
     "fp16_subnormal_scale": ("ldexpf((float)f, -24)", "ldexpf((float)f, -25)"),
     "topk_ties_larger_index_first": ("return (a->i < b->i) ? -1 : (a->i > b->i);", "return (a->i > b->i) ? -1 : (a->i < b->i);"),
     "topk_smallest_first": ("if (a->v > b->v) return -1;\n    if (a->v < b->v) return 1;", "if (a->v < b->v) return -1;\n    if (a->v > b->v) return 1;"),
+    "q6k_high_bits_shift": ("const int hi = (qh[32 * h + l] >> (2 * j)) & 3;", "const int hi = (qh[32 * h + l] >> j) & 3;"),
+    "q6k_scale_index": ("(float)sc[8 * h + 2 * j + l / 16]", "(float)sc[8 * h + 2 * j]"),
+    "q6k_no_offset": ("* (float)(q - 32);", "* (float)q;"),
+    "q6k_ql_halves_swapped": ("ql[64 * h + 32 * (j % 2) + l]", "ql[64 * h + 32 * (j / 2) + l]"),
     "rmsnorm_sum_not_mean": ("const double r = 1.0 / sqrt(ss / (double)n + eps);", "const double r = 1.0 / sqrt(ss + eps);"),
     "rmsnorm_eps_outside_root": ("const double r = 1.0 / sqrt(ss / (double)n + eps);", "const double r = 1.0 / (sqrt(ss / (double)n) + eps);"),
     "rmsnorm_weight_dropped": ("out[b * n + j] = (double)x[b * n + j] * r * (double)w[j];", "out[b * n + j] = (double)x[b * n + j] * r;"),
