@@ -268,6 +268,19 @@ def suite(args):
         timed(f"c4 q4k_gemv {n_out}x{n_in} b1", [lambda w=w: qd.q4k_gemv(w, n_in, n_out, x4, out=o4) for w in ws],
               nb4 + n_in * 4 + n_out * 4)
         del ws, raw
+    # Q6_K (next-row f3): the FFN shapes and the output-projection shape
+    for n_out, n_in in ((8192, 3072), (3072, 8192), (128256, 3072)):
+        raw = torch.from_numpy(synth.q6k_weights(synth.seed(6, n_out % 97), n_out, n_in)).to(dev)
+        nb6 = n_out * (n_in // 256) * 210
+        ws = []
+        for _ in range(copies_for(nb6)):
+            c = raw.clone()
+            qd.prepare(c, qd.TYPE_Q6_K, n_in, n_out)
+            ws.append(c)
+        x6, o6 = xdev(synth.seed(6, 50), (1, n_in)), torch.empty((1, n_out), device=dev)
+        timed(f"f3 q6k_gemv {n_out}x{n_in} b1", [lambda w=w: qd.q6k_gemv(w, n_in, n_out, x6, out=o6) for w in ws],
+              nb6 + n_in * 4 + n_out * 4, iters=40 if n_out > 100000 else 100)
+        del ws, raw
     wvoc = q8_dev(4, 3, 128256, 3072, 2)
     xv, ov = xdev(synth.seed(4, 4), (1, 3072)), torch.empty((1, 128256), device=dev)
     timed("c4 q8_0_gemv vocab 128256x3072 b1", [lambda w=w: qd.q8_0_gemv(w, 3072, 128256, xv, out=ov) for w in wvoc],

@@ -16,6 +16,12 @@
  *         eight 6-bit scales and eight 6-bit mins (GGML K-quant packing), 128
  *         bytes of nibbles (low nibbles of each 64-element chunk p = sub-block
  *         2p, high nibbles = sub-block 2p+1); w = d*sc*q - dmin*m.
+ *   Q6_K: named by [QTensorEngine] (embedding and output tensors) without a
+ *         layout; the public GGML K-quant layout is used: 210-byte super-blocks
+ *         of 256 weights = ql[128] (low 4 bits), qh[64] (high 2 bits), int8
+ *         scales[16], fp16 d; weight 128h + 32j + l takes the low (j < 2) or
+ *         high nibble of ql[64h + 32(j%2) + l], bits 2j..2j+1 of qh[32h + l]
+ *         and scales[8h + 2j + l/16]; w = d*scale*(q - 32).
  *
  * Conventions for every call below
  *   - Weights are GGML raw block bytes in DEVICE memory, row-major: row i of an
@@ -80,7 +86,7 @@ typedef enum {
 } qdec_status;
 
 /* GGML type ids. */
-typedef enum { QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12 } qdec_type;
+typedef enum { QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12, QDEC_TYPE_Q6_K = 14 } qdec_type;
 
 /* Largest batch accepted by the GEMV-shaped calls (decode).  The batched GEMM
  * calls take any batch >= 1. */
@@ -183,6 +189,13 @@ QDEC_API int q8_0_attn_out_ffn(const void* wo, const void* w_gate, const void* w
 QDEC_API int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
              const float* x, float* out, hipStream_t stream);
 
+/* Q6_K dequant-GEMV (the GEMV family of [cuda_lane] over the Q6_K blocks
+ * that [QTensorEngine] uses for the output and embedding tensors): as
+ * q8_0_gemv over Q6_K weights; n_in % 256 == 0, 1 <= batch <= 8.  Products
+ * are exact (each weight is an integer times an exact scale), f32 sums. */
+QDEC_API int q6k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
+             const float* x, float* out, hipStream_t stream);
+
 /* Batched prefill-shaped GEMM over Q8_0 weights ([weight_cache]
  * try_cuda_batch_gemv: C[m x n] = A[m x k] B[k x n] with m = batch,
  * k = n_in, n = n_out, B = W transposed).  Dequantised weight tiles and x
@@ -201,7 +214,7 @@ QDEC_API int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64
 
 /* -------------------------------------------------------- repack cache -- */
 
-/* Repack w now (load time, not timed), type QDEC_TYPE_Q8_0 or QDEC_TYPE_Q4_K
+/* Repack w now (load time, not timed), type QDEC_TYPE_Q8_0, QDEC_TYPE_Q4_K or QDEC_TYPE_Q6_K
  * ([cuda_lane] preload_q4k_soa_weights), and wait on the host until the copy
  * is complete.  Idempotent. */
 QDEC_API int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream);
@@ -224,6 +237,8 @@ QDEC_API int64_t qdec_cache_len(void);
  * products are exact in f32; Q4_K rounds once, in the final subtraction. */
 QDEC_API int q8_0_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream);
 QDEC_API int q4k_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream);
+/* Q6_K: d*scale*(q - 32) has at most 23 significant bits, exact in f32. */
+QDEC_API int q6k_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream);
 
 /* ---------------------------------------------------------- diagnostics -- */
 

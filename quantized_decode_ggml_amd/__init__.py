@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libqdec.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qdec.h")
 
 QDEC_OK, QDEC_EINVAL, QDEC_ENOMEM, QDEC_EHIP, QDEC_EUNSUPPORTED = 0, -1, -2, -3, -4
-TYPE_Q8_0, TYPE_Q4_K = 8, 12
+TYPE_Q8_0, TYPE_Q4_K, TYPE_Q6_K = 8, 12, 14
 GEMV_MAX_BATCH = 8
 TOPK_MAX = 256
 
@@ -39,6 +39,8 @@ _SIGS = {
     "q8_0_qkv": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P],
     "q8_0_swiglu": [_P, _P, _I, _I, _I, _P, _P, _P],
     "q4k_gemv": [_P, _I, _I, _I, _P, _P, _P],
+    "q6k_gemv": [_P, _I, _I, _I, _P, _P, _P],
+    "q6k_dequantize": [_P, _I, _I, _P, _P],
     "q8_0_gemv_topk": [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P],
     "qdec_rmsnorm": [_P, _I, _I, _P, ctypes.c_float, _P, _P],
     "q8_0_rmsnorm_qkv": [_P, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P],
@@ -238,6 +240,14 @@ def q4k_gemv(w, n_in, n_out, x, out=None, stream=None):
     return out
 
 
+def q6k_gemv(w, n_in, n_out, x, out=None, stream=None):
+    batch = _batch(x, n_in)
+    out = _f32_out(out, batch, n_out, x)
+    _check(lib.q6k_gemv(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
+    _track(w)
+    return out
+
+
 def q8_0_gemm_batched(w, n_in, n_out, x, out=None, stream=None):
     batch = _batch(x, n_in)
     out = _f32_out(out, batch, n_out, x)
@@ -289,6 +299,14 @@ def q4k_dequantize(w, n_in, n_out, out=None, stream=None):
     if out is None:
         out = torch.empty((n_out, n_in), dtype=torch.float32, device=w.device)
     _check(lib.q4k_dequantize(_ptr(w), n_in, n_out, _ptr(out), _stream(stream)))
+    _track(w)
+    return out
+
+
+def q6k_dequantize(w, n_in, n_out, out=None, stream=None):
+    if out is None:
+        out = torch.empty((n_out, n_in), dtype=torch.float32, device=w.device)
+    _check(lib.q6k_dequantize(_ptr(w), n_in, n_out, _ptr(out), _stream(stream)))
     _track(w)
     return out
 

@@ -84,6 +84,7 @@ int64_t copy_bytes(int type, int64_t n_in, int64_t n_out)
 {
     return type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out)
          : type == kTypeQ8_0Tiled ? q8t_plane_bytes(n_in, n_out)
+         : type == QDEC_TYPE_Q6_K ? q6k_plane_bytes(n_in, n_out)
                                   : q4k_plane_bytes(n_in, n_out);
 }
 
@@ -92,6 +93,7 @@ hipError_t launch_copy_of(int type, const void* w, int64_t n_in, int64_t n_out, 
     const uint8_t* raw = static_cast<const uint8_t*>(w);
     return type == QDEC_TYPE_Q8_0 ? launch_repack_q8_0(raw, n_in, n_out, dst, s)
          : type == kTypeQ8_0Tiled ? launch_repack_q8_0_tiled(raw, n_in, n_out, dst, s)
+         : type == QDEC_TYPE_Q6_K ? launch_repack_q6k(raw, n_in, n_out, dst, s)
                                   : launch_repack_q4k(raw, n_in, n_out, dst, s);
 }
 
@@ -512,6 +514,20 @@ int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const fl
     return finish(launch_q4k_gemv(q4k_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
 }
 
+int q6k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
+             hipStream_t stream)
+{
+    const char* fn = "q6k_gemv";
+    QDEC_TRY(check_dims(fn, n_in, n_out, batch, 256, QDEC_GEMV_MAX_BATCH));
+    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    QDEC_TRY(check_ptr(fn, "x", x, 16));
+    QDEC_TRY(check_ptr(fn, "out", out, 4));
+    if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4)) return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
+    const void* buf = nullptr;
+    QDEC_TRY(repacked(w, QDEC_TYPE_Q6_K, n_in, n_out, stream, &buf));
+    return finish(launch_q6k_gemv(q6k_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
+}
+
 int q8_0_gemm_batched(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                       float* out, hipStream_t stream)
 {
@@ -543,7 +559,8 @@ int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
 int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream)
 {
     const char* fn = "qdec_prepare";
-    if (type != QDEC_TYPE_Q8_0 && type != QDEC_TYPE_Q4_K) return fail(QDEC_EINVAL, "%s: unknown type %d", fn, type);
+    if (type != QDEC_TYPE_Q8_0 && type != QDEC_TYPE_Q4_K && type != QDEC_TYPE_Q6_K)
+        return fail(QDEC_EINVAL, "%s: unknown type %d", fn, type);
     QDEC_TRY(check_dims(fn, n_in, n_out, 1, type == QDEC_TYPE_Q8_0 ? 32 : 256, 0));
     QDEC_TRY(check_ptr(fn, "weight", w, 2));
     const void* buf = nullptr;
@@ -630,6 +647,17 @@ int q4k_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipSt
 const char* qdec_last_error(void) { return t_error.c_str(); }
 
 uint64_t qdec_launch_count(void) { return g_launches.load(std::memory_order_relaxed); }
+
+int q6k_dequantize(const void* w, int64_t n_in, int64_t n_out, float* out, hipStream_t stream)
+{
+    const char* fn = "q6k_dequantize";
+    QDEC_TRY(check_dims(fn, n_in, n_out, 1, 256, 0));
+    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    QDEC_TRY(check_ptr(fn, "out", out, 16));
+    const void* buf = nullptr;
+    QDEC_TRY(repacked(w, QDEC_TYPE_Q6_K, n_in, n_out, stream, &buf));
+    return finish(launch_dequant_q6k(q6k_view(buf, n_in, n_out), n_in, n_out, out, stream), fn);
+}
 
 int qdec_empty_kernel(hipStream_t stream) { return finish(launch_empty(stream), "qdec_empty_kernel"); }
 

@@ -47,6 +47,21 @@ struct Q4KView {
     const uint32_t* sm;
 };
 
+// Q6_K copy (256-weight super-blocks; GGML block: ql[128] low nibbles,
+// qh[64] high bit pairs, int8 scales[16], fp16 d):
+//   q plane : per super-block 16 chunks of 12 bytes; chunk 8h + m holds the
+//             three GGML words ql[64h + 4m ..+3], ql[64h + 32 + 4m ..+3] and
+//             qh[32h + 4m ..+3], i.e. the bits of the 16 weights
+//             128h + 32j + 4m + t (j, t = 0..3); 192 bytes per super-block.
+//   h plane : per super-block two 12-byte half headers: scales[8h ..8h+7],
+//             fp16 d, two zero bytes.
+//   (216 bytes per 256 weights instead of 210: one lane's 16 weights are one
+//   contiguous 12-byte load and its scales and d one 12-byte load.)
+struct Q6KView {
+    const uint8_t* q;
+    const uint8_t* h;
+};
+
 constexpr int64_t kAlign = 256;
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -79,6 +94,19 @@ inline Q8TView q8t_view(const void* base, int64_t n_in, int64_t n_out)
                    reinterpret_cast<const uint16_t*>(p + align_up(tiles * 512, kAlign))};
 }
 
+inline int64_t q6k_plane_bytes(int64_t n_in, int64_t n_out)
+{
+    const int64_t nsb = n_out * (n_in / 256);
+    return align_up(nsb * 192, kAlign) + align_up(nsb * 24, kAlign);
+}
+
+inline Q6KView q6k_view(const void* base, int64_t n_in, int64_t n_out)
+{
+    const char* p = static_cast<const char*>(base);
+    const int64_t nsb = n_out * (n_in / 256);
+    return Q6KView{reinterpret_cast<const uint8_t*>(p), reinterpret_cast<const uint8_t*>(p + align_up(nsb * 192, kAlign))};
+}
+
 // Cache type of the tiled copy (internal; the public types are the GGML ids).
 constexpr int kTypeQ8_0Tiled = 0x108;
 
@@ -108,6 +136,10 @@ hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, vo
                              hipStream_t s);
 hipError_t launch_repack_q8_0_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
                                     hipStream_t s);
+hipError_t launch_repack_q6k(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s);
+hipError_t launch_dequant_q6k(Q6KView w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
+hipError_t launch_q6k_gemv(Q6KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
+                           hipStream_t s);
 hipError_t launch_dequant_q8_0(Q8View w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
 hipError_t launch_dequant_q4k(Q4KView w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
 

@@ -49,6 +49,10 @@ def test_initial_state():
     lambda L: L.q8_0_dequantize(FAKE, 64, 8, FAKE * 2 + 4, None),         # out not 16-aligned
     lambda L: L.qdec_copy(FAKE, FAKE * 2, 24, None),                      # bytes % 16
     lambda L: L.qdec_release(None),
+    lambda L: L.q6k_gemv(FAKE, 128, 8, 1, FAKE, FAKE * 2, None),           # Q6_K needs n_in % 256
+    lambda L: L.q6k_gemv(FAKE, 256, 8, 9, FAKE, FAKE * 2, None),           # batch > 8
+    lambda L: L.qdec_prepare(FAKE, 14, 64, 8, None),                      # Q6_K needs n_in % 256
+    lambda L: L.q6k_dequantize(FAKE, 256, 8, FAKE * 2 + 4, None),         # out not 16-aligned
     lambda L: L.q8_0_gemv_topk(FAKE, 64, 16, 1, FAKE, 0, FAKE * 2, FAKE * 3, FAKE * 4, None),    # k = 0
     lambda L: L.q8_0_gemv_topk(FAKE, 64, 16, 1, FAKE, 17, FAKE * 2, FAKE * 3, FAKE * 4, None),   # k > n_out
     lambda L: L.q8_0_gemv_topk(FAKE, 64, 400, 1, FAKE, 257, FAKE * 2, FAKE * 3, FAKE * 4, None), # k > 256
