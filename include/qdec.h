@@ -46,13 +46,16 @@
  *     (QDEC_EINVAL): call qdec_prepare, which returns once the copy is
  *     complete, for every weight before capturing.
  *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in of
- *     1024..8192 in the supported steps) splits x, and q8_0_gemv_topk keeps
- *     its candidate lists, in a library-owned device buffer, one per
+ *     1024..8192 in the supported steps) splits x, q8_0_gemv_topk keeps its
+ *     candidate lists, and q8_0_gemm_batched (at >= 256 output tiles of
+ *     128 x 128, n_in % 64 == 0, n_out % 8 == 0) rounds x to bf16, in a
+ *     library-owned device buffer, one per
  *     (device, stream), made (or grown) on the first such call on that stream
  *     and freed by qdec_clear_cache.  Calls on one stream share it in
  *     stream order; calls on different streams never share one.  A stream
  *     capture cannot allocate it, so a capture on a stream that has none takes
- *     the VALU kernels (same results to the f32 tolerance).
+ *     the VALU kernels (same results to the f32 tolerance), or for the GEMM the
+ *     register-staged kernel (same arithmetic).
  *   - Return value: QDEC_OK (0) or a negative qdec_status.  Invalid arguments
  *     are rejected with QDEC_EINVAL before any HIP call; a failed allocation
  *     returns QDEC_ENOMEM; a failed launch or HIP call returns QDEC_EHIP.

@@ -227,6 +227,263 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
     }
 }
 
+// ----------------------------------------------------------- pipelined --
+// Q8_0 GEMM for grids that fill the chip without K splits (>= 256 tiles of
+// 128 x 128, K % 64 == 0, n_out % 8 == 0).  The register-staged kernel above
+// waits a full memory latency every 64 k (one K step of prefetch); here every
+// operand streams global->LDS by DMA (global_load_lds, 16 bytes a lane) into a
+// ring of P = 4 super-stages of 64 k, so three super-stages are in flight
+// while one is consumed:
+//   x  : bf16 rows (rounded once into the workspace by x_to_bf16), 128 bytes
+//        of a row per 8 lanes, chunk c of row r stored at c ^ (r & 7) against
+//        LDS bank conflicts;
+//   W  : raw int8 rows, 64 bytes each;
+//   d  : the block-major scale plane, one 16-byte load per lane covering two
+//        blocks x 128 rows.
+// Each 32-k compute stage dequantises its W half-tile from LDS into one of
+// three bf16 buffers (two stages ahead of the MFMAs that read it), loads the
+// A and B fragments of the next stage while the current stage's MFMAs run,
+// and ends with one barrier.  The scheduling fences interleave LDS reads,
+// MFMAs and the dequantisation VALU work; all waits on the DMA counter are
+// explicit (vmcnt counts whole super-stages of PER instructions).
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline void dma16(const void* g, lds_void* l) { __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0); }
+
+template <int N>
+__device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+struct PipeArgs {
+    const __bf16* xb;      // M x K bf16 (workspace)
+    const int8_t* q;       // N x K
+    const uint16_t* dT;    // (K/32) x N
+    float* out;            // M x N
+    int64_t M, N, K, ntiles;
+    int64_t kslice;        // K per split (multiple of 64)
+    int splits;            // > 1: partial tiles are added into a zeroed out
+};
+
+__global__ __launch_bounds__(256) void x_to_bf16(const float4* __restrict__ x, bf16x4* __restrict__ xb, int64_t n4)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) xb[i] = to_bf16x4(x[i]);
+}
+
+constexpr int kPipeStages = 4;
+
+#define QDEC_RING(name, type, n)                                                                        \
+    __shared__ __attribute__((aligned(1024))) type name##0[n], name##1[n], name##2[n], name##3[n]
+#define QDEC_PICK(name, u) ((u) == 0 ? name##0 : (u) == 1 ? name##1 : (u) == 2 ? name##2 : name##3)
+
+__global__ __launch_bounds__(256) void gemm_q8_pipe(PipeArgs a)
+{
+    constexpr int PBM = 128, PBN = 128, P = kPipeStages;
+    constexpr int WGN = 2, NWAVE = 4, TM = 4, TN = 4;          // 2 x 2 waves of 64 x 64
+    constexpr int XI = PBM * 128 / 1024, XPW = XI / NWAVE;    // x: 8 rows x 128 B per instruction
+    constexpr int WI = PBN * 64 / 1024, WPW = WI / NWAVE;     // W: 16 rows x 64 B per instruction
+    constexpr int PER = XPW + WPW + 1;                         // DMA instructions per super-stage and wave
+    static_assert(XI % NWAVE == 0 && WI % NWAVE == 0 && PBN * 4 <= 1024, "tile split");
+    QDEC_RING(XR, __bf16, PBM * 64);
+    QDEC_RING(WR, int8_t, PBN * 64);
+    QDEC_RING(DR, uint16_t, 512);
+    __shared__ __attribute__((aligned(1024))) __bf16 WB0[PBN * 32], WB1[PBN * 32], WB2[PBN * 32];
+
+    // block id -> (k slice, n tile, m tile), k fastest
+    const int64_t id = blockIdx.x;
+    const int64_t slice = id % a.splits, tile = id / a.splits;
+    const int64_t n0 = (tile % a.ntiles) * PBN, m0 = (tile / a.ntiles) * PBM;
+    const int64_t kbeg = slice * a.kslice;
+    const int64_t klen = kbeg + a.kslice < a.K ? a.kslice : a.K - kbeg;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int nk = (int)(klen >> 5);  // 32-k compute stages of this slice
+    const int ns = nk >> 1;           // 64-k super-stages
+
+    // x rows: instruction i of this wave covers tile rows 8(wave*XPW + i) ..+7;
+    // lane -> row + lane/8, its 16 bytes land at LDS chunk lane%8, which holds
+    // global chunk (lane%8) ^ (row & 7)
+    const __bf16* xsrc[XPW];
+#pragma unroll
+    for (int i = 0; i < XPW; ++i) {
+        const int r = 8 * (wave * XPW + i) + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        int64_t gr = m0 + r;
+        gr = gr < a.M ? gr : a.M - 1;                          // edge rows repeat the last row
+        xsrc[i] = a.xb + gr * a.K + kbeg + c * 8;
+    }
+    int wi[WPW];
+    const int8_t* wsrc[WPW];
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+        wi[i] = wave * WPW + i;
+        const int r = wi[i] * 16 + (lane >> 2);
+        int64_t gn = n0 + r;
+        gn = gn < a.N ? gn : a.N - 1;
+        wsrc[i] = a.q + gn * a.K + kbeg + (lane & 3) * 16;
+    }
+    // scales: lane l < 32 loads 8 rows of block 2s + l/16 (rows 8(l%16)..); lanes
+    // 32..63 repeat the load into the unused upper half of the slot
+    const int dl = lane & 31;
+    const int dblk = dl >> 4, drow = (dl & 15) * 8;
+    int64_t gdr = n0 + drow;
+    gdr = gdr + 8 <= a.N ? gdr : a.N - 8;                     // n_out % 8 == 0: only whole groups past the edge
+    const uint16_t* dsrc = a.dT + (kbeg / 32 + dblk) * a.N + gdr;
+
+    auto issue = [&](int st, int slot) {
+        const int sc = st < ns ? st : ns - 1;                  // past the end: reload the last super-stage
+        __bf16* xd = QDEC_PICK(XR, slot);
+        int8_t* wd = QDEC_PICK(WR, slot);
+        uint16_t* dd = QDEC_PICK(DR, slot);
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) dma16(xsrc[i] + (int64_t)sc * 64, (lds_void*)(xd + (wave * XPW + i) * 512));
+#pragma unroll
+        for (int i = 0; i < WPW; ++i) dma16(wsrc[i] + (int64_t)sc * 64, (lds_void*)(wd + wi[i] * 1024));
+        dma16(dsrc + (int64_t)(2 * sc) * a.N, (lds_void*)dd);
+    };
+    auto wbuf = [&](int k) -> __bf16* { return k == 0 ? WB0 : k == 1 ? WB1 : WB2; };
+    // dequantisation: thread t takes row t/2 and 16 weights (half t%2) of the
+    // 32-k half of the super-stage
+    const int wr = threadIdx.x >> 1, wh = threadIdx.x & 1;
+    auto dequant = [&](int t, int slot, int wbk) {
+        __bf16* wb = wbuf(wbk);
+        const int h2 = t & 1;
+        const uint4 qv = *reinterpret_cast<const uint4*>(QDEC_PICK(WR, slot) + wr * 64 + h2 * 32 + wh * 16);
+        const float dd = fp16_bits_to_f32(QDEC_PICK(DR, slot)[h2 * PBN + wr]);
+        const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (__bf16)(dd * (float)(int8_t)((w[2 * h + (e >> 2)] >> (8 * (e & 3))) & 0xff));
+            const int c = (wh * 2 + h) ^ ((wr >> 1) & 3);
+            *reinterpret_cast<bf16x8*>(&wb[wr * 32 + c * 8]) = v;
+        }
+    };
+    bf16x8 fa[2][TM], fb[2][TN];
+    auto frags = [&](int t, int slot, int wbk, int f) {
+        const __bf16* xs = QDEC_PICK(XR, slot);
+        const __bf16* wb = wbuf(wbk);
+        const int h2 = t & 1;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = (wm * TM + i) * 16 + (lane & 15);
+            const int c = (h2 * 4 + (lane >> 4)) ^ (r & 7);
+            fa[f][i] = *reinterpret_cast<const bf16x8*>(&xs[r * 64 + c * 8]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int r = (wn * TN + j) * 16 + (lane & 15);
+            const int c = (lane >> 4) ^ ((r >> 1) & 3);
+            fb[f][j] = *reinterpret_cast<const bf16x8*>(&wb[r * 32 + c * 8]);
+        }
+    };
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: super-stages 0..P-2 in flight; 0 and 1 landed
+#pragma unroll
+    for (int st = 0; st < P - 1; ++st) issue(st, st);
+    wait_vm<PER * (P - 3)>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    dequant(0, 0, 0);
+    dequant(1, 0, 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the bf16 tiles are written
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(0, 0, 0, 0);
+    // compute stage t (u = t mod 24, so every ring index is a compile-time constant)
+    auto body = [&](const int t, const int u) {
+        if ((u & 1) == 0) issue(t / 2 + P - 1, (u / 2 + P - 1) % P);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[u & 1][i], fb[u & 1][j], acc[i][j], 0, 0, 0);
+        dequant(t + 2, ((u + 2) / 2) % P, (u + 2) % 3);
+        frags(t + 1, ((u + 1) / 2) % P, (u + 1) % 3, (u + 1) & 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // LDS reads of the dequantisation
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // fragment reads
+#pragma unroll
+        for (int k = 0; k < TM * TN - 2; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);    // VALU between MFMAs
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);        // LDS writes
+        // end of stage t: super-stage (t+3)/2 must have landed
+        if ((u & 1) == 0) wait_vm<PER * (P - 2)>();
+        else wait_vm<PER * (P - 3)>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int t0 = 0;
+    for (; t0 + 24 <= nk; t0 += 24) {
+#pragma unroll
+        for (int u = 0; u < 24; ++u) body(t0 + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < 24; ++u)
+        if (t0 + u < nk) body(t0 + u, u);
+    wait_vm<0>();   // no DMA may still be writing LDS when the workgroup ends
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t n = n0 + (wn * TN + j) * 16 + (lane & 15);
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + e;
+                if (m >= a.M) continue;
+                if (a.splits == 1) a.out[m * a.N + n] = acc[i][j][e];
+                else unsafeAtomicAdd(a.out + m * a.N + n, acc[i][j][e]);
+            }
+        }
+    }
+}
+
+#undef QDEC_RING
+#undef QDEC_PICK
+
+// The pipelined kernel holds 124 KB of LDS, so one workgroup per CU: its grid
+// should be whole rounds of 256 workgroups.  K splits (<= 4, slices >= 512
+// deep and multiples of 64) bring small grids up to 256, but each split adds
+// M*N f32 atomics (4M cost ~12 us), so the split grid is taken only up to 4M
+// atomics.  Measured: 128x8192x3072 split 4: 32.0 us (36.1 unpipelined);
+// 512x8192x3072: 52.7 us (74.5); 512x3072x8192 split 4 (6.3M atomics, 1.5
+// rounds): 84 us against 70.5 unpipelined, so not taken.
+int pipe_splits(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    int s = 1;
+    while (s < 4 && tiles * s < 256 && K % (64 * 2 * s) == 0 && K / (2 * s) >= 512) s *= 2;
+    return s;
+}
+
+bool pipe_ok(int64_t M, int64_t N, int64_t K)
+{
+    if (K % 64 != 0 || N % 8 != 0 || N < 128) return false;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int s = pipe_splits(M, N, K);
+    const int64_t wg = tiles * s;
+    const int64_t rounds = (wg + 255) / 256;
+    const bool full = wg >= 256 && 4 * wg >= 3 * rounds * 256;     // >= 75% of the last round busy
+    return full && (s == 1 || M * N * s <= (int64_t)1 << 22);
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, int64_t n4, float* __restrict__ tail,
                                                    int64_t ntail)
 {
@@ -277,9 +534,46 @@ hipError_t launch(GemmArgs& a, bool quant, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
-                            float* out, hipStream_t s)
+int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
 {
+    return pipe_ok(batch, n_out, n_in) ? batch * n_in * 2 : 0;
+}
+
+hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
+                            float* out, void* workspace, hipStream_t s)
+{
+    if (workspace && pipe_ok(batch, n_out, n_in)) {
+        const int64_t n4 = batch * n_in / 4;   // n_in % 64 == 0
+        int64_t blocks = (n4 + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        hipLaunchKernelGGL(x_to_bf16, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(x),
+                           static_cast<bf16x4*>(workspace), n4);
+        count_launch();
+        PipeArgs p{};
+        p.xb = static_cast<const __bf16*>(workspace);
+        p.q = w.q;
+        p.dT = w.dT;
+        p.out = out;
+        p.M = batch;
+        p.N = n_out;
+        p.K = n_in;
+        p.ntiles = (n_out + 127) / 128;
+        p.splits = pipe_splits(batch, n_out, n_in);
+        p.kslice = n_in / p.splits;
+        if (p.splits > 1) {
+            const int64_t n = batch * n_out, q4 = n / 4;
+            int64_t zb = (q4 + 255) / 256;
+            if (zb > 2048) zb = 2048;
+            if (zb < 1) zb = 1;
+            hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, s, reinterpret_cast<float4*>(out), q4,
+                               out + q4 * 4, n - q4 * 4);
+            count_launch();
+        }
+        const int64_t grid = ((batch + 127) / 128) * p.ntiles * p.splits;
+        hipLaunchKernelGGL(gemm_q8_pipe, dim3((unsigned)grid), dim3(256), 0, s, p);
+        count_launch();
+        return hipGetLastError();
+    }
     GemmArgs a = plan(batch, n_out, n_in);
     a.x = x;
     a.q = w.q;

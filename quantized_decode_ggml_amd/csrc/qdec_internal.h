@@ -14,7 +14,10 @@ namespace qdec {
 //   q plane : n_out rows x n_in int8, row stride n_in bytes.  Row i's chunk c
 //             (16 bytes, weights 16c..16c+15) is one aligned 16-byte load.
 //   d plane : n_out rows x (n_in/32) fp16 scale bits, row stride n_in/32.
-// Total bytes = n_out*n_in*17/16 (the GGML size) plus plane alignment.
+//   dT plane: the same scales block-major (n_in/32 rows of n_out), so that one
+//             load gives a batched-GEMM tile the scales of many rows.
+// Total bytes = n_out*n_in*18/16 (the GGML size plus the second scale plane)
+// plus plane alignment; the GEMV kernels read the q and d planes only.
 //
 // Repacked Q4_K matrix:
 //   qs plane : n_out rows x n_in/2 bytes of nibbles, in GGML order within each
@@ -28,6 +31,7 @@ namespace qdec {
 struct Q8View {
     const int8_t* q;
     const uint16_t* d;
+    const uint16_t* dT;   // the scales again, block-major: dT[b * n_out + row] (batched GEMM)
 };
 
 // Fragment-tiled Q8_0 matrix (the matrix-core GEMV's copy): rows in groups of
@@ -68,14 +72,16 @@ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 inline int64_t q8_plane_bytes(int64_t n_in, int64_t n_out)
 {
-    return align_up(n_out * n_in, kAlign) + align_up(n_out * (n_in / 32) * 2, kAlign);
+    return align_up(n_out * n_in, kAlign) + 2 * align_up(n_out * (n_in / 32) * 2, kAlign);
 }
 
 inline Q8View q8_view(const void* base, int64_t n_in, int64_t n_out)
 {
     const char* p = static_cast<const char*>(base);
-    return Q8View{reinterpret_cast<const int8_t*>(p),
-                  reinterpret_cast<const uint16_t*>(p + align_up(n_out * n_in, kAlign))};
+    const int64_t off_d = align_up(n_out * n_in, kAlign);
+    const int64_t off_dt = off_d + align_up(n_out * (n_in / 32) * 2, kAlign);
+    return Q8View{reinterpret_cast<const int8_t*>(p), reinterpret_cast<const uint16_t*>(p + off_d),
+                  reinterpret_cast<const uint16_t*>(p + off_dt)};
 }
 
 inline int64_t q8t_groups(int64_t n_out) { return (n_out + 15) / 16; }
@@ -184,8 +190,13 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
 hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                            float* out, hipStream_t s);
 
+// Batched GEMM over a Q8_0 copy.  With a workspace of q8_gemm_workspace_bytes
+// (non-zero only for shapes the pipelined kernel takes) x is first rounded to
+// bf16 there and the DMA-fed kernel runs; without one the register-staged
+// kernel runs (same arithmetic, same results).
+int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch);
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
-                            float* out, hipStream_t s);
+                            float* out, void* workspace, hipStream_t s);
 hipError_t launch_f32_gemm(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, hipStream_t s);
 

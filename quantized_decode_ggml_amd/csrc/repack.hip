@@ -32,8 +32,8 @@ __device__ inline float fp16_bits_to_f32(uint16_t h)
 // so they are read as 17 halfwords.
 __global__ __launch_bounds__(256) void repack_q8_0_kernel(const uint16_t* __restrict__ raw,
                                                           int64_t nblocks, int64_t nb_row,
-                                                          int64_t n_in, int8_t* __restrict__ qp,
-                                                          uint16_t* __restrict__ dp)
+                                                          int64_t n_in, int64_t n_out, int8_t* __restrict__ qp,
+                                                          uint16_t* __restrict__ dp, uint16_t* __restrict__ dtp)
 {
     const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blk >= nblocks) return;
@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void repack_q8_0_kernel(const uint16_t* __rest
     dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
     dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
     dp[blk] = src[0];
+    dtp[kb * n_out + row] = src[0];
 }
 
 // 6-bit scale and min of sub-block s from the 12 packed bytes (GGML K-quant
@@ -203,8 +204,8 @@ hipError_t launch_repack_q8_0(const uint8_t* raw, int64_t n_in, int64_t n_out, v
     const Q8View v = q8_view(dst, n_in, n_out);
     const int64_t nb = n_in / 32, nblocks = nb * n_out;
     hipLaunchKernelGGL(repack_q8_0_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t*>(raw), nblocks, nb, n_in,
-                       const_cast<int8_t*>(v.q), const_cast<uint16_t*>(v.d));
+                       reinterpret_cast<const uint16_t*>(raw), nblocks, nb, n_in, n_out,
+                       const_cast<int8_t*>(v.q), const_cast<uint16_t*>(v.d), const_cast<uint16_t*>(v.dT));
     count_launch();
     return hipGetLastError();
 }

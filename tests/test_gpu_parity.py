@@ -294,3 +294,59 @@ def test_launch_counter_witness(qd):
     qd.q8_0_gemv(raw, 64, 32, x)
     sync()
     assert qd.launch_count() >= before + 2
+
+
+# The DMA-pipelined Q8_0 GEMM (>= 256 workgroups of 128 x 128 tiles with up to
+# 4 K splits, n_in % 64 == 0, n_out % 8 == 0): x rounded to bf16 in the stream
+# workspace, then the kernel (2 launches), plus the zero fill when K is split.
+@pytest.mark.parametrize("n_out,n_in,batch,launches", [(2048, 256, 2048, 2), (2040, 192, 2000, 2),
+                                                       (4096, 64, 1000, 2), (2048, 2048, 512, 3)])
+def test_q8_0_gemm_pipelined(qd, n_out, n_in, batch, launches):
+    raw = q8_weights(7100 + n_in, n_out, n_in)
+    x = synth.normal_f32(7101 + batch, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    qd.q8_0_gemm_batched(w, n_in, n_out, xd)        # makes the stream workspace
+    torch.cuda.synchronize()
+    before = qd.launch_count()
+    out = host(qd.q8_0_gemm_batched(w, n_in, n_out, xd))
+    assert qd.launch_count() - before == launches
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, "gemm q8_0 pipelined", rel=BF16_REL, abs_=0.0)
+
+
+def test_q8_0_gemm_pipelined_long_k_sampled(qd):
+    """n_in = 1600: 50 compute stages, past one 24-stage unrolled block and
+    into the tail; rows sampled against the oracle."""
+    n_out, n_in, batch = 4096, 1600, 1024            # 32 x 8 tiles
+    raw = q8_weights(7110, n_out, n_in)
+    x = synth.normal_f32(7111, (batch, n_in))
+    out = host(qd.q8_0_gemm_batched(dev(raw), n_in, n_out, dev(x)))
+    rng = np.random.default_rng(7112)
+    row_bytes = (n_in // 32) * 34
+    for b, i in zip(rng.integers(0, batch, 256), rng.integers(0, n_out, 256)):
+        ref, S = oracle.q8_0_gemv(raw[i * row_bytes:(i + 1) * row_bytes], n_in, 1, x[b:b + 1])
+        check_f32(out[b, i:i + 1], ref[0], S[0], f"gemm long-k b{b} i{i}", rel=BF16_REL, abs_=0.0)
+    assert np.isfinite(out).all()
+
+
+def test_q8_0_gemm_capture_without_workspace(qd):
+    """A capture on a stream with no workspace takes the register-staged kernel
+    (one launch) and still meets the bound."""
+    n_out, n_in, batch = 2048, 256, 2048
+    raw = q8_weights(7120, n_out, n_in)
+    x = synth.normal_f32(7121, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    torch.cuda.synchronize()
+    out = torch.empty((batch, n_out), device="cuda")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    before = qd.launch_count()
+    with torch.cuda.graph(g, stream=s):
+        qd.q8_0_gemm_batched(w, n_in, n_out, xd, out=out)
+    assert qd.launch_count() - before == 1
+    g.replay()
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(host(out), ref, S, "gemm captured", rel=BF16_REL, abs_=0.0)
+    del g
