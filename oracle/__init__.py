@@ -68,6 +68,10 @@ def _load():
             lib.oracle_topk.restype = ctypes.c_int
             lib.oracle_rmsnorm.argtypes = [P, I, I, P, ctypes.c_double, P]
             lib.oracle_rmsnorm.restype = ctypes.c_int
+            lib.oracle_rope.argtypes = [P, I, I, I, ctypes.c_double]
+            lib.oracle_rope.restype = None
+            lib.oracle_attention.argtypes = [P, P, P, I, I, I, I, I, ctypes.c_double, P, P]
+            lib.oracle_attention.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -244,3 +248,28 @@ def q8_0_swiglu_f64(w_gate, w_up, n_in: int, n_out: int, y) -> dict:
     u, su = q8_0_gemv_f64(w_up, n_in, n_out, y)
     silu_g = g / (1.0 + np.exp(-g))          # silu(z) = z / (1 + e^-z), as oracle_silu
     return {"out": silu_g * u, "g": g, "u": u, "Sg": sg, "Su": su}
+
+
+def rope(x, pos: int, base: float) -> np.ndarray:
+    """f64 (n_heads, d): adjacent pairs of each head rotated by pos * base^(-2i/d)."""
+    v = np.array(x, np.float64, copy=True)
+    n_heads, d = v.shape
+    _load().oracle_rope(_ptr(v), n_heads, d, int(pos), float(base))
+    return v
+
+
+def attention(q, k_cache, v_cache, n_ctx: int, scale: float):
+    """(out, A), each f64 (n_head, d): GQA softmax attention of q (n_head, d,
+    any float) over positions < n_ctx of the f32 caches (n_kv, max_seq, d);
+    A = sum_t p_t |V[t]| per element."""
+    qv = np.ascontiguousarray(q, np.float64)
+    kc = np.ascontiguousarray(k_cache, np.float32)
+    vc = np.ascontiguousarray(v_cache, np.float32)
+    n_head, d = qv.shape
+    n_kv, max_seq, _ = kc.shape
+    out = np.empty((n_head, d), np.float64)
+    a = np.empty((n_head, d), np.float64)
+    if _load().oracle_attention(_ptr(qv), _ptr(kc), _ptr(vc), n_head, n_kv, d, int(n_ctx), max_seq, float(scale),
+                                _ptr(out), _ptr(a)) != 0:
+        raise ValueError("attention: bad arguments")
+    return out, a

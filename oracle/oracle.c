@@ -415,3 +415,70 @@ int oracle_rmsnorm(const float* x, int64_t n, int64_t batch, const float* w, dou
     }
     return 0;
 }
+
+/* ------------------------------------------------------ decode attention -- */
+
+/* Device decode attention ([P1] try_q4k_soa_attention_device: rotary position
+ * embedding of the new q and k, append of k and v to the device KV cache, GQA
+ * scaled dot-product attention; the O projection that follows is a GEMV with
+ * residual).  The pages name these steps and keep an f32 KV cache, but print
+ * no formula; the readings used:
+ *   - RoPE on adjacent pairs: pair i = (x[2i], x[2i+1]) of a head of even
+ *     length d rotates by angle pos * base^(-2i/d):
+ *       (a, b) -> (a cos - b sin, a sin + b cos);
+ *   - cache layout [kv_head][max_seq][d], f32, position pos written in place;
+ *   - GQA: q head h reads kv head h / (n_head / n_kv_head);
+ *   - scores s_t = scale * (q_h . K[t]) for t < n_ctx, p = softmax(s),
+ *     out_h = sum_t p_t V[t].
+ * Everything in f64 here.  oracle_rope rotates in place; oracle_attention
+ * also returns A[h][j] = sum_t p_t |V[t][j]|, the scale of its tolerance. */
+void oracle_rope(double* x, int64_t n_heads, int64_t d, int64_t pos, double base)
+{
+    for (int64_t h = 0; h < n_heads; ++h) {
+        for (int64_t i = 0; i < d / 2; ++i) {
+            const double ang = (double)pos * pow(base, -2.0 * (double)i / (double)d);
+            const double c = cos(ang), s = sin(ang);
+            const double a = x[h * d + 2 * i], b = x[h * d + 2 * i + 1];
+            x[h * d + 2 * i] = a * c - b * s;
+            x[h * d + 2 * i + 1] = a * s + b * c;
+        }
+    }
+}
+
+int oracle_attention(const double* q, const float* k_cache, const float* v_cache, int64_t n_head,
+                     int64_t n_kv, int64_t d, int64_t n_ctx, int64_t max_seq, double scale,
+                     double* out, double* a_abs)
+{
+    if (n_head < 1 || n_kv < 1 || n_head % n_kv != 0 || d < 2 || n_ctx < 1 || n_ctx > max_seq) return -1;
+    double* s = (double*)malloc((size_t)n_ctx * sizeof(double));
+    if (!s) return -1;
+    const int64_t group = n_head / n_kv;
+    for (int64_t h = 0; h < n_head; ++h) {
+        const int64_t kv = h / group;
+        const float* K = k_cache + kv * max_seq * d;
+        const float* V = v_cache + kv * max_seq * d;
+        double m = -INFINITY;
+        for (int64_t t = 0; t < n_ctx; ++t) {
+            double dot = 0.0;
+            for (int64_t j = 0; j < d; ++j) dot += q[h * d + j] * (double)K[t * d + j];
+            s[t] = scale * dot;
+            if (s[t] > m) m = s[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < n_ctx; ++t) {
+            s[t] = exp(s[t] - m);
+            l += s[t];
+        }
+        for (int64_t j = 0; j < d; ++j) {
+            double o = 0.0, a = 0.0;
+            for (int64_t t = 0; t < n_ctx; ++t) {
+                o += s[t] * (double)V[t * d + j];
+                a += s[t] * fabs((double)V[t * d + j]);
+            }
+            out[h * d + j] = o / l;
+            if (a_abs) a_abs[h * d + j] = a / l;
+        }
+    }
+    free(s);
+    return 0;
+}

@@ -650,3 +650,85 @@ def test_q6k_gemv_exact_rational(n_out, n_in, batch):
             ex = exact_dot(W[i], x[b])
             assert out[b, i] == pytest.approx(float(ex), rel=1e-12, abs=1e-15)
             assert S[b, i] == pytest.approx(float(sum(abs(Fraction(float(a)) * Fraction(float(c))) for a, c in zip(W[i], x[b]))), rel=1e-12)
+
+
+# ------------------------------------------------------- decode attention --
+# Readings (the pages name RoPE, the KV append and GQA SDPA without formulas):
+# RoPE on adjacent pairs, angle pos * base^(-2i/d); GQA head h -> kv h // group;
+# softmax(scale * q.K) V.
+
+def test_rope_hand_example_and_identity():
+    x = np.array([[1.0, 0.0, 0.0, 1.0]])
+    y = oracle.rope(x, 1, 10000.0)
+    a1, a2 = 1.0, 10000.0 ** -0.5
+    assert y[0].tolist() == pytest.approx([math.cos(a1), math.sin(a1), -math.sin(a2), math.cos(a2)], abs=1e-15)
+    assert np.array_equal(oracle.rope(x, 0, 10000.0), x)
+
+
+def test_rope_rotations_compose_and_keep_pair_norms():
+    rng = np.random.default_rng(101)
+    x = rng.standard_normal((3, 16))
+    y = oracle.rope(oracle.rope(x, 7, 500000.0), 11, 500000.0)
+    assert np.allclose(y, oracle.rope(x, 18, 500000.0), rtol=0, atol=1e-12)
+    z = oracle.rope(x, 12345, 10000.0)
+    assert np.allclose(z[:, 0::2] ** 2 + z[:, 1::2] ** 2, x[:, 0::2] ** 2 + x[:, 1::2] ** 2, rtol=1e-13)
+
+
+def test_rope_scores_depend_on_relative_position():
+    rng = np.random.default_rng(102)
+    q, k = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
+    d1 = float(oracle.rope(q, 5, 10000.0)[0] @ oracle.rope(k, 3, 10000.0)[0])
+    d2 = float(oracle.rope(q, 1002, 10000.0)[0] @ oracle.rope(k, 1000, 10000.0)[0])
+    assert d1 == pytest.approx(d2, rel=1e-10)
+
+
+def _caches(rng, n_kv, max_seq, d):
+    return (rng.standard_normal((n_kv, max_seq, d)).astype(np.float32),
+            rng.standard_normal((n_kv, max_seq, d)).astype(np.float32))
+
+
+def test_attention_single_position_and_uniform_weights():
+    rng = np.random.default_rng(103)
+    kc, vc = _caches(rng, 2, 16, 8)
+    q = rng.standard_normal((4, 8))
+    out, _ = oracle.attention(q, kc, vc, 1, 0.35)
+    for h in range(4):
+        assert np.array_equal(out[h], vc[h // 2, 0].astype(np.float64))
+    out, _ = oracle.attention(np.zeros((4, 8)), kc, vc, 10, 0.35)
+    for h in range(4):
+        assert np.allclose(out[h], vc[h // 2, :10].astype(np.float64).mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_attention_two_positions_by_hand():
+    kc = np.zeros((1, 4, 2), np.float32)
+    vc = np.zeros((1, 4, 2), np.float32)
+    kc[0, 1, 0] = np.float32(2.0)
+    vc[0, 0] = [1.0, -2.0]
+    vc[0, 1] = [3.0, 4.0]
+    scale = math.log(3.0) / 2.0                # scores 0 and ln 3: weights 1/4, 3/4
+    out, a = oracle.attention(np.array([[1.0, 0.0]]), kc, vc, 2, scale)
+    assert out[0].tolist() == pytest.approx([0.25 * 1 + 0.75 * 3, 0.25 * -2 + 0.75 * 4], rel=1e-14)
+    assert a[0].tolist() == pytest.approx([0.25 * 1 + 0.75 * 3, 0.25 * 2 + 0.75 * 4], rel=1e-14)
+
+
+def test_attention_large_scores_stay_finite():
+    rng = np.random.default_rng(104)
+    kc, vc = _caches(rng, 1, 32, 16)
+    q = 1e3 * kc[0, 17].astype(np.float64)[None, :]       # position 17 dominates by far
+    out, _ = oracle.attention(q, kc, vc, 32, 1.0)
+    assert np.isfinite(out).all()
+    assert np.allclose(out[0], vc[0, 17], rtol=0, atol=1e-12)
+
+
+def test_attention_matches_dense_softmax():
+    """Against numpy's own softmax over explicitly repeated kv heads."""
+    rng = np.random.default_rng(105)
+    kc, vc = _caches(rng, 2, 40, 16)
+    q = rng.standard_normal((6, 16))
+    out, _ = oracle.attention(q, kc, vc, 33, 0.25)
+    for h in range(6):
+        K = kc[h // 3, :33].astype(np.float64)
+        V = vc[h // 3, :33].astype(np.float64)
+        s = 0.25 * (K @ q[h])
+        p = np.exp(s - s.max())
+        assert np.allclose(out[h], (p / p.sum()) @ V, rtol=1e-12, atol=1e-14)

@@ -39,6 +39,12 @@ MUTANTS = {
     "q6k_scale_index": ("(float)sc[8 * h + 2 * j + l / 16]", "(float)sc[8 * h + 2 * j]"),
     "q6k_no_offset": ("* (float)(q - 32);", "* (float)q;"),
     "q6k_ql_halves_swapped": ("ql[64 * h + 32 * (j % 2) + l]", "ql[64 * h + 32 * (j / 2) + l]"),
+    "rope_rotation_sign": ("x[h * d + 2 * i] = a * c - b * s;", "x[h * d + 2 * i] = a * c + b * s;"),
+    "rope_angle_exponent": ("pow(base, -2.0 * (double)i / (double)d)", "pow(base, -1.0 * (double)i / (double)d)"),
+    "rope_pairs_split_halves": ("const double a = x[h * d + 2 * i], b = x[h * d + 2 * i + 1];", "const double a = x[h * d + i], b = x[h * d + i + d / 2];"),
+    "attention_gqa_mapping": ("const int64_t kv = h / group;", "const int64_t kv = h % n_kv;"),
+    "attention_scale_dropped": ("s[t] = scale * dot;", "s[t] = dot;"),
+    "attention_off_by_one_context": ("for (int64_t t = 0; t < n_ctx; ++t) {\n            double dot", "for (int64_t t = 0; t + 1 < n_ctx; ++t) {\n            double dot"),
     "rmsnorm_sum_not_mean": ("const double r = 1.0 / sqrt(ss / (double)n + eps);", "const double r = 1.0 / sqrt(ss + eps);"),
     "rmsnorm_eps_outside_root": ("const double r = 1.0 / sqrt(ss / (double)n + eps);", "const double r = 1.0 / (sqrt(ss / (double)n) + eps);"),
     "rmsnorm_weight_dropped": ("out[b * n + j] = (double)x[b * n + j] * r * (double)w[j];", "out[b * n + j] = (double)x[b * n + j] * r;"),
