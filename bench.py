@@ -237,7 +237,38 @@ def suite(args):
     act = 4 * (E + E + (NQ + 2 * NKV) + NQ + 2 * E + E + FF + FF + 2 * E)
     timed("f2 pre-norm block b1 (norm+QKV, O+res, norm+SwiGLU, down+res; 4 launches)",
           [lambda i=i: block(i) for i in range(Lb)], blk + act, iters=40)
-    del bw
+    # decode attention (next-row f4): 24 query heads, 8 kv heads, d = 128, f32 cache
+    NH, NKV_H, HD = 24, 8, 128
+    for n_ctx in (1024, 4096, 8192):
+        cache_b = 2 * NKV_H * n_ctx * HD * 4
+        Lc = copies_for(cache_b)
+        caches = [(xdev(synth.seed(7, 2 * i), (NKV_H, n_ctx, HD)), xdev(synth.seed(7, 2 * i + 1), (NKV_H, n_ctx, HD)))
+                  for i in range(Lc)]
+        qa = xdev(synth.seed(7, 99), (NH, HD))
+        oa = torch.empty((NH, HD), device=dev)
+        timed(f"f4 attention decode n_ctx={n_ctx} (24 q / 8 kv heads, d 128, f32 cache)",
+              [lambda kc=kc, vc=vc: qd.attention_decode(qa, kc, vc, n_ctx, HD ** -0.5, out=oa) for kc, vc in caches],
+              cache_b + 2 * NH * HD * 4, iters=100)
+        del caches
+    # the whole pre-norm block with real attention at n_ctx 4096: norm+QKV, RoPE+append,
+    # attention, O+res, norm+SwiGLU, down+res (7 launches), blocks rotate
+    n_ctx = 4096
+    kcs = [xdev(synth.seed(8, 2 * i), (NKV_H, n_ctx, HD)) for i in range(Lb)]
+    vcs = [xdev(synth.seed(8, 2 * i + 1), (NKV_H, n_ctx, HD)) for i in range(Lb)]
+    att = torch.empty((1, NQ), device=dev)
+
+    def full_block(i):
+        qd.q8_0_rmsnorm_qkv(bw["q"][i], bw["k"][i], bw["v"][i], E, NQ, NKV, hb, g1, 1e-5, q_out=qb, k_out=kb,
+                            v_out=vb)
+        qd.rope_kv_append(qb.view(NH, HD), kb.view(NKV_H, HD), vb.view(NKV_H, HD), n_ctx - 1, 500000.0, kcs[i],
+                          vcs[i])
+        qd.attention_decode(qb.view(NH, HD), kcs[i], vcs[i], n_ctx, HD ** -0.5, out=att.view(NH, HD))
+        qd.q8_0_attn_out_ffn(bw["o"][i], bw["g"][i], bw["u"][i], bw["d"][i], E, NQ, FF, hb, att, g2, 1e-5,
+                             scratch=sb)
+
+    timed("f4 pre-norm block b1 with attention, n_ctx 4096 (7 launches)", [lambda i=i: full_block(i) for i in range(Lb)],
+          blk + act + 2 * NKV_H * n_ctx * HD * 4, iters=40)
+    del bw, kcs, vcs
     # config 3: batched GEMM (Q8_0 weights reuse up/down rotations; dense f32 separate)
     for B in (128, 512):
         for nm, ws, n_out, n_in in (("up 8192x3072", wup, 8192, 3072), ("down 3072x8192", wdn, 3072, 8192)):

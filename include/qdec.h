@@ -187,6 +187,36 @@ QDEC_API int q8_0_attn_out_ffn(const void* wo, const void* w_gate, const void* w
                       int64_t batch, float* h, const float* attn, const float* ffn_norm,
                       float eps, float* scratch, hipStream_t stream);
 
+/* Decode attention for one new token ([cuda_lane]
+ * try_q4k_soa_attention_device: RoPE, device KV append, GQA scaled
+ * dot-product attention; the O projection after it is q8_0_gemv_residual or
+ * q8_0_attn_out_ffn).  The pages give no formulas; the ones used:
+ *   RoPE: adjacent pairs (x[2i], x[2i+1]) of each head rotate by the angle
+ *         pos * base^(-2i/head_dim): (a, b) -> (a cos - b sin, a sin + b cos),
+ *         computed in f64 and rounded once to f32;
+ *   KV cache: device f32 [n_kv][max_seq][head_dim] for K and for V;
+ *   GQA: query head h reads kv head h / (n_head / n_kv);
+ *   attention: out_h = sum_{t < n_ctx} softmax_t(scale * q_h . K[t]) V[t].
+ * head_dim 64 or 128; n_kv divides n_head with at most 16 query heads per kv
+ * head.  q (n_head x head_dim), k, v (n_kv x head_dim) are device f32. */
+
+/* Rotate q and k in place for position pos (0 <= pos < max_seq) and write the
+ * rotated k and v at position pos of the caches.  base > 1 (e.g. 10000 or
+ * 500000).  No buffers may overlap. */
+QDEC_API int qdec_rope_kv_append(float* q, float* k, const float* v, int64_t n_head,
+                        int64_t n_kv, int64_t head_dim, int64_t pos, float base, float* k_cache,
+                        float* v_cache, int64_t max_seq, hipStream_t stream);
+
+/* out (n_head x head_dim, device f32) = attention of q over positions
+ * 0 .. n_ctx-1 (1 <= n_ctx <= max_seq), scale > 0 (usually 1/sqrt(head_dim)).
+ * f32 dot products and sums, expf; with n_ctx > 128 the per-chunk partials
+ * (n_head * ceil(n_ctx/128) * (head_dim + 2) floats) live in the stream's
+ * workspace: a capturing stream must already hold one (make one call on it
+ * before capturing), else QDEC_EINVAL.  out must not overlap the inputs. */
+QDEC_API int qdec_attention_decode(const float* q, const float* k_cache, const float* v_cache,
+                          int64_t n_head, int64_t n_kv, int64_t head_dim, int64_t n_ctx,
+                          int64_t max_seq, float scale, float* out, hipStream_t stream);
+
 /* Q4_K dequant-GEMV ([cuda_lane] try_q4k_soa_gemv): as q8_0_gemv over Q4_K
  * weights; n_in % 256 == 0, 1 <= batch <= 8. */
 QDEC_API int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,

@@ -40,6 +40,8 @@ _SIGS = {
     "q8_0_swiglu": [_P, _P, _I, _I, _I, _P, _P, _P],
     "q4k_gemv": [_P, _I, _I, _I, _P, _P, _P],
     "q6k_gemv": [_P, _I, _I, _I, _P, _P, _P],
+    "qdec_rope_kv_append": [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _I, _P],
+    "qdec_attention_decode": [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P],
     "q6k_dequantize": [_P, _I, _I, _P, _P],
     "q8_0_gemv_topk": [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P],
     "qdec_rmsnorm": [_P, _I, _I, _P, ctypes.c_float, _P, _P],
@@ -245,6 +247,27 @@ def q6k_gemv(w, n_in, n_out, x, out=None, stream=None):
     out = _f32_out(out, batch, n_out, x)
     _check(lib.q6k_gemv(_ptr(w), n_in, n_out, batch, _ptr(x), _ptr(out), _stream(stream)))
     _track(w)
+    return out
+
+
+def rope_kv_append(q, k, v, pos, base, k_cache, v_cache, stream=None):
+    """RoPE on q (n_head, d) and k (n_kv, d) in place for position pos, then
+    k and v written at pos of the caches (n_kv, max_seq, d)."""
+    n_head, d = q.shape
+    n_kv, max_seq, _ = k_cache.shape
+    _check(lib.qdec_rope_kv_append(_ptr(q), _ptr(k), _ptr(v), n_head, n_kv, d, int(pos), float(base), _ptr(k_cache),
+                                   _ptr(v_cache), max_seq, _stream(stream)))
+    return q, k
+
+
+def attention_decode(q, k_cache, v_cache, n_ctx, scale, out=None, stream=None):
+    """GQA softmax attention of q (n_head, d) over positions < n_ctx."""
+    n_head, d = q.shape
+    n_kv, max_seq, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((n_head, d), dtype=torch.float32, device=q.device)
+    _check(lib.qdec_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), n_head, n_kv, d, int(n_ctx), max_seq,
+                                     float(scale), _ptr(out), _stream(stream)))
     return out
 
 

@@ -500,6 +500,69 @@ int q8_0_attn_out_ffn(const void* wo, const void* w_gate, const void* w_up, cons
     return q8_gemv_common(kResidual, fn, ws, 1, n_ff, rows, batch, f, h, outs, 1, stream);
 }
 
+namespace {
+
+int check_heads(const char* fn, int64_t n_head, int64_t n_kv, int64_t head_dim, int64_t max_seq)
+{
+    if (head_dim != 64 && head_dim != 128) return fail(QDEC_EINVAL, "%s: head_dim=%lld not 64 or 128", fn, (long long)head_dim);
+    if (n_head < 1 || n_kv < 1 || n_head % n_kv != 0 || n_head / n_kv > 16 || n_head > 4096)
+        return fail(QDEC_EINVAL, "%s: n_head=%lld n_kv=%lld: need n_kv | n_head and n_head/n_kv <= 16", fn,
+                    (long long)n_head, (long long)n_kv);
+    if (max_seq < 1 || max_seq > (int64_t)1 << 24) return fail(QDEC_EINVAL, "%s: max_seq=%lld out of range", fn, (long long)max_seq);
+    return QDEC_OK;
+}
+
+}  // namespace
+
+int qdec_rope_kv_append(float* q, float* k, const float* v, int64_t n_head, int64_t n_kv, int64_t head_dim, int64_t pos,
+                        float base, float* k_cache, float* v_cache, int64_t max_seq, hipStream_t stream)
+{
+    const char* fn = "qdec_rope_kv_append";
+    QDEC_TRY(check_heads(fn, n_head, n_kv, head_dim, max_seq));
+    if (pos < 0 || pos >= max_seq) return fail(QDEC_EINVAL, "%s: pos=%lld outside [0, max_seq)", fn, (long long)pos);
+    if (!(base > 1.0f) || !(base < 1e30f)) return fail(QDEC_EINVAL, "%s: base=%g must be > 1", fn, (double)base);
+    QDEC_TRY(check_ptr(fn, "q", q, 8));
+    QDEC_TRY(check_ptr(fn, "k", k, 8));
+    QDEC_TRY(check_ptr(fn, "v", v, 8));
+    QDEC_TRY(check_ptr(fn, "k_cache", k_cache, 16));
+    QDEC_TRY(check_ptr(fn, "v_cache", v_cache, 16));
+    const int64_t qb = n_head * head_dim * 4, kb = n_kv * head_dim * 4, cb = n_kv * max_seq * head_dim * 4;
+    const void* bufs[5] = {q, k, v, k_cache, v_cache};
+    const int64_t lens[5] = {qb, kb, kb, cb, cb};
+    for (int a = 0; a < 5; ++a)
+        for (int b = a + 1; b < 5; ++b)
+            if (overlaps(bufs[a], lens[a], bufs[b], lens[b]))
+                return fail(QDEC_EINVAL, "%s: q, k, v and the two caches must not overlap", fn);
+    return finish(launch_rope_append(q, k, v, n_head, n_kv, head_dim, pos, (double)base, k_cache, v_cache, max_seq,
+                                     stream), fn);
+}
+
+int qdec_attention_decode(const float* q, const float* k_cache, const float* v_cache, int64_t n_head, int64_t n_kv,
+                          int64_t head_dim, int64_t n_ctx, int64_t max_seq, float scale, float* out, hipStream_t stream)
+{
+    const char* fn = "qdec_attention_decode";
+    QDEC_TRY(check_heads(fn, n_head, n_kv, head_dim, max_seq));
+    if (n_ctx < 1 || n_ctx > max_seq) return fail(QDEC_EINVAL, "%s: n_ctx=%lld outside [1, max_seq]", fn, (long long)n_ctx);
+    if (!(scale > 0.0f) || !(scale < 1e30f)) return fail(QDEC_EINVAL, "%s: scale=%g must be > 0", fn, (double)scale);
+    QDEC_TRY(check_ptr(fn, "q", q, 16));
+    QDEC_TRY(check_ptr(fn, "k_cache", k_cache, 16));
+    QDEC_TRY(check_ptr(fn, "v_cache", v_cache, 16));
+    QDEC_TRY(check_ptr(fn, "out", out, 4));
+    const int64_t ob = n_head * head_dim * 4, cb = n_kv * max_seq * head_dim * 4;
+    if (overlaps(out, ob, q, ob) || overlaps(out, ob, k_cache, cb) || overlaps(out, ob, v_cache, cb))
+        return fail(QDEC_EINVAL, "%s: out overlaps an input", fn);
+    void* wsp = nullptr;
+    const int64_t need = attention_workspace_bytes(n_head, head_dim, n_ctx);
+    if (need > 0) {
+        QDEC_TRY(stream_workspace(stream, need, &wsp));
+        if (!wsp)
+            return fail(QDEC_EINVAL, "%s: no workspace on this capturing stream: make one call on the stream "
+                        "before capturing it", fn);
+    }
+    return finish(launch_attention(q, k_cache, v_cache, n_head, n_kv, head_dim, n_ctx, max_seq, scale, out, wsp,
+                                   stream), fn);
+}
+
 int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
              hipStream_t stream)
 {

@@ -1,0 +1,291 @@
+// Device decode attention for one new token ("Module cuda_lane" page,
+// try_q4k_soa_attention_device: RoPE on the new q and k, append of k and v to
+// the device KV cache, GQA scaled dot-product attention; the O projection after
+// it is the Q8_0 GEMV with residual).  The pages name the steps and keep an f32
+// KV cache but give no formulas; the ones used:
+//   RoPE   : adjacent pairs (x[2i], x[2i+1]) of a head of length d rotate by
+//            pos * base^(-2i/d); angle, sine and cosine in f64, the rotated
+//            pair rounded once to f32;
+//   cache  : f32 [kv_head][max_seq][d], position pos written in place;
+//   GQA    : q head h reads kv head h / (n_head / n_kv);
+//   output : softmax over t < n_ctx of scale * (q_h . K[t]), times V.
+//
+// Attention is HBM-bound on the cache (2 * n_ctx * n_kv * d * 4 bytes per
+// token), so each workgroup takes one kv head and a chunk of 128 positions
+// (flash-decoding split): the G = n_head / n_kv query heads of the group share
+// every K and V row it reads.  A pair of threads owns a position for the
+// scores (half a K row each, streamed as float4, the G query vectors broadcast
+// from LDS), the chunk's max and sum come from a wave/LDS reduction, the
+// weights go to LDS, and each wave then sums p_t V[t] over a quarter of the
+// positions with its lanes across the columns (coalesced V rows), the four
+// wave partials meeting in LDS.  Each chunk leaves (max, sum, unnormalised
+// output) per head; a second kernel merges the chunks (log-sum-exp).  One
+// chunk writes the output directly.
+#include "qdec_internal.h"
+
+namespace qdec {
+
+namespace {
+
+constexpr int kAttnChunk = 128;   // positions per workgroup (two threads each for the scores)
+constexpr int kMaxGroup = 16;     // query heads per kv head
+
+__global__ __launch_bounds__(64) void rope_append_kernel(float* q, float* k, const float* v, int64_t n_head,
+                                                         int64_t d, int64_t pos, double log2_base,
+                                                         float* k_cache, float* v_cache, int64_t max_seq)
+{
+    const int64_t hh = blockIdx.x;
+    const bool is_q = hh < n_head;
+    const int64_t kvh = hh - n_head;
+    float* x = is_q ? q + hh * d : k + kvh * d;
+    for (int64_t i = threadIdx.x; i < d / 2; i += blockDim.x) {
+        const double ang = (double)pos * exp2(-2.0 * (double)i / (double)d * log2_base);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const double a = x[2 * i], b = x[2 * i + 1];
+        const float ra = (float)(a * cs - b * sn), rb = (float)(a * sn + b * cs);
+        x[2 * i] = ra;
+        x[2 * i + 1] = rb;
+        if (!is_q) {
+            float* kc = k_cache + (kvh * max_seq + pos) * d;
+            kc[2 * i] = ra;
+            kc[2 * i + 1] = rb;
+            const float* vv = v + kvh * d;
+            float* vc = v_cache + (kvh * max_seq + pos) * d;
+            vc[2 * i] = vv[2 * i];
+            vc[2 * i + 1] = vv[2 * i + 1];
+        }
+    }
+}
+
+__device__ inline float block_reduce(float v, float* red, bool is_max)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(v, off);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    const int w = threadIdx.x >> 6;
+    __syncthreads();                          // red may still be read from the previous reduction
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Partial attention of one (chunk, kv head).  part layout per (kv, chunk, g):
+// [max, sum, o[0..D)].  FINAL (a single chunk): out = o / sum directly.
+// Scores: position p = tid / 2 of the chunk, half (tid & 1) of the d columns
+// per thread, the halves added across the lane pair.  Weighted sum: wave w
+// takes positions w, w+4, ...; lane l takes columns D/64 * l ..; the four
+// wave partials meet in LDS.
+template <int D, bool FINAL>
+__global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_cache,
+                                                         const float* __restrict__ v_cache, int64_t n_kv, int group,
+                                                         int64_t n_ctx, int64_t max_seq, float scale,
+                                                         float* __restrict__ part, float* __restrict__ out)
+{
+    constexpr int HALF = D / 2, CPL = D / 64;     // columns per lane in the weighted sum
+    __shared__ __attribute__((aligned(16))) float qs[kMaxGroup * D];
+    __shared__ float ps[kMaxGroup][kAttnChunk];
+    __shared__ float red[4];
+    __shared__ float mx[kMaxGroup], sm[kMaxGroup];
+    __shared__ float ow[4][kMaxGroup][D];
+    const int64_t chunk = blockIdx.x, kv = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t nchunks = gridDim.x;
+    for (int u = tid; u < group * D; u += 256) qs[u] = q[(kv * group) * D + u];   // heads kv*group .. +group
+    __syncthreads();
+
+    const int pl = tid >> 1, half = tid & 1;
+    const int64_t t = chunk * kAttnChunk + pl;
+    const bool valid = t < n_ctx;
+    const int64_t tbase = chunk * kAttnChunk;
+    const int tn = (int)(n_ctx - tbase < kAttnChunk ? n_ctx - tbase : kAttnChunk);
+    // every load of the workgroup is issued before any arithmetic waits on one:
+    // this wave's V rows (used after the softmax), then the thread's K half-row
+    constexpr int VPW = kAttnChunk / 4;           // positions per wave in the weighted sum
+    const float* vbase = v_cache + (kv * max_seq + tbase) * D + CPL * lane;
+    float vr[VPW][CPL];
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+        const int tt = wave + 4 * i;
+        const int ts = tt < tn ? tt : tn - 1;     // in bounds; weight 0 past tn
+        if constexpr (CPL == 2) {
+            const float2 v2 = *reinterpret_cast<const float2*>(vbase + (int64_t)ts * D);
+            vr[i][0] = v2.x;
+            vr[i][1] = v2.y;
+        } else {
+            vr[i][0] = vbase[(int64_t)ts * D];
+        }
+    }
+    float4 kr[HALF / 4];
+    {
+        const int64_t tk = valid ? t : n_ctx - 1;
+        const float4* krow = reinterpret_cast<const float4*>(k_cache + (kv * max_seq + tk) * D + half * HALF);
+#pragma unroll
+        for (int j4 = 0; j4 < HALF / 4; ++j4) kr[j4] = krow[j4];
+    }
+    float s[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) s[g] = 0.0f;
+    {
+#pragma unroll
+        for (int j4 = 0; j4 < HALF / 4; ++j4) {
+            const float4 kk = kr[j4];
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g) {
+                if (g < group) {
+                    const float4 qq = *reinterpret_cast<const float4*>(&qs[g * D + half * HALF + 4 * j4]);
+                    s[g] = __builtin_fmaf(qq.x, kk.x, s[g]);
+                    s[g] = __builtin_fmaf(qq.y, kk.y, s[g]);
+                    s[g] = __builtin_fmaf(qq.z, kk.z, s[g]);
+                    s[g] = __builtin_fmaf(qq.w, kk.w, s[g]);
+                }
+            }
+        }
+    }
+    for (int g = 0; g < group; ++g) {
+        const float full = s[g] + __shfl_xor(s[g], 1);
+        const float sc = valid ? full * scale : -INFINITY;
+        const float m = block_reduce(sc, red, true);
+        const float p = valid ? expf(sc - m) : 0.0f;
+        const float l = block_reduce(half == 0 ? p : 0.0f, red, false);
+        if (half == 0) ps[g][pl] = p;
+        if (tid == 0) {
+            mx[g] = m;
+            sm[g] = l;
+        }
+    }
+    __syncthreads();
+
+    // weighted sum of V over this wave's positions (rows already in registers;
+    // positions past tn have weight 0)
+    float o[kMaxGroup][CPL];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[g][c] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+        const int tt = wave + 4 * i;
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) {
+            if (g < group) {
+                const float p = tt < tn ? ps[g][tt] : 0.0f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) o[g][c] = __builtin_fmaf(p, vr[i][c], o[g][c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g)
+        if (g < group)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) ow[wave][g][CPL * lane + c] = o[g][c];
+    __syncthreads();
+    for (int u = tid; u < group * D; u += 256) {
+        const int g = u / D, j = u % D;
+        const float ot = (ow[0][g][j] + ow[1][g][j]) + (ow[2][g][j] + ow[3][g][j]);
+        if constexpr (FINAL) {
+            out[(kv * group + g) * D + j] = ot / sm[g];
+        } else {
+            float* pr = part + ((kv * nchunks + chunk) * group + g) * (D + 2);
+            pr[2 + j] = ot;
+            if (j == 0) {
+                pr[0] = mx[g];
+                pr[1] = sm[g];
+            }
+        }
+    }
+}
+
+// Merge of the chunk partials of one query head (log-sum-exp): the chunk
+// maxima and weights are read in parallel (one chunk per thread, strided) and
+// kept in LDS, then each thread sums its column over the chunks.  (A variant
+// with 256 threads splitting the chunks four ways and an exp per chunk and
+// thread measured slower.)
+template <int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int64_t nchunks, int group,
+                                                         float* __restrict__ out)
+{
+    __shared__ float wsh[1024];
+    __shared__ float red[4];
+    const int64_t h = blockIdx.x;
+    const int64_t kv = h / group, g = h % group;
+    const int j = threadIdx.x;
+    auto at = [&](int64_t c) { return part + ((kv * nchunks + c) * group + g) * (D + 2); };
+    float m = -INFINITY;
+    for (int64_t c = j; c < nchunks; c += D) m = fmaxf(m, at(c)[0]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((j & 63) == 0) red[j >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < D / 64; ++w) m = fmaxf(m, red[w]);
+    float l = 0.0f, o = 0.0f;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += 1024) {
+        const int64_t cn = nchunks - c0 < 1024 ? nchunks - c0 : 1024;
+        __syncthreads();                                   // wsh of the previous block is consumed
+        for (int64_t c = j; c < cn; c += D) wsh[c] = expf(at(c0 + c)[0] - m);
+        __syncthreads();
+#pragma unroll 8
+        for (int64_t c = 0; c < cn; ++c) {
+            const float* pr = at(c0 + c);
+            l = __builtin_fmaf(pr[1], wsh[c], l);
+            o = __builtin_fmaf(pr[2 + j], wsh[c], o);
+        }
+    }
+    out[h * D + j] = o / l;
+}
+
+}  // namespace
+
+int64_t attention_workspace_bytes(int64_t n_head, int64_t head_dim, int64_t n_ctx)
+{
+    const int64_t nchunks = (n_ctx + kAttnChunk - 1) / kAttnChunk;
+    return nchunks > 1 ? n_head * nchunks * (head_dim + 2) * 4 : 0;
+}
+
+hipError_t launch_rope_append(float* q, float* k, const float* v, int64_t n_head, int64_t n_kv, int64_t d, int64_t pos,
+                              double base, float* k_cache, float* v_cache, int64_t max_seq, hipStream_t s)
+{
+    hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)(n_head + n_kv)), dim3(64), 0, s, q, k, v, n_head, d, pos,
+                       log2(base), k_cache, v_cache, max_seq);
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const float* q, const float* k_cache, const float* v_cache, int64_t n_head, int64_t n_kv,
+                            int64_t d, int64_t n_ctx, int64_t max_seq, float scale, float* out, void* workspace,
+                            hipStream_t s)
+{
+    const int group = (int)(n_head / n_kv);
+    const int64_t nchunks = (n_ctx + kAttnChunk - 1) / kAttnChunk;
+    const dim3 grid((unsigned)nchunks, (unsigned)n_kv);
+    float* part = static_cast<float*>(workspace);
+    if (nchunks == 1) {
+        if (d == 64)
+            hipLaunchKernelGGL((attn_chunk_kernel<64, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
+                               n_ctx, max_seq, scale, part, out);
+        else
+            hipLaunchKernelGGL((attn_chunk_kernel<128, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
+                               n_ctx, max_seq, scale, part, out);
+        count_launch();
+        return hipGetLastError();
+    }
+    if (d == 64) {
+        hipLaunchKernelGGL((attn_chunk_kernel<64, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
+                           n_ctx, max_seq, scale, part, out);
+        hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((unsigned)n_head), dim3(64), 0, s, part, nchunks, group, out);
+    } else {
+        hipLaunchKernelGGL((attn_chunk_kernel<128, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
+                           n_ctx, max_seq, scale, part, out);
+        hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((unsigned)n_head), dim3(128), 0, s, part, nchunks, group,
+                           out);
+    }
+    count_launch(2);
+    return hipGetLastError();
+}
+
+}  // namespace qdec

@@ -207,6 +207,16 @@ int64_t topk_workspace_bytes(int64_t n_out, int64_t batch, int k);
 hipError_t launch_topk(const float* logits, int64_t n_out, int64_t batch, int k, void* workspace,
                        int32_t* top_idx, float* top_val, hipStream_t s);
 
+// Decode attention (attention.hip): RoPE + KV append, and GQA attention over
+// n_ctx cached positions (head_dim 64 or 128, <= 16 query heads per kv head;
+// the workspace holds per-chunk partials, none for n_ctx <= 128).
+int64_t attention_workspace_bytes(int64_t n_head, int64_t head_dim, int64_t n_ctx);
+hipError_t launch_rope_append(float* q, float* k, const float* v, int64_t n_head, int64_t n_kv, int64_t d, int64_t pos,
+                              double base, float* k_cache, float* v_cache, int64_t max_seq, hipStream_t s);
+hipError_t launch_attention(const float* q, const float* k_cache, const float* v_cache, int64_t n_head, int64_t n_kv,
+                            int64_t d, int64_t n_ctx, int64_t max_seq, float scale, float* out, void* workspace,
+                            hipStream_t s);
+
 hipError_t launch_empty(hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 

@@ -49,6 +49,10 @@ def test_initial_state():
     lambda L: L.q8_0_dequantize(FAKE, 64, 8, FAKE * 2 + 4, None),         # out not 16-aligned
     lambda L: L.qdec_copy(FAKE, FAKE * 2, 24, None),                      # bytes % 16
     lambda L: L.qdec_release(None),
+    lambda L: L.qdec_attention_decode(FAKE, FAKE * 2, FAKE * 3, 24, 8, 96, 10, 100, 0.1, FAKE * 4, None),  # head_dim
+    lambda L: L.qdec_attention_decode(FAKE, FAKE * 2, FAKE * 3, 24, 5, 128, 10, 100, 0.1, FAKE * 4, None),  # 5 !| 24
+    lambda L: L.qdec_attention_decode(FAKE, FAKE * 2, FAKE * 3, 24, 8, 128, 101, 100, 0.1, FAKE * 4, None), # n_ctx
+    lambda L: L.qdec_rope_kv_append(FAKE, FAKE * 2, FAKE * 3, 24, 8, 128, 100, 10000.0, FAKE * 4, FAKE * 5, 100, None),  # pos
     lambda L: L.q6k_gemv(FAKE, 128, 8, 1, FAKE, FAKE * 2, None),           # Q6_K needs n_in % 256
     lambda L: L.q6k_gemv(FAKE, 256, 8, 9, FAKE, FAKE * 2, None),           # batch > 8
     lambda L: L.qdec_prepare(FAKE, 14, 64, 8, None),                      # Q6_K needs n_in % 256
