@@ -20,9 +20,13 @@
 // (x 2 matrices for SwiGLU) at once, so each x value in registers serves R
 // rows.  Per wave the order is: x of its columns (registers), every fp16 scale,
 // every q chunk, then the arithmetic, so the loads return in use order while
-// later ones are still in flight.  One batch row: one chunk column per wave
-// and one row group per workgroup, which keeps the arithmetic a wave still
-// owes after its last load short (the kernel's tail).  The scalar set-up
+// later ones are still in flight.  One batch row: x is copied once per
+// workgroup into LDS (direct global->LDS loads issued before the weight
+// loads) and shared by several row groups, and a wave takes two rows whole or
+// split over few waves; with a folded RMSNorm or SwiGLU x stays in registers,
+// one chunk column per wave and one row group per workgroup, which keeps the
+// arithmetic a wave still owes after its last load short (the kernel's tail).
+// A residual is fetched by the storing lanes before the weight stream.  The scalar set-up
 // before the first weight load is kept to a few dozen instructions: the
 // scalar unit is shared by every wave of a compute unit, and all of them
 // start together.  With several batch rows whose x does not
@@ -148,7 +152,6 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
     constexpr int NM = (MODE == kSwiGLU) ? 2 : 1;   // weight matrices per output row
     constexpr int GROUPS = NW / KS;                  // row groups per workgroup
     static_assert(GROUPS * KS == NW, "whole row groups per workgroup");
-    static_assert(!XL || NW == 4, "the LDS copy of x assumes 256 threads");
     constexpr bool XREG = !XL && B * CH <= 4;        // x in registers (<= 64 VGPRs)
     __shared__ float part[KS > 1 ? NW : 1][R][NM][B];
     __shared__ double part_ss[KS > 1 && B == 1 ? NW : 1];    // folded RMSNorm: sum of squares per wave
@@ -165,14 +168,13 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
     for (int b = 0; b < B; ++b) xrow[b] = a.x + (int64_t)(b < a.batch ? b : a.batch - 1) * a.n_in;
 
     if constexpr (XL) {
-        // batch * n_in / 4 float4 slots, a multiple of 256 on this path; slot s
-        // of the layout holds global float4 4c + (j ^ ((c >> 1) & 3)), c = s / 4
-        const int nper = (int)(((int64_t)a.batch * a.n_in) >> 10);
-        for (int i = 0; i < nper; ++i) {
-            const int sb = i * 256 + w * 64;
+        // batch * n_in / 4 float4 slots, 64 per wave and step; slot s of the
+        // layout holds global float4 4c + (j ^ ((c >> 1) & 3)), c = s / 4
+        const int nslot = (int)(((int64_t)a.batch * a.n_in) >> 2);
+        for (int sb = w * 64; sb < nslot; sb += 64 * NW) {
             const int c = (sb + lane) >> 2, j = (sb + lane) & 3;
             const float* src = a.x + (int64_t)(4 * c + (j ^ ((c >> 1) & 3))) * 4;
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(xs + sb * 4), 16, 0, 0);
+            if (sb + lane < nslot) __builtin_amdgcn_global_load_lds(src, (lds_void*)(xs + sb * 4), 16, 0, 0);
         }
         // the vmcnt wait below counts only the weight loads issued after these
         asm volatile("" ::: "memory");
@@ -184,6 +186,14 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
         for (int k = 0; k < CH; ++k)
 #pragma unroll
             for (int b = 0; b < B; ++b) load_x16(xrow[b] + (int64_t)(lane + 64 * (cbase + k)) * 16, xr[k][b]);
+    }
+    // Residual epilogue: the storing lanes fetch their residual value before
+    // the weight stream, so no load round trip is left for the kernel's tail.
+    float rpre = 0.0f;
+    if constexpr (MODE == kResidual) {
+        const int rl = lane / B, bl = lane % B;
+        if (ks == 0 && lane < R * B && bl < a.batch && row0 + rl < a.total_rows)
+            rpre = a.residual[(int64_t)bl * a.total_rows + row0 + rl];
     }
     // One batch row may fold an RMSNorm of x into the product: the norm
     // weights of the wave's columns are loaded with x (before the weight
@@ -276,6 +286,8 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
             if constexpr (XREG) {
 #pragma unroll
                 for (int t = 0; t < 16; ++t) xv[t] = xr[XREG ? k : 0][0][t];
+            } else if constexpr (XL) {
+                lds_x16(xs, lane + 64 * (cbase + k), xv);
             } else {
                 load_x16(xrow[0] + (int64_t)(lane + 64 * (cbase + k)) * 16, xv);
             }
@@ -381,7 +393,10 @@ __global__ __launch_bounds__(64 * NW) void q8_0_gemv_fast(Q8GemvArgs a)
         }
     }
     const int rl = lane / B, bl = lane % B;
-    if (lane < R * B && bl < a.batch && row0 + rl < a.total_rows) store_row<MODE>(a, row0 + rl, bl, v0, v1);
+    if (lane < R * B && bl < a.batch && row0 + rl < a.total_rows) {
+        if constexpr (MODE == kResidual) a.out0[(int64_t)bl * a.total_rows + row0 + rl] = rpre + v0;
+        else store_row<MODE>(a, row0 + rl, bl, v0, v1);
+    }
 }
 
 // General path: row groups of LPR lanes, one row per group, bounds-checked loop.
@@ -554,6 +569,64 @@ KernelFn pick_b1(int r, int nch64)
     }
 }
 
+// One batch row with x staged in LDS (no folded norm, one weight matrix per
+// row): G row groups of a workgroup share one LDS copy of x, and a wave takes
+// R whole rows (n_in <= 4096) or a row's K split over KS waves (wider rows).
+// Measured against the register shapes (graph-replayed launches over rotated
+// copies): fewer cross-wave reductions, and x read from L2 once per
+// workgroup instead of once per wave.  Up to 4096 columns one row per wave,
+// 8 row groups, 4 while that leaves fewer than 1024 workgroups (8192x3072:
+// 6.6 -> 6.0-6.1 us; 5120x3072: 4.96 -> 4.75 us), and two rows per wave in 4
+// groups for very tall matrices (128256x3072: 67 -> 62 us); 8192 columns two rows per
+// wave, four waves per row, two groups (3072x8192 with residual: 7.0 ->
+// 6.7-6.8 us).
+struct B1XlShape { int ks, ch, g, r; };
+
+B1XlShape b1_xl_shape(int nch64, int64_t total_rows)
+{
+    if (nch64 >= 1 && nch64 <= 4) {
+        if (total_rows / 8 >= 8192) return {1, nch64, 4, 2};
+        return {1, nch64, total_rows / 8 >= 1024 ? 8 : 4, 1};
+    }
+    B1XlShape sh{0, 0, 2, 2};
+    switch (nch64) {
+        case 6: sh.ks = 2; sh.ch = 3; break;
+        case 8: sh.ks = 4; sh.ch = 2; break;
+        case 12: sh.ks = 4; sh.ch = 3; break;
+        default: return {0, 0, 0, 0};
+    }
+    if (total_rows / (sh.g * 2) < 512) sh.r = 1;
+    return sh;
+}
+
+template <int MODE, int CH, int KS, int NW>
+KernelFn pick_b1_xl_r(int r)
+{
+    return r == 2 ? q8_0_gemv_fast<MODE, 1, 2, CH, KS, true, NW> : q8_0_gemv_fast<MODE, 1, 1, CH, KS, true, NW>;
+}
+
+template <int MODE, int CH>
+KernelFn pick_b1_xl_g(const B1XlShape& sh)
+{
+    if (sh.r == 2) return q8_0_gemv_fast<MODE, 1, 2, CH, 1, true, 4>;
+    return sh.g == 8 ? q8_0_gemv_fast<MODE, 1, 1, CH, 1, true, 8> : q8_0_gemv_fast<MODE, 1, 1, CH, 1, true, 4>;
+}
+
+template <int MODE>
+KernelFn pick_b1_xl(const B1XlShape& sh, int nch64)
+{
+    switch (nch64) {
+        case 1: return pick_b1_xl_g<MODE, 1>(sh);
+        case 2: return pick_b1_xl_g<MODE, 2>(sh);
+        case 3: return pick_b1_xl_g<MODE, 3>(sh);
+        case 4: return pick_b1_xl_g<MODE, 4>(sh);
+        case 6: return pick_b1_xl_r<MODE, 3, 2, 4>(sh.r);
+        case 8: return pick_b1_xl_r<MODE, 2, 4, 8>(sh.r);
+        case 12: return pick_b1_xl_r<MODE, 3, 4, 8>(sh.r);
+        default: return nullptr;
+    }
+}
+
 // Largest x staged in LDS (bytes): up to 48 KB three workgroups still fit on a
 // CU; beyond that the lost occupancy costs more than the L2 reads of x save
 // (measured on the 8-row 3072-wide and 2-row 8192-wide cases).  Larger batch
@@ -593,7 +666,18 @@ hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
     int64_t blocks = 0;
     int threads = 256;
     bool xl = false;
-    if (nch64 > 0 && bt == 1) {
+    const B1XlShape xsh = b1_xl_shape(nch64, a.total_rows);
+    if (bt == 1 && xsh.ks > 0 && p.mode != kSwiGLU && !p.norm_w && a.n_in * 4 <= kXldsMax) {
+        switch (p.mode) {
+            case kPlain: fn = pick_b1_xl<kPlain>(xsh, nch64); break;
+            case kResidual: fn = pick_b1_xl<kResidual>(xsh, nch64); break;
+            default: fn = pick_b1_xl<kQKV>(xsh, nch64); break;
+        }
+        threads = 64 * xsh.ks * xsh.g;
+        const int64_t rows_per_block = (int64_t)xsh.g * xsh.r;
+        blocks = (a.total_rows + rows_per_block - 1) / rows_per_block;
+        xl = true;
+    } else if (nch64 > 0 && bt == 1) {
         const B1Shape sh = b1_shape(nch64);
         const int r = b1_rows(p.mode, sh.ks, a.total_rows);
         switch (p.mode) {

@@ -25,8 +25,9 @@
 //   (hi + mid) + lo.
 // Rounding: at most 31 roundings inside each MFMA sum, one per block in the
 // scale-and-accumulate chain (NBW blocks per wave), KS - 1 in the cross-wave
-// sum and 2 for the parts: below 110 units of 2^-24 of sum_j |w x| at
-// n_in = 8192, i.e. under 7e-6, inside the 1e-5 bound.
+// sum, 2 for the parts and, with the K split, one per workgroup slice plus
+// the residual: below 110 units of 2^-24 of sum_j |w x| at n_in = 8192,
+// i.e. under 7e-6, inside the 1e-5 bound.
 //
 // Operands per MFMA (16x16x32): A = an x-split fragment, lane l holding
 // stacked row l % 16 and k = 8*(l/16)..+8 of the block; B = the weight
@@ -42,7 +43,12 @@
 // (x 2 matrices for SwiGLU), which share each x fragment, and splits K over
 // its KS waves, NBW blocks each; a wave streams its blocks in straight-line
 // code with loads D blocks ahead, then the waves add their partial sums
-// through LDS.
+// through LDS.  Where that grid would not fill the chip (fewer than 512 row
+// groups, plain and residual forms), K is also split over workgroups: the
+// x-split launch first sets out = residual (or 0), and each workgroup adds
+// its partial sums with f32 atomics (up to n_in/256 more roundings, in an
+// order that can change between calls: such results are not bitwise
+// reproducible, and stay inside the bound below).
 #include "gemv_common.h"
 
 namespace qdec {
@@ -60,11 +66,16 @@ constexpr int kParts = 3;
 // holds part p of x[b] (3*batch rows, zero beyond), in NV = ceil(3*batch/16)
 // fragments of 16 rows.  One thread per (block, fragment, lane): 8 bf16 of
 // virtual row 16f + lane % 16 at k = 32*block + 8*(lane/16) .. +7.
+// With the K split over workgroups (partial sums added atomically) the same
+// launch first sets out = residual (or 0) for the ninit = batch * n_out
+// outputs.
 __global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ x, int batch,
                                                       int64_t n_in, int nv, int64_t nslots,
-                                                      u32x4* __restrict__ xs)
+                                                      u32x4* __restrict__ xs, float* out,
+                                                      const float* residual, int64_t ninit)
 {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < ninit) out[t] = residual ? residual[t] : 0.0f;
     if (t >= nslots) return;
     const int l = (int)(t & 63);
     const int64_t bf = t >> 6;
@@ -114,12 +125,17 @@ struct TileArgs {
     int64_t tq1, tq2, td1, td2;
     int64_t gend0, gend1, groups;
     int64_t nb;
+    int ksplit;   // workgroups per row-group set along K (AT kernels)
 };
 
-template <int MODE, int KS, int NBW, int DP, int RG, int NV>
+// AT: the workgroup covers KS * NBW blocks of K (slice blockIdx.x % ksplit)
+// and adds its partial sums to the output atomically (plain and residual
+// forms; the output was initialised by the split kernel).
+template <int MODE, int KS, int NBW, int DP, int RG, int NV, bool AT>
 __global__ __launch_bounds__(KS * 64) void q8_0_gemv_mfma(Q8GemvArgs a, TileArgs t, const u32x4* __restrict__ xs)
 {
     constexpr int NM = (MODE == kSwiGLU) ? 2 : 1;
+    static_assert(!AT || MODE == kPlain || MODE == kResidual, "atomic K split: linear epilogues only");
     constexpr int D = DP < NBW ? DP : NBW;   // blocks in flight ahead of the one computed
     constexpr int RS = D + 1;                 // register ring slots
     static_assert(KS > 1, "the epilogue runs on wave 0 after the K reduction");
@@ -129,7 +145,9 @@ __global__ __launch_bounds__(KS * 64) void q8_0_gemv_mfma(Q8GemvArgs a, TileArgs
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g4 = lane >> 4;
-    const int blk0 = w * NBW;
+    const int64_t gb = AT ? blockIdx.x / t.ksplit : blockIdx.x;   // row-group set
+    const int kp = AT ? (int)(blockIdx.x % t.ksplit) : 0;          // K slice
+    const int blk0 = (kp * KS + w) * NBW;
     const int64_t tile_stride = t.nb * 512, dtile_stride = t.nb * 16;
 
     // tile and scale pointers of this wave's first block, per row group and matrix
@@ -137,7 +155,7 @@ __global__ __launch_bounds__(KS * 64) void q8_0_gemv_mfma(Q8GemvArgs a, TileArgs
     const uint16_t* td[RG][NM];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-        int64_t G = (int64_t)blockIdx.x * RG + rg;
+        int64_t G = gb * RG + rg;
         G = G < t.groups ? G : t.groups - 1;                  // loads stay in bounds
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
@@ -255,13 +273,14 @@ __global__ __launch_bounds__(KS * 64) void q8_0_gemv_mfma(Q8GemvArgs a, TileArgs
     const int r = lane & 15;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-        const int64_t row = ((int64_t)blockIdx.x * RG + rg) * 16 + r;
+        const int64_t row = (gb * RG + rg) * 16 + r;
         if (row >= a.total_rows) continue;
         for (int b = g4; b < a.batch; b += 4) {
             const float v0 = (fin[rg][0][b][r] + fin[rg][0][a.batch + b][r]) + fin[rg][0][2 * a.batch + b][r];
             const float v1 = (fin[rg][NM - 1][b][r] + fin[rg][NM - 1][a.batch + b][r]) +
                              fin[rg][NM - 1][2 * a.batch + b][r];
-            store_row<MODE>(a, row, b, v0, v1);
+            if constexpr (AT) unsafeAtomicAdd(a.out0 + (int64_t)b * a.total_rows + row, v0);
+            else store_row<MODE>(a, row, b, v0, v1);
         }
     }
 }
@@ -280,12 +299,28 @@ template <int MODE, int KS, int RG, int NV>
 MfmaFn pick_nbw(int nbw)
 {
     switch (nbw) {
-        case 8: return q8_0_gemv_mfma<MODE, KS, 8, depth<MODE, RG>(), RG, NV>;
-        case 16: return q8_0_gemv_mfma<MODE, KS, 16, depth<MODE, RG>(), RG, NV>;
-        case 24: return q8_0_gemv_mfma<MODE, KS, 24, depth<MODE, RG>(), RG, NV>;
-        case 32: return q8_0_gemv_mfma<MODE, KS, 32, depth<MODE, RG>(), RG, NV>;
+        case 8: return q8_0_gemv_mfma<MODE, KS, 8, depth<MODE, RG>(), RG, NV, false>;
+        case 16: return q8_0_gemv_mfma<MODE, KS, 16, depth<MODE, RG>(), RG, NV, false>;
+        case 24: return q8_0_gemv_mfma<MODE, KS, 24, depth<MODE, RG>(), RG, NV, false>;
+        case 32: return q8_0_gemv_mfma<MODE, KS, 32, depth<MODE, RG>(), RG, NV, false>;
         default: return nullptr;
     }
+}
+
+// K split over workgroups (plain and residual): kAtKs waves of kAtNbw blocks
+// per workgroup, kAtRg row groups sharing every x fragment.  Taken where the
+// one-workgroup-per-row-group grid would leave compute units idle; measured
+// on 3072x8192 with residual (graph-replayed, both launches): batch 3 / 4 / 8
+// 12.9 / 13.0 / 16.7 -> 10.7 / 10.9 / 13.1 us (4 x 8 x 2 against 4 x 8 x 4,
+// 4 x 16 x 2 and 4 x 8 x 1: 11.7-14.7 us).  On 8192x3072, where two row
+// groups per workgroup already fill the chip, it gained nothing.
+constexpr int kAtKs = 4, kAtNbw = 8, kAtRg = 2;
+
+template <int MODE>
+MfmaFn pick_at(int nv)
+{
+    return nv == 1 ? q8_0_gemv_mfma<MODE, kAtKs, kAtNbw, 8, kAtRg, 1, true>
+                   : q8_0_gemv_mfma<MODE, kAtKs, kAtNbw, 8, kAtRg, 2, true>;
 }
 
 template <int MODE, int RG, int NV>
@@ -361,26 +396,40 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
         t.groups = q8t_groups(p.rows[0]);
         t.gend0 = t.gend1 = t.groups;
     }
-    // two row groups per workgroup while that still gives one workgroup per CU
-    // (SwiGLU already shares each x fragment between its two matrices)
-    const int rg = p.mode != kSwiGLU && t.groups / 2 >= 256 ? 2 : 1;
     const int nv = frags_for(p.batch);
     MfmaFn fn = nullptr;
-    switch (p.mode) {
-        case kPlain: fn = pick_mfma<kPlain>(ks, nbw, rg, nv); break;
-        case kResidual: fn = pick_mfma<kResidual>(ks, nbw, rg, nv); break;
-        case kQKV: fn = pick_mfma<kQKV>(ks, nbw, rg, nv); break;
-        default: fn = pick_mfma<kSwiGLU>(ks, nbw, rg, nv); break;
+    int64_t blocks = 0;
+    int64_t ninit = 0;
+    const int64_t at_blocks = (int64_t)kAtKs * kAtNbw;
+    if ((p.mode == kPlain || p.mode == kResidual) && t.nb % at_blocks == 0 && t.groups / 2 < 256) {
+        // K split over workgroups: x fragments are read by kAtRg row groups
+        // per workgroup and only for its K slice
+        t.ksplit = (int)(t.nb / at_blocks);
+        fn = p.mode == kPlain ? pick_at<kPlain>(nv) : pick_at<kResidual>(nv);
+        blocks = (t.groups + kAtRg - 1) / kAtRg * t.ksplit;
+        ninit = p.batch * p.rows[0];
+        ks = kAtKs;
+    } else {
+        // two row groups per workgroup while that still gives one workgroup per CU
+        // (SwiGLU already shares each x fragment between its two matrices)
+        const int rg = p.mode != kSwiGLU && t.groups / 2 >= 256 ? 2 : 1;
+        switch (p.mode) {
+            case kPlain: fn = pick_mfma<kPlain>(ks, nbw, rg, nv); break;
+            case kResidual: fn = pick_mfma<kResidual>(ks, nbw, rg, nv); break;
+            case kQKV: fn = pick_mfma<kQKV>(ks, nbw, rg, nv); break;
+            default: fn = pick_mfma<kSwiGLU>(ks, nbw, rg, nv); break;
+        }
+        blocks = (t.groups + rg - 1) / rg;
     }
     if (!fn) return hipErrorNotSupported;
     u32x4* xs = static_cast<u32x4*>(workspace);
     const int64_t nslots = (p.n_in / 32) * nv * 64;
-    hipLaunchKernelGGL(split_x_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, p.x,
-                       (int)p.batch, p.n_in, nv, nslots, xs);
+    const int64_t nthreads = nslots > ninit ? nslots : ninit;
+    hipLaunchKernelGGL(split_x_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, p.x,
+                       (int)p.batch, p.n_in, nv, nslots, xs, a.out0, ninit ? p.residual : nullptr, ninit);
     count_launch();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t blocks = (t.groups + rg - 1) / rg;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(ks * 64), 0, s, a, t, xs);
     count_launch();
     return hipGetLastError();

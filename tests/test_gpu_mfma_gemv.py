@@ -132,11 +132,15 @@ def test_residual_in_place(qd, batch):
     check_f32(host(buf), ref, S, f"residual in place b{batch}")
 
 
-def test_graph_capture_with_workspace(qd):
+@pytest.mark.parametrize("n_out,bitwise", [(8192, True), (1024, False)])
+def test_graph_capture_with_workspace(qd, n_out, bitwise):
     """Warm-up on the capture stream makes its workspace; the captured graph then
     uses the matrix-core path (2 launches recorded) and every replay, with eager
-    work in between, matches the eager result bit for bit."""
-    n_out, n_in, batch = 1024, 3072, 4
+    work in between, stays within the bound and, where the result is
+    reproducible (8192 rows: one workgroup per row pair), matches the eager
+    result bit for bit.  Below 8192 rows K is split over workgroups with
+    atomic partial sums, whose order (and so the last bits) may change."""
+    n_in, batch = 3072, 4
     raw = q8_weights(9600, n_out, n_in)
     x = synth.normal_f32(9601, (batch, n_in))
     w, xd = dev(raw), dev(x)
@@ -158,7 +162,8 @@ def test_graph_capture_with_workspace(qd):
         out.fill_(float("nan"))
         g.replay()
         got = host(out)
-        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {k}"
+        if bitwise:
+            assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {k}"
         check_f32(got, ref, S, f"replay {k}")
         qd.q8_0_gemv(w, n_in, n_out, xd)          # eager work between replays
     del g
