@@ -13,7 +13,14 @@
 // lane (16 weights: 8 of sub-block 2p, 8 of sub-block 2p+1), so a row of n_in
 // weights is n_in/16 chunks and lane j of a wave takes chunks j, j+64, ...; K
 // is split over KS waves of the workgroup and each wave computes R rows.  One
-// batch row: one chunk column per wave and one row group per workgroup.  Per
+// batch row: x is copied once per workgroup into LDS (direct global->LDS
+// loads before the weight loads, each chunk's 16 values gathered into one
+// bank-swizzled 64-byte slot) and shared by several row groups; up to 4096
+// columns a wave takes one whole row.  Measured against one chunk column per
+// wave with x in registers (graph-replayed launches over rotated copies):
+// 8192x3072 6.58 -> 6.06 us; more rows per wave were slower (the kernel is
+// close to the VALU issue limit).  Wider rows keep x in registers: at
+// 3072x8192 the LDS shapes measured 6.5-6.7 us against 6.53.  Per
 // chunk the dot product is taken per sub-block in the factored form
 //     sum_t w_t x_t = (d*sc) * sum_t q_t x_t - (dmin*m) * sum_t x_t,
 // where d*sc and dmin*m are exact in f32.  sum_t x_t depends only on the lane's
@@ -137,15 +144,47 @@ __device__ inline float wave_sum(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// x staged in LDS (one batch row): chunk c's 16 values (8 of the low-nibble
+// sub-block, 8 of the high one) as four float4, part q stored at float4 slot
+// 4c + (q ^ ((c >> 1) & 3)) so that neighbouring lanes hit distinct banks.
+__device__ inline const float* xchunk_src(const float* x, int c, int q)
+{
+    return x + chunk_x_offset(c) + (q < 2 ? 4 * q : 32 + 4 * (q - 2));
+}
+
+__device__ inline void lds_xchunk(const float* xs, int c, XChunk& xc)
+{
+    const float4* xp = reinterpret_cast<const float4*>(xs);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 v = xp[4 * c + (q ^ ((c >> 1) & 3))];
+        float* d = q < 2 ? xc.lo + 4 * q : xc.hi + 4 * (q - 2);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+}
+
 // Fast path: n_in a multiple of 1024; CH chunk columns per lane, KS waves per
-// row group, R rows per wave, B batch rows.
-template <int B, int R, int CH, int KS, int NW>
+// row group, R rows per wave, B batch rows; XL: x of one batch row staged in
+// LDS (n_in floats of dynamic shared memory) and shared by the NW / KS row
+// groups of the workgroup.
+template <int B, int R, int CH, int KS, int NW, bool XL = false>
 __global__ __launch_bounds__(64 * NW) void q4k_gemv_fast(Q4KArgs a)
 {
     constexpr int GROUPS = NW / KS;
     static_assert(GROUPS * KS == NW, "whole row groups per workgroup");
-    constexpr bool XREG = B * CH <= 4;
+    static_assert(!XL || B == 1, "LDS-staged x: one batch row");
+    constexpr bool XREG = !XL && B * CH <= 4;
     __shared__ float part[KS > 1 ? NW : 1][R][B];
+    extern __shared__ __attribute__((aligned(16))) float xs[];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -158,6 +197,16 @@ __global__ __launch_bounds__(64 * NW) void q4k_gemv_fast(Q4KArgs a)
 #pragma unroll
     for (int b = 0; b < B; ++b) xrow[b] = a.x + (int64_t)(b < a.batch ? b : a.batch - 1) * a.n_in;
 
+    if constexpr (XL) {
+        const int nslot = (int)(a.n_in >> 2);
+        for (int sb = w * 64; sb < nslot; sb += 64 * NW) {
+            const int sl = sb + lane, c = sl >> 2, j = sl & 3;
+            if (sl < nslot)
+                __builtin_amdgcn_global_load_lds(xchunk_src(a.x, c, j ^ ((c >> 1) & 3)), (lds_void*)(xs + sb * 4), 16, 0, 0);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
     XChunk xr[XREG ? CH : 1][XREG ? B : 1];
     if constexpr (XREG) {
 #pragma unroll
@@ -209,6 +258,13 @@ __global__ __launch_bounds__(64 * NW) void q4k_gemv_fast(Q4KArgs a)
         for (int r = 0; r < R; ++r) qv[k][r] = stream_load8(qrow[r] + (int64_t)(lane + 64 * (cbase + k)) * 8);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XL) {
+        // this wave's x slots have landed once at most the weight loads remain;
+        // the barrier makes every wave's slots visible
+        wait_vmcnt<3 * CH * R>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     if constexpr (XREG) {
 #pragma unroll
@@ -229,6 +285,9 @@ __global__ __launch_bounds__(64 * NW) void q4k_gemv_fast(Q4KArgs a)
             XChunk xc;
             if constexpr (XREG) {
                 xc = xr[XREG ? k : 0][XREG ? b : 0];
+            } else if constexpr (XL) {
+                lds_xchunk(xs, lane + 64 * (cbase + k), xc);
+                sum_xchunk(xc);
             } else {
                 load_xchunk(xrow[b], lane + 64 * (cbase + k), xc);
                 sum_xchunk(xc);
@@ -352,6 +411,34 @@ B1Shape b1_shape(int nch64)
     }
 }
 
+// One batch row with x in LDS (up to 4096 columns): one whole row per wave,
+// G = 8 row groups per workgroup, 4 while that leaves fewer than 1024
+// workgroups.
+struct B1XlShape { int ks, ch, g, r; };
+
+B1XlShape b1_xl_shape(int nch64, int64_t n_out)
+{
+    if (nch64 >= 1 && nch64 <= 4) return {1, nch64, n_out / 8 >= 1024 ? 8 : 4, 1};
+    return {0, 0, 0, 0};
+}
+
+template <int CH>
+KernelFn pick_b1_xl_g(int g)
+{
+    return g == 8 ? q4k_gemv_fast<1, 1, CH, 1, 8, true> : q4k_gemv_fast<1, 1, CH, 1, 4, true>;
+}
+
+KernelFn pick_b1_xl(const B1XlShape& sh, int nch64)
+{
+    switch (nch64) {
+        case 1: return pick_b1_xl_g<1>(sh.g);
+        case 2: return pick_b1_xl_g<2>(sh.g);
+        case 3: return pick_b1_xl_g<3>(sh.g);
+        case 4: return pick_b1_xl_g<4>(sh.g);
+        default: return nullptr;
+    }
+}
+
 template <int R>
 KernelFn pick_b1_split(int nch64)
 {
@@ -388,7 +475,15 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
     KernelFn fn = nullptr;
     int64_t blocks = 0;
     int threads = 256;
-    if (nch64 > 0 && bt == 1) {
+    size_t lds = 0;
+    const B1XlShape xsh = b1_xl_shape(nch64, n_out);
+    if (bt == 1 && xsh.ks > 0) {
+        fn = pick_b1_xl(xsh, nch64);
+        threads = 64 * xsh.ks * xsh.g;
+        const int64_t rows_per_block = (int64_t)xsh.g * xsh.r;
+        blocks = (n_out + rows_per_block - 1) / rows_per_block;
+        lds = (size_t)n_in * 4;
+    } else if (nch64 > 0 && bt == 1) {
         // 4 rows per wave (a Q4_K chunk costs ~50 VALU operations, so fewer
         // rows per wave than Q8_0; measured best of 2, 4 and 8 on the 8192x3072
         // and 3072x8192 shapes), halved while the grid would hold fewer than
@@ -435,7 +530,7 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
         const int64_t rows_per_wave = 64 >> lpr_log2;
         blocks = ((n_out + rows_per_wave - 1) / rows_per_wave + 3) / 4;
     }
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), lds, s, a);
     count_launch();
     return hipGetLastError();
 }

@@ -192,6 +192,40 @@ def test_q4k_gemv(qd, n_out, n_in, batch):
     check_f32(out, ref, S, f"q4k {n_out}x{n_in} b{batch}")
 
 
+# One batch row with x staged in LDS: every width case of the shape table
+# (whole rows per wave up to 4096 columns, K split over waves beyond), ragged
+# row counts that leave the last workgroup partly empty, and both row counts
+# per wave.
+XL_SHAPES = [(13, 1024), (5, 2048), (29, 3072), (7, 4096), (9, 6144), (100, 8192), (11, 12288), (2051, 8192)]
+
+
+@pytest.mark.parametrize("n_out,n_in", XL_SHAPES)
+def test_one_row_lds_x_shapes(qd, n_out, n_in):
+    x = synth.normal_f32(6100 + n_in, (1, n_in))
+    raw8 = q8_weights(6101 + n_in, n_out, n_in)
+    out = host(qd.q8_0_gemv(dev(raw8), n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(raw8, n_in, n_out, x)
+    check_f32(out, ref, S, f"q8_0 {n_out}x{n_in}")
+    r = synth.normal_f32(6102 + n_in, (1, n_out))
+    out = host(qd.q8_0_gemv_residual(dev(raw8), n_in, n_out, dev(x), dev(r)))
+    ref, S = oracle.q8_0_gemv_residual(raw8, n_in, n_out, x, r)
+    check_f32(out, ref, S, f"q8_0 residual {n_out}x{n_in}")
+    raw4 = synth.q4k_weights(6103 + n_in, n_out, n_in)
+    out = host(qd.q4k_gemv(dev(raw4), n_in, n_out, dev(x)))
+    ref, S = oracle.q4k_gemv(raw4, n_in, n_out, x)
+    check_f32(out, ref, S, f"q4k {n_out}x{n_in}")
+
+
+@pytest.mark.parametrize("n_in,n_q,n_kv", [(1024, 40, 8), (4096, 48, 16), (8192, 64, 32)])
+def test_one_row_lds_x_qkv(qd, n_in, n_q, n_kv):
+    wq, wk, wv = (q8_weights(6110 + i, n, n_in) for i, n in enumerate((n_q, n_kv, n_kv)))
+    x = synth.normal_f32(6113, (1, n_in))
+    got = [host(t) for t in qd.q8_0_qkv(dev(wq), dev(wk), dev(wv), n_in, n_q, n_kv, dev(x))]
+    refs, ss = oracle.q8_0_qkv(wq, wk, wv, n_in, n_q, n_kv, x)
+    for g, ref, S, key in zip(got, refs, ss, "qkv"):
+        check_f32(g, ref, S, f"qkv {key} {n_in}")
+
+
 # --------------------------------------------------------- batched GEMM --
 
 @pytest.mark.parametrize("n_out,n_in,batch", [(16, 32, 1), (130, 96, 3), (256, 512, 128),
