@@ -22,8 +22,8 @@
 // every q chunk, then the arithmetic, so the loads return in use order while
 // later ones are still in flight.  One batch row: x is copied once per
 // workgroup into LDS (direct global->LDS loads issued before the weight
-// loads) and shared by several row groups, and a wave takes two rows whole or
-// split over few waves; with a folded RMSNorm or SwiGLU x stays in registers,
+// loads) and shared by several row groups, and a wave takes one or two rows
+// whole or split over few waves; with a folded RMSNorm x stays in registers,
 // one chunk column per wave and one row group per workgroup, which keeps the
 // arithmetic a wave still owes after its last load short (the kernel's tail).
 // A residual is fetched by the storing lanes before the weight stream.  The scalar set-up
@@ -612,6 +612,19 @@ KernelFn pick_b1_xl_g(const B1XlShape& sh)
     return sh.g == 8 ? q8_0_gemv_fast<MODE, 1, 1, CH, 1, true, 8> : q8_0_gemv_fast<MODE, 1, 1, CH, 1, true, 4>;
 }
 
+// SwiGLU (gate and up rows per output row): whole rows only, 4 row groups
+// (2x8192x3072: 10.6-11.2 -> 10.1 us; 8 groups 10.2, 2 rows per wave 10.6).
+KernelFn pick_b1_xl_swiglu(const B1XlShape& sh, int nch64)
+{
+    switch (nch64) {
+        case 1: return pick_b1_xl_g<kSwiGLU, 1>(sh);
+        case 2: return pick_b1_xl_g<kSwiGLU, 2>(sh);
+        case 3: return pick_b1_xl_g<kSwiGLU, 3>(sh);
+        case 4: return pick_b1_xl_g<kSwiGLU, 4>(sh);
+        default: return nullptr;
+    }
+}
+
 template <int MODE>
 KernelFn pick_b1_xl(const B1XlShape& sh, int nch64)
 {
@@ -666,12 +679,14 @@ hipError_t launch_q8_0_gemv(const Q8GemvProblem& p, hipStream_t s)
     int64_t blocks = 0;
     int threads = 256;
     bool xl = false;
-    const B1XlShape xsh = b1_xl_shape(nch64, a.total_rows);
-    if (bt == 1 && xsh.ks > 0 && p.mode != kSwiGLU && !p.norm_w && a.n_in * 4 <= kXldsMax) {
+    B1XlShape xsh = b1_xl_shape(nch64, a.total_rows);
+    if (p.mode == kSwiGLU) xsh = xsh.ks == 1 ? B1XlShape{1, xsh.ch, 4, 1} : B1XlShape{0, 0, 0, 0};
+    if (bt == 1 && xsh.ks > 0 && !p.norm_w && a.n_in * 4 <= kXldsMax) {
         switch (p.mode) {
             case kPlain: fn = pick_b1_xl<kPlain>(xsh, nch64); break;
             case kResidual: fn = pick_b1_xl<kResidual>(xsh, nch64); break;
-            default: fn = pick_b1_xl<kQKV>(xsh, nch64); break;
+            case kQKV: fn = pick_b1_xl<kQKV>(xsh, nch64); break;
+            default: fn = pick_b1_xl_swiglu(xsh, nch64); break;
         }
         threads = 64 * xsh.ks * xsh.g;
         const int64_t rows_per_block = (int64_t)xsh.g * xsh.r;

@@ -193,7 +193,8 @@ def test_q4k_gemv(qd, n_out, n_in, batch):
 
 
 # One batch row with x staged in LDS: every width case of the shape table
-# (whole rows per wave up to 4096 columns, K split over waves beyond), ragged
+# (whole rows per wave up to 4096 columns, K split over waves beyond; SwiGLU
+# and Q4_K take it up to 4096 columns, the register shapes beyond), ragged
 # row counts that leave the last workgroup partly empty, and both row counts
 # per wave.
 XL_SHAPES = [(13, 1024), (5, 2048), (29, 3072), (7, 4096), (9, 6144), (100, 8192), (11, 12288), (2051, 8192)]
@@ -214,6 +215,11 @@ def test_one_row_lds_x_shapes(qd, n_out, n_in):
     out = host(qd.q4k_gemv(dev(raw4), n_in, n_out, dev(x)))
     ref, S = oracle.q4k_gemv(raw4, n_in, n_out, x)
     check_f32(out, ref, S, f"q4k {n_out}x{n_in}")
+    wu = q8_weights(6104 + n_in, n_out, n_in)
+    out = host(qd.q8_0_swiglu(dev(raw8), dev(wu), n_in, n_out, dev(x)))
+    r = oracle.q8_0_swiglu(raw8, wu, n_in, n_out, x)
+    err = np.abs(out.astype(np.float64) - r["out"])
+    assert np.all(err <= swiglu_tol(r)), f"swiglu {n_out}x{n_in}: worst err/tol {np.max(err / swiglu_tol(r)):.3g}"
 
 
 @pytest.mark.parametrize("n_in,n_q,n_kv", [(1024, 40, 8), (4096, 48, 16), (8192, 64, 32)])
