@@ -72,22 +72,56 @@ __device__ inline float block_reduce(float v, float* red, bool is_max)
     return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// The same reduction for NG values at once (one pair of barriers for all the
+// query heads of a group); red holds 4 x kMaxGroup floats.  Per value the
+// order of operations is that of block_reduce.
+template <int NG>
+__device__ inline void block_reduce_n(float (&v)[NG], float* red, bool is_max)
+{
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float o = __shfl_xor(v[g], off);
+            v[g] = is_max ? fmaxf(v[g], o) : v[g] + o;
+        }
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) red[w * kMaxGroup + g] = v[g];
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const float r0 = red[g], r1 = red[kMaxGroup + g], r2 = red[2 * kMaxGroup + g], r3 = red[3 * kMaxGroup + g];
+        v[g] = is_max ? fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)) : (r0 + r1) + (r2 + r3);
+    }
+}
+
 // Partial attention of one (chunk, kv head).  part layout per (kv, chunk, g):
 // [max, sum, o[0..D)].  FINAL (a single chunk): out = o / sum directly.
 // Scores: position p = tid / 2 of the chunk, half (tid & 1) of the d columns
 // per thread, the halves added across the lane pair.  Weighted sum: wave w
 // takes positions w, w+4, ...; lane l takes columns D/64 * l ..; the four
-// wave partials meet in LDS.
-template <int D, bool FINAL>
+// wave partials meet in LDS.  G > 0: the group size (query heads per kv
+// head) is fixed at compile time, so every loop over the heads unrolls without
+// branches and the LDS reads of a step issue together; G = 0 takes it from
+// `group` (any size up to kMaxGroup), with a branch per head and step (at 24
+// query / 8 kv heads that form measured 18.6 us at 1024 positions, bound by
+// the serialised LDS round trips of its four waves).
+template <int D, bool FINAL, int G>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_cache,
-                                                         const float* __restrict__ v_cache, int64_t n_kv, int group,
+                                                         const float* __restrict__ v_cache, int64_t n_kv, int group_rt,
                                                          int64_t n_ctx, int64_t max_seq, float scale,
                                                          float* __restrict__ part, float* __restrict__ out)
 {
     constexpr int HALF = D / 2, CPL = D / 64;     // columns per lane in the weighted sum
+    constexpr int GM = G > 0 ? G : kMaxGroup;     // unrolled head loops
+    const int group = G > 0 ? G : group_rt;
     __shared__ __attribute__((aligned(16))) float qs[kMaxGroup * D];
     __shared__ float ps[kMaxGroup][kAttnChunk];
     __shared__ float red[4];
+    __shared__ float redn[4 * kMaxGroup];
     __shared__ float mx[kMaxGroup], sm[kMaxGroup];
     __shared__ float ow[4][kMaxGroup][D];
     const int64_t chunk = blockIdx.x, kv = blockIdx.y;
@@ -125,16 +159,16 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
 #pragma unroll
         for (int j4 = 0; j4 < HALF / 4; ++j4) kr[j4] = krow[j4];
     }
-    float s[kMaxGroup];
+    float s[GM];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) s[g] = 0.0f;
+    for (int g = 0; g < GM; ++g) s[g] = 0.0f;
     {
 #pragma unroll
         for (int j4 = 0; j4 < HALF / 4; ++j4) {
             const float4 kk = kr[j4];
 #pragma unroll
-            for (int g = 0; g < kMaxGroup; ++g) {
-                if (g < group) {
+            for (int g = 0; g < GM; ++g) {
+                if (G > 0 || g < group) {
                     const float4 qq = *reinterpret_cast<const float4*>(&qs[g * D + half * HALF + 4 * j4]);
                     s[g] = __builtin_fmaf(qq.x, kk.x, s[g]);
                     s[g] = __builtin_fmaf(qq.y, kk.y, s[g]);
@@ -144,33 +178,58 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
             }
         }
     }
-    for (int g = 0; g < group; ++g) {
-        const float full = s[g] + __shfl_xor(s[g], 1);
-        const float sc = valid ? full * scale : -INFINITY;
-        const float m = block_reduce(sc, red, true);
-        const float p = valid ? expf(sc - m) : 0.0f;
-        const float l = block_reduce(half == 0 ? p : 0.0f, red, false);
-        if (half == 0) ps[g][pl] = p;
-        if (tid == 0) {
-            mx[g] = m;
-            sm[g] = l;
+    if constexpr (G > 0) {
+        float sc[G], m[G], l[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float full = s[g] + __shfl_xor(s[g], 1);
+            sc[g] = valid ? full * scale : -INFINITY;
+            m[g] = sc[g];
+        }
+        block_reduce_n<G>(m, redn, true);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            sc[g] = valid ? expf(sc[g] - m[g]) : 0.0f;   // the weight p
+            l[g] = half == 0 ? sc[g] : 0.0f;
+        }
+        block_reduce_n<G>(l, redn, false);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (half == 0) ps[g][pl] = sc[g];
+            if (tid == 0) {
+                mx[g] = m[g];
+                sm[g] = l[g];
+            }
+        }
+    } else {
+        for (int g = 0; g < group; ++g) {
+            const float full = s[g] + __shfl_xor(s[g], 1);
+            const float sc = valid ? full * scale : -INFINITY;
+            const float m = block_reduce(sc, red, true);
+            const float p = valid ? expf(sc - m) : 0.0f;
+            const float l = block_reduce(half == 0 ? p : 0.0f, red, false);
+            if (half == 0) ps[g][pl] = p;
+            if (tid == 0) {
+                mx[g] = m;
+                sm[g] = l;
+            }
         }
     }
     __syncthreads();
 
     // weighted sum of V over this wave's positions (rows already in registers;
     // positions past tn have weight 0)
-    float o[kMaxGroup][CPL];
+    float o[GM][CPL];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g)
+    for (int g = 0; g < GM; ++g)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) o[g][c] = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
         const int tt = wave + 4 * i;
 #pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g) {
-            if (g < group) {
+        for (int g = 0; g < GM; ++g) {
+            if (G > 0 || g < group) {
                 const float p = tt < tn ? ps[g][tt] : 0.0f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) o[g][c] = __builtin_fmaf(p, vr[i][c], o[g][c]);
@@ -178,8 +237,8 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
         }
     }
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g)
-        if (g < group)
+    for (int g = 0; g < GM; ++g)
+        if (G > 0 || g < group)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) ow[wave][g][CPL * lane + c] = o[g][c];
     __syncthreads();
@@ -239,6 +298,25 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     out[h * D + j] = o / l;
 }
 
+using ChunkFn = void (*)(const float*, const float*, const float*, int64_t, int, int64_t, int64_t, float, float*,
+                        float*);
+
+// Compile-time group sizes for the usual GQA ratios; others take the generic
+// kernel.
+template <int D, bool FINAL>
+ChunkFn pick_chunk(int group)
+{
+    switch (group) {
+        case 1: return attn_chunk_kernel<D, FINAL, 1>;
+        case 2: return attn_chunk_kernel<D, FINAL, 2>;
+        case 3: return attn_chunk_kernel<D, FINAL, 3>;
+        case 4: return attn_chunk_kernel<D, FINAL, 4>;
+        case 6: return attn_chunk_kernel<D, FINAL, 6>;
+        case 8: return attn_chunk_kernel<D, FINAL, 8>;
+        default: return attn_chunk_kernel<D, FINAL, 0>;
+    }
+}
+
 }  // namespace
 
 int64_t attention_workspace_bytes(int64_t n_head, int64_t head_dim, int64_t n_ctx)
@@ -264,27 +342,18 @@ hipError_t launch_attention(const float* q, const float* k_cache, const float* v
     const int64_t nchunks = (n_ctx + kAttnChunk - 1) / kAttnChunk;
     const dim3 grid((unsigned)nchunks, (unsigned)n_kv);
     float* part = static_cast<float*>(workspace);
-    if (nchunks == 1) {
-        if (d == 64)
-            hipLaunchKernelGGL((attn_chunk_kernel<64, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
-                               n_ctx, max_seq, scale, part, out);
-        else
-            hipLaunchKernelGGL((attn_chunk_kernel<128, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
-                               n_ctx, max_seq, scale, part, out);
-        count_launch();
-        return hipGetLastError();
-    }
-    if (d == 64) {
-        hipLaunchKernelGGL((attn_chunk_kernel<64, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
-                           n_ctx, max_seq, scale, part, out);
+    const bool final = nchunks == 1;
+    const ChunkFn fn = d == 64 ? (final ? pick_chunk<64, true>(group) : pick_chunk<64, false>(group))
+                               : (final ? pick_chunk<128, true>(group) : pick_chunk<128, false>(group));
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group, n_ctx, max_seq, scale, part, out);
+    count_launch();
+    if (final) return hipGetLastError();
+    if (d == 64)
         hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((unsigned)n_head), dim3(64), 0, s, part, nchunks, group, out);
-    } else {
-        hipLaunchKernelGGL((attn_chunk_kernel<128, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group,
-                           n_ctx, max_seq, scale, part, out);
+    else
         hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((unsigned)n_head), dim3(128), 0, s, part, nchunks, group,
                            out);
-    }
-    count_launch(2);
+    count_launch();
     return hipGetLastError();
 }
 
