@@ -459,17 +459,21 @@ __global__ __launch_bounds__(256) void gemm_q8_pipe(PipeArgs a)
 #undef QDEC_PICK
 
 // The pipelined kernel holds 124 KB of LDS, so one workgroup per CU: its grid
-// should be whole rounds of 256 workgroups.  K splits (<= 4, slices >= 512
-// deep and multiples of 64) bring small grids up to 256, but each split adds
-// M*N f32 atomics (4M cost ~12 us), so the split grid is taken only up to 4M
-// atomics.  Measured: 128x8192x3072 split 4: 32.0 us (36.1 unpipelined);
-// 512x8192x3072: 52.7 us (74.5); 512x3072x8192 split 4 (6.3M atomics, 1.5
-// rounds): 84 us against 70.5 unpipelined, so not taken.
+// should be whole rounds of 256 workgroups.  K splits (slices >= 512 deep and
+// multiples of 64) bring small grids up, but each split adds M*N f32 atomics
+// (4M cost ~12 us), so the split grid is taken only up to 4M atomics.  Up to 4
+// splits the grid must reach 256 workgroups; the 8-way split is also taken at
+// 192 (three quarters of a round, one workgroup per CU).  Measured:
+// 128x8192x3072 split 4: 32.0 us (36.1 unpipelined); 512x8192x3072: 52.7 us
+// (74.5); 128x3072x8192 split 8 (192 workgroups, 3.1M atomics): 30.1 us
+// against 36.3 unpipelined; 512x3072x8192 split 4 (6.3M atomics, 1.5
+// rounds): 84 us against 70.5 unpipelined, and split 2 (192 workgroups):
+// 72.3, so neither is taken.
 int pipe_splits(int64_t M, int64_t N, int64_t K)
 {
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     int s = 1;
-    while (s < 4 && tiles * s < 256 && K % (64 * 2 * s) == 0 && K / (2 * s) >= 512) s *= 2;
+    while (s < 8 && tiles * s < 256 && K % (64 * 2 * s) == 0 && K / (2 * s) >= 512) s *= 2;
     return s;
 }
 
@@ -480,7 +484,7 @@ bool pipe_ok(int64_t M, int64_t N, int64_t K)
     const int s = pipe_splits(M, N, K);
     const int64_t wg = tiles * s;
     const int64_t rounds = (wg + 255) / 256;
-    const bool full = wg >= 256 && 4 * wg >= 3 * rounds * 256;     // >= 75% of the last round busy
+    const bool full = (wg >= 256 || (s == 8 && wg >= 192)) && 4 * wg >= 3 * rounds * 256;   // >= 75% of the last round busy
     return full && (s == 1 || M * N * s <= (int64_t)1 << 22);
 }
 

@@ -340,7 +340,8 @@ def test_launch_counter_witness(qd):
 # 4 K splits, n_in % 64 == 0, n_out % 8 == 0): x rounded to bf16 in the stream
 # workspace, then the kernel (2 launches), plus the zero fill when K is split.
 @pytest.mark.parametrize("n_out,n_in,batch,launches", [(2048, 256, 2048, 2), (2040, 192, 2000, 2),
-                                                       (4096, 64, 1000, 2), (2048, 2048, 512, 3)])
+                                                       (4096, 64, 1000, 2), (2048, 2048, 512, 3),
+                                                       (3072, 4096, 128, 3)])   # 24 tiles, 8-way split
 def test_q8_0_gemm_pipelined(qd, n_out, n_in, batch, launches):
     raw = q8_weights(7100 + n_in, n_out, n_in)
     x = synth.normal_f32(7101 + batch, (batch, n_in))
