@@ -47,9 +47,11 @@
  *     complete, for every weight before capturing.
  *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in of
  *     1024..8192 in the supported steps) splits x, q8_0_gemv_topk keeps its
- *     candidate lists, and q8_0_gemm_batched (at >= 256 output tiles of
- *     128 x 128, n_in % 64 == 0, n_out % 8 == 0) rounds x to bf16, in a
- *     library-owned device buffer, one per
+ *     candidate lists, and q8_0_gemm_batched (on its pipelined path:
+ *     n_in % 64 == 0, n_out % 8 == 0, output tiles of 128 x 128 that fill
+ *     the chip, if need be with K split over up to 8 slices) rounds x to bf16
+ *     and keeps the slices' partial products, in a library-owned device
+ *     buffer, one per
  *     (device, stream), made (or grown) on the first such call on that stream
  *     and freed by qdec_clear_cache.  Calls on one stream share it in
  *     stream order; calls on different streams never share one.  A stream

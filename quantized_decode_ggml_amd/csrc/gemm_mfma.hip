@@ -264,7 +264,8 @@ struct PipeArgs {
     float* out;            // M x N
     int64_t M, N, K, ntiles;
     int64_t kslice;        // K per split (multiple of 64)
-    int splits;            // > 1: partial tiles are added into a zeroed out
+    int splits;            // > 1: slice s writes its partial tiles to part[s][M][N]
+    float* part;           // splits * M * N f32 (workspace), summed by sum_slices
 };
 
 __global__ __launch_bounds__(256) void x_to_bf16(const float4* __restrict__ x, bf16x4* __restrict__ xb, int64_t n4)
@@ -449,9 +450,31 @@ __global__ __launch_bounds__(256) void gemm_q8_pipe(PipeArgs a)
                 const int64_t m = m0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + e;
                 if (m >= a.M) continue;
                 if (a.splits == 1) a.out[m * a.N + n] = acc[i][j][e];
-                else unsafeAtomicAdd(a.out + m * a.N + n, acc[i][j][e]);
+                else a.part[(slice * a.M + m) * a.N + n] = acc[i][j][e];
             }
         }
+    }
+}
+
+// out = sum over the K slices of their partial products, slice 0 first (a
+// fixed order: the split result is reproducible, unlike atomic adds).
+__global__ __launch_bounds__(256) void sum_slices(const float* __restrict__ part, int splits, int64_t mn,
+                                                  float* __restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = mn / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 t = reinterpret_cast<const float4*>(part)[i];
+        for (int sl = 1; sl < splits; ++sl) {
+            const float4 u = reinterpret_cast<const float4*>(part + sl * mn)[i];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        }
+        reinterpret_cast<float4*>(out)[i] = t;
+    }
+    for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
+        float t = part[i];
+        for (int sl = 1; sl < splits; ++sl) t += part[sl * mn + i];
+        out[i] = t;
     }
 }
 
@@ -460,8 +483,9 @@ __global__ __launch_bounds__(256) void gemm_q8_pipe(PipeArgs a)
 
 // The pipelined kernel holds 124 KB of LDS, so one workgroup per CU: its grid
 // should be whole rounds of 256 workgroups.  K splits (slices >= 512 deep and
-// multiples of 64) bring small grids up, but each split adds M*N f32 atomics
-// (4M cost ~12 us), so the split grid is taken only up to 4M atomics.  Up to 4
+// multiples of 64) bring small grids up; each slice writes its M*N partial
+// products to the workspace and a small kernel sums them (f32 atomics into a
+// zeroed output cost ~12 us per 4M), up to 4M partial values.  Up to 4
 // splits the grid must reach 256 workgroups; the 8-way split is also taken at
 // 192 (three quarters of a round, one workgroup per CU).  Measured:
 // 128x8192x3072 split 4: 32.0 us (36.1 unpipelined); 512x8192x3072: 52.7 us
@@ -538,9 +562,14 @@ hipError_t launch(GemmArgs& a, bool quant, hipStream_t s)
 
 }  // namespace
 
+// x rounded to bf16, then (with a K split) the slices' partial products.
+static int64_t pipe_x_bytes(int64_t n_in, int64_t batch) { return align_up(batch * n_in * 2, kAlign); }
+
 int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
 {
-    return pipe_ok(batch, n_out, n_in) ? batch * n_in * 2 : 0;
+    if (!pipe_ok(batch, n_out, n_in)) return 0;
+    const int s = pipe_splits(batch, n_out, n_in);
+    return pipe_x_bytes(n_in, batch) + (s > 1 ? (int64_t)s * batch * n_out * 4 : 0);
 }
 
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
@@ -564,18 +593,18 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
         p.ntiles = (n_out + 127) / 128;
         p.splits = pipe_splits(batch, n_out, n_in);
         p.kslice = n_in / p.splits;
-        if (p.splits > 1) {
-            const int64_t n = batch * n_out, q4 = n / 4;
-            int64_t zb = (q4 + 255) / 256;
-            if (zb > 2048) zb = 2048;
-            if (zb < 1) zb = 1;
-            hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, s, reinterpret_cast<float4*>(out), q4,
-                               out + q4 * 4, n - q4 * 4);
-            count_launch();
-        }
+        p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pipe_x_bytes(n_in, batch));
         const int64_t grid = ((batch + 127) / 128) * p.ntiles * p.splits;
         hipLaunchKernelGGL(gemm_q8_pipe, dim3((unsigned)grid), dim3(256), 0, s, p);
         count_launch();
+        if (p.splits > 1) {
+            const int64_t mn = batch * n_out;
+            int64_t sb = (mn / 4 + 255) / 256;
+            if (sb > 2048) sb = 2048;
+            if (sb < 1) sb = 1;
+            hipLaunchKernelGGL(sum_slices, dim3((unsigned)sb), dim3(256), 0, s, p.part, p.splits, mn, out);
+            count_launch();
+        }
         return hipGetLastError();
     }
     GemmArgs a = plan(batch, n_out, n_in);
