@@ -50,8 +50,8 @@
  *     candidate lists, and q8_0_gemm_batched (on its pipelined path:
  *     n_in % 64 == 0, n_out % 8 == 0, output tiles of 128 x 128 that fill
  *     the chip, if need be with K split over up to 8 slices) rounds x to bf16
- *     and keeps the slices' partial products, in a library-owned device
- *     buffer, one per
+ *     and keeps the slices' partial products (as do both batched GEMMs on
+ *     their other K-split shapes), in a library-owned device buffer, one per
  *     (device, stream), made (or grown) on the first such call on that stream
  *     and freed by qdec_clear_cache.  Calls on one stream share it in
  *     stream order; calls on different streams never share one.  A stream

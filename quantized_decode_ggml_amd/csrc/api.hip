@@ -602,8 +602,9 @@ int q8_0_gemm_batched(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
     if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4)) return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
     const void* buf = nullptr;
     QDEC_TRY(repacked(w, QDEC_TYPE_Q8_0, n_in, n_out, stream, &buf));
-    // the pipelined kernel rounds x to bf16 in the stream's workspace; a
-    // capture on a stream without one runs the register-staged kernel
+    // the pipelined kernel rounds x to bf16 in the stream's workspace, the
+    // register-staged one keeps its K-slice partials there; a capture on a
+    // stream without one runs the register-staged kernel with atomics
     void* wsp = nullptr;
     const int64_t need = q8_gemm_workspace_bytes(n_in, n_out, batch);
     if (need > 0) QDEC_TRY(stream_workspace(stream, need, &wsp));
@@ -621,7 +622,12 @@ int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
     if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4) ||
         overlaps(out, batch * n_out * 4, w, n_out * n_in * 4))
         return fail(QDEC_EINVAL, "%s: out overlaps an input", fn);
-    return finish(launch_f32_gemm(w, n_in, n_out, batch, x, out, stream), fn);
+    // K-split partial products go to the stream's workspace; a capture on a
+    // stream without one adds them with atomics instead
+    void* wsp = nullptr;
+    const int64_t need = f32_gemm_workspace_bytes(n_in, n_out, batch);
+    if (need > 0) QDEC_TRY(stream_workspace(stream, need, &wsp));
+    return finish(launch_f32_gemm(w, n_in, n_out, batch, x, out, wsp, stream), fn);
 }
 
 int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream)

@@ -53,6 +53,7 @@ struct GemmArgs {
     int64_t mtiles, ntiles;
     int64_t kslice;        // K per split (multiple of BK)
     int splits;
+    float* part;           // splits > 1: slice s writes part[s][M][N] (workspace), or null: atomics into a zeroed out
 };
 
 __device__ inline float fp16_bits_to_f32(uint16_t h)
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
                 const int64_t m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
                 if (m >= a.M) continue;
                 if (a.splits == 1) a.out[m * a.N + n] = acc[i][j][e];
+                else if (a.part) a.part[(slice * a.M + m) * a.N + n] = acc[i][j][e];
                 else unsafeAtomicAdd(a.out + m * a.N + n, acc[i][j][e]);
             }
         }
@@ -542,7 +544,7 @@ GemmArgs plan(int64_t M, int64_t N, int64_t K)
 
 hipError_t launch(GemmArgs& a, bool quant, hipStream_t s)
 {
-    if (a.splits > 1) {
+    if (a.splits > 1 && !a.part) {
         const int64_t n = a.M * a.N;
         const int64_t n4 = n / 4;
         const int64_t ntail = n - n4 * 4;
@@ -557,7 +559,22 @@ hipError_t launch(GemmArgs& a, bool quant, hipStream_t s)
     if (quant) hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, dim3(256), 0, s, a);
     count_launch();
+    if (a.splits > 1 && a.part) {
+        const int64_t mn = a.M * a.N;
+        int64_t sb = (mn / 4 + 255) / 256;
+        if (sb > 2048) sb = 2048;
+        if (sb < 1) sb = 1;
+        hipLaunchKernelGGL(sum_slices, dim3((unsigned)sb), dim3(256), 0, s, a.part, a.splits, mn, a.out);
+        count_launch();
+    }
     return hipGetLastError();
+}
+
+// Register-staged path: the slices' partial products (none without a K split).
+int64_t reg_part_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const GemmArgs a = plan(M, N, K);
+    return a.splits > 1 ? (int64_t)a.splits * M * N * 4 : 0;
 }
 
 }  // namespace
@@ -567,9 +584,14 @@ static int64_t pipe_x_bytes(int64_t n_in, int64_t batch) { return align_up(batch
 
 int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
 {
-    if (!pipe_ok(batch, n_out, n_in)) return 0;
+    if (!pipe_ok(batch, n_out, n_in)) return reg_part_bytes(batch, n_out, n_in);
     const int s = pipe_splits(batch, n_out, n_in);
     return pipe_x_bytes(n_in, batch) + (s > 1 ? (int64_t)s * batch * n_out * 4 : 0);
+}
+
+int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
+{
+    return reg_part_bytes(batch, n_out, n_in);
 }
 
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
@@ -612,16 +634,20 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
     a.q = w.q;
     a.d = w.d;
     a.out = out;
+    // a workspace given for a shape off the pipelined path holds the slices'
+    // partial products (q8_gemm_workspace_bytes sized it)
+    a.part = workspace && a.splits > 1 && !pipe_ok(batch, n_out, n_in) ? static_cast<float*>(workspace) : nullptr;
     return launch(a, true, s);
 }
 
 hipError_t launch_f32_gemm(const float* wf, int64_t n_in, int64_t n_out, int64_t batch,
-                           const float* x, float* out, hipStream_t s)
+                           const float* x, float* out, void* workspace, hipStream_t s)
 {
     GemmArgs a = plan(batch, n_out, n_in);
     a.x = x;
     a.wf = wf;
     a.out = out;
+    a.part = workspace && a.splits > 1 ? static_cast<float*>(workspace) : nullptr;
     return launch(a, false, s);
 }
 

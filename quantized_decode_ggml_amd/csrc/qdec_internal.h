@@ -190,15 +190,21 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
 hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                            float* out, hipStream_t s);
 
-// Batched GEMM over a Q8_0 copy.  With a workspace of q8_gemm_workspace_bytes
-// (non-zero only for shapes the pipelined kernel takes) x is first rounded to
-// bf16 there and the DMA-fed kernel runs; without one the register-staged
-// kernel runs (same arithmetic, same results).
+// Batched GEMM over a Q8_0 copy.  With a workspace of q8_gemm_workspace_bytes,
+// on shapes the pipelined kernel takes x is first rounded to bf16 there and the
+// DMA-fed kernel runs; on the others the register-staged kernel keeps the
+// partial products of its K slices there and a small kernel sums them in slice
+// order.  Without a workspace the register-staged kernel runs and adds its K
+// slices with f32 atomics into a zeroed output (same products, summation order
+// not fixed).
 int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch);
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                             float* out, void* workspace, hipStream_t s);
+// Dense f32 weights: the register-staged kernel, with the K-slice partials in
+// a workspace of f32_gemm_workspace_bytes when there is one, as above.
+int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch);
 hipError_t launch_f32_gemm(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
-                           const float* x, float* out, hipStream_t s);
+                           const float* x, float* out, void* workspace, hipStream_t s);
 
 // Top-k of batch rows of n_out logits (1 <= k <= 256): the workspace holds two
 // candidate buffers of batch * ceil(n_out / 4096) * k 64-bit keys (none for
