@@ -56,8 +56,9 @@
  *     and freed by qdec_clear_cache.  Calls on one stream share it in
  *     stream order; calls on different streams never share one.  A stream
  *     capture cannot allocate it, so a capture on a stream that has none takes
- *     the VALU kernels (same results to the f32 tolerance), or for the GEMM the
- *     register-staged kernel (same arithmetic).
+ *     the VALU kernels (same results to the f32 tolerance), or for the GEMMs
+ *     the register-staged kernel with its K slices added by f32 atomics (same
+ *     products; the order of the slice sums, and so the last bits, can vary).
  *   - Return value: QDEC_OK (0) or a negative qdec_status.  Invalid arguments
  *     are rejected with QDEC_EINVAL before any HIP call; a failed allocation
  *     returns QDEC_ENOMEM; a failed launch or HIP call returns QDEC_EHIP.
