@@ -132,6 +132,8 @@ def suite(args):
         Warm-up and capture use one dedicated stream, so per-stream library
         state (the batched GEMV workspace) exists before the capture starts."""
         nonlocal stream
+        if args.only and not name.startswith(args.only):
+            return                      # --only: this line is not wanted (its inputs were still made)
         n = len(launches)
         cs = torch.cuda.Stream()
         cs.wait_stream(torch.cuda.current_stream())
@@ -336,6 +338,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true",
                     help="time every workload configuration (one JSON line each) instead of the step")
+    ap.add_argument("--only", default="",
+                    help="with --suite: time only the workloads whose name starts with this prefix (e.g. 'c3')")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 64 MiB device copy (untimed), the known-size reference that "
                          "scales the profiler's HBM byte counters")
