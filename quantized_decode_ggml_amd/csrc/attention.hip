@@ -11,11 +11,12 @@
 //   output : softmax over t < n_ctx of scale * (q_h . K[t]), times V.
 //
 // Attention is HBM-bound on the cache (2 * n_ctx * n_kv * d * 4 bytes per
-// token), so each workgroup takes one kv head and a chunk of 128 positions
-// (flash-decoding split): the G = n_head / n_kv query heads of the group share
-// every K and V row it reads.  A pair of threads owns a position for the
-// scores (half a K row each, streamed as float4, the G query vectors broadcast
-// from LDS), the chunk's max and sum come from a wave/LDS reduction, the
+// token), so each workgroup takes one kv head and a chunk of CH = 128 (or,
+// up to 2048 positions, 64) positions (flash-decoding split): the G =
+// n_head / n_kv query heads of the group share every K and V row it reads.
+// 256 / CH threads own a position for the scores (a segment of the K row
+// each, streamed as float4, the G query vectors broadcast from LDS), the
+// chunk's max and sum come from a wave/LDS reduction, the
 // weights go to LDS, and each wave then sums p_t V[t] over a quarter of the
 // positions with its lanes across the columns (coalesced V rows), the four
 // wave partials meeting in LDS.  Each chunk leaves (max, sum, unnormalised
@@ -27,7 +28,10 @@ namespace qdec {
 
 namespace {
 
-constexpr int kAttnChunk = 128;   // positions per workgroup (two threads each for the scores)
+// Positions per workgroup: 128 (two threads per position for the scores), or
+// 64 (four threads per position) up to 2048 positions, so that short
+// contexts still spread over more compute units.
+inline int attn_chunk(int64_t n_ctx) { return n_ctx <= 2048 ? 64 : 128; }
 constexpr int kMaxGroup = 16;     // query heads per kv head
 
 __global__ __launch_bounds__(64) void rope_append_kernel(float* q, float* k, const float* v, int64_t n_head,
@@ -100,8 +104,9 @@ __device__ inline void block_reduce_n(float (&v)[NG], float* red, bool is_max)
 
 // Partial attention of one (chunk, kv head).  part layout per (kv, chunk, g):
 // [max, sum, o[0..D)].  FINAL (a single chunk): out = o / sum directly.
-// Scores: position p = tid / 2 of the chunk, half (tid & 1) of the d columns
-// per thread, the halves added across the lane pair.  Weighted sum: wave w
+// Scores: position p = tid / TPP of the chunk, segment tid % TPP of the d
+// columns per thread, the segments added across the TPP neighbouring lanes
+// (TPP = 256 / CH threads per position).  Weighted sum: wave w
 // takes positions w, w+4, ...; lane l takes columns D/64 * l ..; the four
 // wave partials meet in LDS.  G > 0: the group size (query heads per kv
 // head) is fixed at compile time, so every loop over the heads unrolls without
@@ -109,17 +114,18 @@ __device__ inline void block_reduce_n(float (&v)[NG], float* red, bool is_max)
 // `group` (any size up to kMaxGroup), with a branch per head and step (at 24
 // query / 8 kv heads that form measured 18.6 us at 1024 positions, bound by
 // the serialised LDS round trips of its four waves).
-template <int D, bool FINAL, int G>
+template <int D, bool FINAL, int G, int CH>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_cache,
                                                          const float* __restrict__ v_cache, int64_t n_kv, int group_rt,
                                                          int64_t n_ctx, int64_t max_seq, float scale,
                                                          float* __restrict__ part, float* __restrict__ out)
 {
-    constexpr int HALF = D / 2, CPL = D / 64;     // columns per lane in the weighted sum
+    constexpr int TPP = 256 / CH, SEG = D / TPP;   // threads per position, d columns per thread (scores)
+    constexpr int CPL = D / 64;                    // columns per lane in the weighted sum
     constexpr int GM = G > 0 ? G : kMaxGroup;     // unrolled head loops
     const int group = G > 0 ? G : group_rt;
     __shared__ __attribute__((aligned(16))) float qs[kMaxGroup * D];
-    __shared__ float ps[kMaxGroup][kAttnChunk];
+    __shared__ float ps[kMaxGroup][CH];
     __shared__ float red[4];
     __shared__ float redn[4 * kMaxGroup];
     __shared__ float mx[kMaxGroup], sm[kMaxGroup];
@@ -130,14 +136,14 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
     for (int u = tid; u < group * D; u += 256) qs[u] = q[(kv * group) * D + u];   // heads kv*group .. +group
     __syncthreads();
 
-    const int pl = tid >> 1, half = tid & 1;
-    const int64_t t = chunk * kAttnChunk + pl;
+    const int pl = tid / TPP, seg = tid % TPP;
+    const int64_t t = chunk * CH + pl;
     const bool valid = t < n_ctx;
-    const int64_t tbase = chunk * kAttnChunk;
-    const int tn = (int)(n_ctx - tbase < kAttnChunk ? n_ctx - tbase : kAttnChunk);
+    const int64_t tbase = chunk * CH;
+    const int tn = (int)(n_ctx - tbase < CH ? n_ctx - tbase : CH);
     // every load of the workgroup is issued before any arithmetic waits on one:
-    // this wave's V rows (used after the softmax), then the thread's K half-row
-    constexpr int VPW = kAttnChunk / 4;           // positions per wave in the weighted sum
+    // this wave's V rows (used after the softmax), then the thread's K segment
+    constexpr int VPW = CH / 4;                   // positions per wave in the weighted sum
     const float* vbase = v_cache + (kv * max_seq + tbase) * D + CPL * lane;
     float vr[VPW][CPL];
 #pragma unroll
@@ -152,24 +158,24 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
             vr[i][0] = vbase[(int64_t)ts * D];
         }
     }
-    float4 kr[HALF / 4];
+    float4 kr[SEG / 4];
     {
         const int64_t tk = valid ? t : n_ctx - 1;
-        const float4* krow = reinterpret_cast<const float4*>(k_cache + (kv * max_seq + tk) * D + half * HALF);
+        const float4* krow = reinterpret_cast<const float4*>(k_cache + (kv * max_seq + tk) * D + seg * SEG);
 #pragma unroll
-        for (int j4 = 0; j4 < HALF / 4; ++j4) kr[j4] = krow[j4];
+        for (int j4 = 0; j4 < SEG / 4; ++j4) kr[j4] = krow[j4];
     }
     float s[GM];
 #pragma unroll
     for (int g = 0; g < GM; ++g) s[g] = 0.0f;
     {
 #pragma unroll
-        for (int j4 = 0; j4 < HALF / 4; ++j4) {
+        for (int j4 = 0; j4 < SEG / 4; ++j4) {
             const float4 kk = kr[j4];
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
                 if (G > 0 || g < group) {
-                    const float4 qq = *reinterpret_cast<const float4*>(&qs[g * D + half * HALF + 4 * j4]);
+                    const float4 qq = *reinterpret_cast<const float4*>(&qs[g * D + seg * SEG + 4 * j4]);
                     s[g] = __builtin_fmaf(qq.x, kk.x, s[g]);
                     s[g] = __builtin_fmaf(qq.y, kk.y, s[g]);
                     s[g] = __builtin_fmaf(qq.z, kk.z, s[g]);
@@ -182,7 +188,9 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
         float sc[G], m[G], l[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float full = s[g] + __shfl_xor(s[g], 1);
+            float full = s[g];
+#pragma unroll
+            for (int o = 1; o < TPP; o <<= 1) full += __shfl_xor(full, o);
             sc[g] = valid ? full * scale : -INFINITY;
             m[g] = sc[g];
         }
@@ -190,12 +198,12 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             sc[g] = valid ? expf(sc[g] - m[g]) : 0.0f;   // the weight p
-            l[g] = half == 0 ? sc[g] : 0.0f;
+            l[g] = seg == 0 ? sc[g] : 0.0f;
         }
         block_reduce_n<G>(l, redn, false);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            if (half == 0) ps[g][pl] = sc[g];
+            if (seg == 0) ps[g][pl] = sc[g];
             if (tid == 0) {
                 mx[g] = m[g];
                 sm[g] = l[g];
@@ -203,12 +211,14 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
         }
     } else {
         for (int g = 0; g < group; ++g) {
-            const float full = s[g] + __shfl_xor(s[g], 1);
+            float full = s[g];
+#pragma unroll
+            for (int o = 1; o < TPP; o <<= 1) full += __shfl_xor(full, o);
             const float sc = valid ? full * scale : -INFINITY;
             const float m = block_reduce(sc, red, true);
             const float p = valid ? expf(sc - m) : 0.0f;
-            const float l = block_reduce(half == 0 ? p : 0.0f, red, false);
-            if (half == 0) ps[g][pl] = p;
+            const float l = block_reduce(seg == 0 ? p : 0.0f, red, false);
+            if (seg == 0) ps[g][pl] = p;
             if (tid == 0) {
                 mx[g] = m;
                 sm[g] = l;
@@ -305,25 +315,32 @@ using ChunkFn = void (*)(const float*, const float*, const float*, int64_t, int,
 
 // Compile-time group sizes for the usual GQA ratios; others take the generic
 // kernel.
-template <int D, bool FINAL>
-ChunkFn pick_chunk(int group)
+template <int D, bool FINAL, int CH>
+ChunkFn pick_group(int group)
 {
     switch (group) {
-        case 1: return attn_chunk_kernel<D, FINAL, 1>;
-        case 2: return attn_chunk_kernel<D, FINAL, 2>;
-        case 3: return attn_chunk_kernel<D, FINAL, 3>;
-        case 4: return attn_chunk_kernel<D, FINAL, 4>;
-        case 6: return attn_chunk_kernel<D, FINAL, 6>;
-        case 8: return attn_chunk_kernel<D, FINAL, 8>;
-        default: return attn_chunk_kernel<D, FINAL, 0>;
+        case 1: return attn_chunk_kernel<D, FINAL, 1, CH>;
+        case 2: return attn_chunk_kernel<D, FINAL, 2, CH>;
+        case 3: return attn_chunk_kernel<D, FINAL, 3, CH>;
+        case 4: return attn_chunk_kernel<D, FINAL, 4, CH>;
+        case 6: return attn_chunk_kernel<D, FINAL, 6, CH>;
+        case 8: return attn_chunk_kernel<D, FINAL, 8, CH>;
+        default: return attn_chunk_kernel<D, FINAL, 0, CH>;
     }
+}
+
+template <int D, bool FINAL>
+ChunkFn pick_chunk(int group, int ch)
+{
+    return ch == 64 ? pick_group<D, FINAL, 64>(group) : pick_group<D, FINAL, 128>(group);
 }
 
 }  // namespace
 
 int64_t attention_workspace_bytes(int64_t n_head, int64_t head_dim, int64_t n_ctx)
 {
-    const int64_t nchunks = (n_ctx + kAttnChunk - 1) / kAttnChunk;
+    const int ch = attn_chunk(n_ctx);
+    const int64_t nchunks = (n_ctx + ch - 1) / ch;
     return nchunks > 1 ? n_head * nchunks * (head_dim + 2) * 4 : 0;
 }
 
@@ -341,12 +358,13 @@ hipError_t launch_attention(const float* q, const float* k_cache, const float* v
                             hipStream_t s)
 {
     const int group = (int)(n_head / n_kv);
-    const int64_t nchunks = (n_ctx + kAttnChunk - 1) / kAttnChunk;
+    const int ch = attn_chunk(n_ctx);
+    const int64_t nchunks = (n_ctx + ch - 1) / ch;
     const dim3 grid((unsigned)nchunks, (unsigned)n_kv);
     float* part = static_cast<float*>(workspace);
     const bool final = nchunks == 1;
-    const ChunkFn fn = d == 64 ? (final ? pick_chunk<64, true>(group) : pick_chunk<64, false>(group))
-                               : (final ? pick_chunk<128, true>(group) : pick_chunk<128, false>(group));
+    const ChunkFn fn = d == 64 ? (final ? pick_chunk<64, true>(group, ch) : pick_chunk<64, false>(group, ch))
+                               : (final ? pick_chunk<128, true>(group, ch) : pick_chunk<128, false>(group, ch));
     hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group, n_ctx, max_seq, scale, part, out);
     count_launch();
     if (final) return hipGetLastError();
