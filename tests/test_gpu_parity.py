@@ -222,6 +222,18 @@ def test_one_row_lds_x_shapes(qd, n_out, n_in):
     assert np.all(err <= swiglu_tol(r)), f"swiglu {n_out}x{n_in}: worst err/tol {np.max(err / swiglu_tol(r)):.3g}"
 
 
+@pytest.mark.parametrize("n_out,n_in", [(13, 1024), (5, 2048), (29, 3072), (7, 4096)])
+def test_two_row_swiglu_lds_x_shapes(qd, n_out, n_in):
+    """Two batch rows of SwiGLU up to 4096 columns: one row pair per wave, x
+    staged in LDS, ragged last workgroup."""
+    wg, wu = q8_weights(6120 + n_in, n_out, n_in), q8_weights(6121 + n_in, n_out, n_in)
+    x = synth.normal_f32(6122 + n_in, (2, n_in))
+    out = host(qd.q8_0_swiglu(dev(wg), dev(wu), n_in, n_out, dev(x)))
+    r = oracle.q8_0_swiglu(wg, wu, n_in, n_out, x)
+    err = np.abs(out.astype(np.float64) - r["out"])
+    assert np.all(err <= swiglu_tol(r)), f"worst err/tol {np.max(err / swiglu_tol(r)):.3g}"
+
+
 @pytest.mark.parametrize("n_in,n_q,n_kv", [(1024, 40, 8), (4096, 48, 16), (8192, 64, 32)])
 def test_one_row_lds_x_qkv(qd, n_in, n_q, n_kv):
     wq, wk, wv = (q8_weights(6110 + i, n, n_in) for i, n in enumerate((n_q, n_kv, n_kv)))
