@@ -242,6 +242,17 @@ def q8_0_gemv_f64(w, n_in: int, n_out: int, y) -> tuple[np.ndarray, np.ndarray]:
     return y @ deq.T, np.abs(y) @ np.abs(deq).T
 
 
+def f32_gemm_f64(w, n_in: int, n_out: int, y) -> tuple[np.ndarray, np.ndarray]:
+    """(out, S) of the dense batched product of ``f32_gemm`` for large shapes:
+    out = y W^T and S = |y| |W|^T with W the f32 row-major (n_out, n_in)
+    weights widened to f64 (exact) and numpy's f64 matrix product as the step
+    (weight_cache.rs source view, try_cuda_batch_gemv: C = A B with A the
+    batch x n_in hidden rows and B the transposed weight)."""
+    y = np.asarray(y, np.float64).reshape(-1, n_in)
+    wd = np.asarray(w, np.float32).reshape(n_out, n_in).astype(np.float64)
+    return y @ wd.T, np.abs(y) @ np.abs(wd).T
+
+
 def q8_0_swiglu_f64(w_gate, w_up, n_in: int, n_out: int, y) -> dict:
     """As q8_0_swiglu for an f64 input y: dict with out, g, u, Sg, Su."""
     g, sg = q8_0_gemv_f64(w_gate, n_in, n_out, y)

@@ -427,6 +427,62 @@ def test_swiglu_closed_forms():
     assert not np.allclose(s1, s2)
 
 
+def test_swiglu_f64_matches_c_oracle():
+    """The f64-input SwiGLU helper (used where the input is a normalised vector
+    that never exists in f32) agrees with the C oracle when the input is an
+    f32 vector: same g, u, S and output, to f64 rounding."""
+    raw_g, _ = synth.q8_0_weights(43, 24, 320)
+    raw_u, _ = synth.q8_0_weights(44, 24, 320)
+    x = synth.normal_f32(45, (3, 320))
+    c = oracle.q8_0_swiglu(raw_g, raw_u, 320, 24, x)
+    f = oracle.q8_0_swiglu_f64(raw_g, raw_u, 320, 24, x.astype(np.float64))
+    for key in ("g", "u", "Sg", "Su", "out"):
+        assert np.allclose(f[key], c[key], rtol=1e-12, atol=1e-14), key
+
+
+def test_swiglu_f64_closed_forms():
+    """Hand-worked values with an input that is not an f32 number (ln 3 in
+    f64): silu(ln 3) = (3/4) ln 3 and silu(-ln 3) = -(1/4) ln 3 exactly in real
+    arithmetic, so silu(g) * u with g = y5, u = 2 y5 is (3/2) ln^2 3 and
+    (1/2) ln^2 3.  The swapped product silu(u) * g is a different number
+    (silu(2 ln 3) = (9/5) ln 3), so a gate/up exchange fails; so does a sign
+    error inside silu (silu would become z / (1 + e^z))."""
+    n_in, n_out = 64, 4
+    gate = _unit_weight_block_rows(n_out, n_in, 5)               # g = y[5]
+    up = _unit_weight_block_rows(n_out, n_in, 5, q=2)            # u = 2 y[5]
+    ln3 = math.log(3.0)
+    for y5, want in ((ln3, 1.5 * ln3 * ln3), (-ln3, 0.5 * ln3 * ln3)):
+        y = np.zeros((1, n_in), np.float64)
+        y[0, 5] = y5
+        r = oracle.q8_0_swiglu_f64(gate, up, n_in, n_out, y)
+        assert np.all(r["g"] == y5) and np.all(r["u"] == 2 * y5)
+        assert np.all(np.abs(r["out"] - want) <= 1e-15 * want)
+        assert np.all(r["Sg"] == abs(y5)) and np.all(r["Su"] == 2 * abs(y5))
+    y = np.zeros((1, n_in), np.float64)
+    y[0, 5] = ln3
+    swapped = oracle.q8_0_swiglu_f64(up, gate, n_in, n_out, y)["out"]
+    assert np.all(np.abs(swapped - 1.8 * ln3 * ln3) <= 1e-15 * 1.8 * ln3 * ln3)
+    zero = _unit_weight_block_rows(n_out, n_in, 5, q=0)
+    assert np.all(oracle.q8_0_swiglu_f64(zero, up, n_in, n_out, y)["out"] == 0)
+    assert np.all(oracle.q8_0_swiglu_f64(gate, zero, n_in, n_out, y)["out"] == 0)
+
+
+def test_f32_gemm_f64_matches_c_oracle_and_columns():
+    """The f64 matrix-product route of the dense batched GEMM agrees with the C
+    oracle's sequential f64 sums, and unit vectors pick out weight columns."""
+    w = synth.normal_f32(16, (40, 96), 0.02)
+    x = synth.normal_f32(17, (5, 96))
+    a, sa = oracle.f32_gemm(w, 96, 40, x)
+    b, sb = oracle.f32_gemm_f64(w, 96, 40, x)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+    assert np.allclose(sa, sb, rtol=1e-13, atol=1e-15)
+    e = np.zeros((3, 96), np.float64)
+    e[0, 7] = e[1, 50] = e[2, 95] = 1.0
+    cols, _ = oracle.f32_gemm_f64(w, 96, 40, e)
+    for r, j in enumerate((7, 50, 95)):
+        assert np.array_equal(cols[r], w[:, j].astype(np.float64))
+
+
 def test_swiglu_matches_gemvs():
     raw_g, _ = synth.q8_0_weights(40, 16, 256)
     raw_u, _ = synth.q8_0_weights(41, 16, 256)

@@ -67,3 +67,62 @@ def test_pins_reject_mutant(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the oracle pins"
+
+
+# Mistakes planted in the numpy helpers of oracle/__init__.py (the f64-input
+# products the chained-layer and full-size batched parity tests use).  The pins
+# run in a copy of the oracle, synth and test files with the helper mutated,
+# against the unmodified C library.
+PY_MUTANTS = {
+    "f64_gemv_s_without_abs": ("return y @ deq.T, np.abs(y) @ np.abs(deq).T",
+                               "return y @ deq.T, np.abs(y @ deq.T)"),
+    "f64_gemv_input_rows_reversed": ("return y @ deq.T, np.abs(y) @ np.abs(deq).T",
+                                     "return y[::-1] @ deq.T, np.abs(y) @ np.abs(deq).T"),
+    "f64_swiglu_operands_swapped": ("silu_g = g / (1.0 + np.exp(-g))",
+                                    "silu_g = u / (1.0 + np.exp(-u)); u = g"),
+    "f64_swiglu_silu_sign": ("silu_g = g / (1.0 + np.exp(-g))", "silu_g = g / (1.0 + np.exp(g))"),
+    "f64_swiglu_sigmoid_only": ("silu_g = g / (1.0 + np.exp(-g))", "silu_g = 1.0 / (1.0 + np.exp(-g))"),
+    "f64_swiglu_s_swapped": ('"Sg": sg, "Su": su', '"Sg": su, "Su": sg'),
+    "f64_dense_transposed_weight": ("return y @ wd.T, np.abs(y) @ np.abs(wd).T",
+                                    "return y @ wd.reshape(n_in, n_out), np.abs(y) @ np.abs(wd).T"),
+    "f64_dense_s_without_abs": ("return y @ wd.T, np.abs(y) @ np.abs(wd).T",
+                                "return y @ wd.T, np.abs(y @ wd.T)"),
+}
+
+
+def _run_pins_on_copy(tmp_path, helper_src):
+    """Copy the oracle (with `helper_src` as its Python module), synth and the
+    pin tests into tmp_path and run the pins there; returns pytest's exit code."""
+    import shutil
+    (tmp_path / "oracle").mkdir()
+    (tmp_path / "oracle" / "__init__.py").write_text(helper_src)
+    shutil.copy(SRC, tmp_path / "oracle" / "oracle.c")
+    shutil.copytree(os.path.join(ROOT, "synth"), tmp_path / "synth",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    (tmp_path / "tests").mkdir()
+    for f in ("conftest.py", "test_oracle.py", "helpers.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path / "pytest.ini")
+    env = dict(os.environ, QDEC_ORACLE_LIB=oracle.build())
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        str(tmp_path / "tests" / "test_oracle.py")],
+                       cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=300)
+    return r.returncode, r.stdout[-2000:]
+
+
+def test_python_helper_copy_passes_unmutated(tmp_path):
+    """Control: the copied tree passes the pins, so a failure below comes from
+    the planted mistake and not from the copy."""
+    rc, out = _run_pins_on_copy(tmp_path, open(os.path.join(ROOT, "oracle", "__init__.py")).read())
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_reject_python_helper_mutant(name, tmp_path):
+    old, new = PY_MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    rc, out = _run_pins_on_copy(tmp_path, src.replace(old, new, 1))
+    # exit code 1: a pin failed (2 would be a collection error, not a rejection)
+    assert rc == 1, f"mutant {name} survived the oracle pins (rc {rc}):\n{out}"
