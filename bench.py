@@ -12,13 +12,20 @@ alone rotates over >= 512 MB, twice the 256 MB Infinity Cache), so the bytes
 come from HBM as in a real decode.
 
 value = algorithmic bytes per step (GGML weight bytes + x + out + residual)
-        / wall time per step, in GB/s, inputs resident in HBM.
+        / wall time per step, in GB/s, inputs resident in HBM.  The timed
+        region is one replay of a HIP graph that holds exactly `steps` steps
+        (3 launches each, layers rotating), bracketed by device syncs.
 roofline = the dominant kernel's algorithmic bytes per launch / its mean
         launch duration (HIP events around a replayed graph of `steps`
         launches of that kernel), against 8 TB/s; traffic = the HBM bytes the
         profiler counted for one launch of it (profiles/, null once the GEMV
         sources differ from the ones profiled).
-cpu_baseline = the CPU oracle (single thread) on a bounded sample of steps.
+batched_gemm = the prefill-shaped Q8_0 GEMM (batch 128 and 512 rows against
+        the layers' FFN up and down weights, the other half of the metric):
+        mean launch duration of graph-replayed launches, TFLOP/s and the
+        fraction of the 2.5 PFLOP/s dense bf16 matrix-core peak.
+cpu_baseline = the CPU oracle on a bounded sample of steps, single-threaded
+        and on all host cores (row slices of every product in a thread pool).
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 LAYERS = 32
 N_IN, N_Q, N_KV, N_FF = 3072, 3072, 1024, 8192
 
@@ -89,23 +97,148 @@ def measured_traffic(kernel_role):
                             "source": "profiles/q8_0_decode_layer_traffic.json"}
 
 
-def cpu_baseline(w, x, budget_s=12.0):
-    """The oracle as it stands, one thread, timed on whole steps until the
-    budget is spent (at least one step)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores():
+    """Worker threads for the all-core baseline: the CPUs this process may
+    run on, at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_step_single(w, x):
     import oracle
+    oracle.q8_0_qkv(w["wq"], w["wk"], w["wv"], N_IN, N_Q, N_KV, x["x_qkv"])
+    oracle.q8_0_gemv(w["up"], N_IN, N_FF, x["x_up"])
+    oracle.q8_0_gemv_residual(w["down"], N_FF, N_IN, x["x_down"], x["r_down"])
+
+
+def cpu_step_tasks(w, x, parts):
+    """The step as independent row-slice calls of the unchanged oracle: every
+    product's output rows split into `parts` contiguous slices (the fused QKV
+    is its three products, as the oracle defines it)."""
+    import oracle
+    tasks = []
+
+    def slices(n_out):
+        edges = [n_out * k // parts for k in range(parts + 1)]
+        return [(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+    for key, n_in, n_out, xk in (("wq", N_IN, N_Q, "x_qkv"), ("wk", N_IN, N_KV, "x_qkv"),
+                                 ("wv", N_IN, N_KV, "x_qkv"), ("up", N_IN, N_FF, "x_up")):
+        rb = (n_in // 32) * 34
+        for a, b in slices(n_out):
+            tasks.append(lambda key=key, n_in=n_in, xk=xk, a=a, b=b, rb=rb:
+                         oracle.q8_0_gemv(w[key][a * rb:b * rb], n_in, b - a, x[xk]))
+    rb = (N_FF // 32) * 34
+    for a, b in slices(N_IN):
+        tasks.append(lambda a=a, b=b: oracle.q8_0_gemv_residual(w["down"][a * rb:b * rb], N_FF, b - a,
+                                                                x["x_down"], x["r_down"][:, a:b]))
+    return tasks
+
+
+def cpu_baseline(w, x, budget_s=12.0):
+    """The oracle as it stands, timed on whole steps until each budget is
+    spent (at least one step): one thread, then all host cores (the C oracle
+    releases the GIL, so a thread pool runs its row slices in parallel)."""
+    import concurrent.futures as cf
+    total = sum(step_bytes().values())
     steps, t0 = 0, time.perf_counter()
     while True:
-        oracle.q8_0_qkv(w["wq"], w["wk"], w["wv"], N_IN, N_Q, N_KV, x["x_qkv"])
-        oracle.q8_0_gemv(w["up"], N_IN, N_FF, x["x_up"])
-        oracle.q8_0_gemv_residual(w["down"], N_FF, N_IN, x["x_down"], x["r_down"])
+        cpu_step_single(w, x)
         steps += 1
         dt = time.perf_counter() - t0
         if dt >= budget_s:
             break
-    total = sum(step_bytes().values())
-    return {"value": round(total * steps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full decode-layer steps (QKV + up + down/residual, batch 1) in {dt:.1f} s, "
-                      f"single-threaded C oracle, f64 accumulation"}
+    single = {"value": round(total * steps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+              "sample": f"{steps} full decode-layer steps (QKV + up + down/residual, batch 1) in {dt:.1f} s, "
+                        f"single-threaded C oracle, f64 accumulation"}
+    n = host_cores()
+    tasks = cpu_step_tasks(w, x, 4 * n)
+    steps, t0 = 0, time.perf_counter()
+    with cf.ThreadPoolExecutor(n) as ex:
+        while True:
+            for f in [ex.submit(t) for t in tasks]:
+                f.result()
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                break
+    allc = {"value": round(total * steps / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"{steps} full decode-layer steps in {dt:.1f} s, the unchanged C oracle on {len(tasks)} "
+                      f"row slices per step in a pool of {n} threads"}
+    allc["cpu_model"] = single["cpu_model"] = cpu_model()
+    return allc, single
+
+
+def fingerprints(w, x):
+    """FNV-1a fingerprint of every input tensor (the pages' weight_fingerprint
+    key), printed to the run log so that runs can be audited."""
+    import synth
+    dims = {"wq": (N_IN, N_Q), "wk": (N_IN, N_KV), "wv": (N_IN, N_KV), "up": (N_IN, N_FF), "down": (N_FF, N_IN),
+            "x_qkv": (N_IN, 1), "x_up": (N_IN, 1), "x_down": (N_FF, 1), "r_down": (N_IN, 1)}
+    out = {}
+    for k, v in list(w.items()) + list(x.items()):
+        n_in, n_out = dims[k]
+        out[k] = f"{synth.fnv1a64(v, n_in, n_out):016x}"
+    return out
+
+
+def ceiling(args):
+    """The plain streaming-read ceiling (qdec_stream_read) at the byte counts
+    of the decode products: one JSON line per (size, loads per lane), mean
+    launch duration of graph-replayed launches over rotated regions of a
+    2.5 GB buffer (>= 512 MB per size, twice the Infinity Cache)."""
+    import torch
+
+    import quantized_decode_ggml_amd as qd
+    dev = torch.device("cuda:0")
+    total = 2560 << 20
+    buf = torch.randint(0, 256, (total,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    sizes = (("QKV 5120x3072 Q8_0", q8_bytes(5120, 3072)), ("FFN 8192x3072 Q8_0", q8_bytes(8192, 3072)),
+             ("Q4_K 8192x3072", 8192 * 12 * 144), ("vocab 128256x3072 Q8_0", q8_bytes(128256, 3072)))
+    for name, nbytes in sizes:
+        nbytes -= nbytes % 16
+        stride = -(-nbytes // 4096) * 4096
+        regions = max(2, min(total // stride, -(-(512 << 20) // nbytes)))
+        for u in (1, 2, 4, 8, 16):
+            offs = [r * stride for r in range(regions)]
+            iters = 40 if nbytes > (100 << 20) else 200
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for i in range(2 * regions):
+                    qd.stream_read(buf[offs[i % regions]:], nbytes, u, sink)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(iters):
+                    qd.stream_read(buf[offs[i % regions]:], nbytes, u, sink)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            cur = torch.cuda.current_stream()
+            e0.record(cur)
+            g.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / iters
+            print(json.dumps({"ceiling": name, "bytes": nbytes, "loads_per_lane": u, "mean_us": round(us, 3),
+                              "gbs": round(nbytes / us / 1e3, 1),
+                              "pct_hbm": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}), flush=True)
+            del g
 
 
 def suite(args):
@@ -330,6 +463,36 @@ def suite(args):
     timed("empty kernel", [lambda: qd.empty_kernel()], 0)
 
 
+def time_graph(launch, n, stream_holder, torch, warm=3):
+    """Mean duration of one launch: `n` calls of launch(i) captured into one
+    HIP graph on a dedicated stream (warmed up there first, so per-stream
+    library state such as a workspace exists before the capture), replayed
+    once untimed and once between HIP events recorded on the replay stream
+    (so only device time is measured)."""
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    stream_holder[0] = cs
+    with torch.cuda.stream(cs):
+        for i in range(warm):
+            launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        for i in range(n):
+            launch(i)
+    rs = torch.cuda.current_stream()
+    stream_holder[0] = rs
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(rs)
+    g.replay()
+    e1.record(rs)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +503,8 @@ def main():
                     help="time every workload configuration (one JSON line each) instead of the step")
     ap.add_argument("--only", default="",
                     help="with --suite: time only the workloads whose name starts with this prefix (e.g. 'c3')")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time the plain streaming-read kernel at the decode products' byte counts")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 64 MiB device copy (untimed), the known-size reference that "
                          "scales the profiler's HBM byte counters")
@@ -348,21 +513,28 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is a "
               "single-GPU weight-streaming kernel and no multi-GPU build exists", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     if args.suite:
         suite(args)
         return
+    if args.ceiling:
+        ceiling(args)
+        return
 
-    import numpy as np
     import torch
 
     import quantized_decode_ggml_amd as qd
+    import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
     w_host, x_host = make_inputs()
     print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    print("[bench] fnv1a64 " + json.dumps(fingerprints(w_host, x_host)), file=sys.stderr, flush=True)
 
     # LAYERS device copies of every weight, repacked once (load time, untimed)
     layers = []
@@ -382,7 +554,7 @@ def main():
     v_out = torch.empty((1, N_KV), device=dev)
     up_out = torch.empty((1, N_FF), device=dev)
     down_out = torch.empty((1, N_IN), device=dev)
-    stream = torch.cuda.current_stream()
+    sh = [torch.cuda.current_stream()]
     torch.cuda.synchronize()
     if args.calibrate:
         # 64 MiB read + 64 MiB written by qdec_copy_kernel, three times
@@ -398,6 +570,7 @@ def main():
 
     def single(name, i):
         L = layers[i % LAYERS]
+        stream = sh[0]
         if name == "qkv":
             qd.q8_0_qkv(L["wq"], L["wk"], L["wv"], N_IN, N_Q, N_KV, xs["x_qkv"], q_out, k_out, v_out, stream=stream)
         elif name == "up":
@@ -413,36 +586,34 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # One HIP graph per layer (its three launches), captured on torch's capture
-    # stream, plus one graph over all LAYERS layers; replaying them removes the
-    # per-call Python/ctypes cost from the device timeline.
-    graphs = []
-    for i in range(LAYERS):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            stream = torch.cuda.current_stream()
+    # Exactly args.steps steps (layers rotating) captured into one HIP graph;
+    # one untimed replay, then the timed replay.  The Python/ctypes cost of
+    # the calls stays out of the timed region.
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    sh[0] = cs
+    g_steps = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_steps, stream=cs):
+        for i in range(args.steps):
             step(i)
-        graphs.append(g)
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all):
-        stream = torch.cuda.current_stream()
-        for i in range(LAYERS):
-            step(i)
-    stream = torch.cuda.current_stream()
-    for _ in range(3):
-        g_all.replay()
+    sh[0] = torch.cuda.current_stream()
+    g_steps.replay()
     torch.cuda.synchronize()
 
-    # timed region 1: exactly args.steps steps through the graphs (headline)
+    # timed region: args.steps steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    full, rest = divmod(args.steps, LAYERS)
-    for _ in range(full):
-        g_all.replay()
-    for i in range(rest):
-        graphs[i].replay()
+    g_steps.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same replay between HIP events (device time of the steps alone)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(sh[0])
+    g_steps.replay()
+    e1.record(sh[0])
+    torch.cuda.synchronize()
+    device_ms = e0.elapsed_time(e1)
+    del g_steps
 
     # eager steps (one host call per product), for reference
     launches0 = qd.launch_count()
@@ -454,32 +625,35 @@ def main():
     wall_eager = time.perf_counter() - t0
     assert qd.launch_count() - launches0 == 3 * args.steps, "not every product ran in libqdec"
 
-    # timed region 2: each product alone, `steps` launches over the rotated
-    # layers captured into one HIP graph and replayed, bracketed by HIP events
-    # on the replay stream: the mean launch duration of that kernel (launch
-    # gaps included, so slightly above the profiler's kernel duration).
+    # each product alone: `steps` launches over the rotated layers in one
+    # graph, mean launch duration (launch gaps included, so slightly above
+    # the profiler's kernel duration)
     per_kernel = {}
     sb = step_bytes()
     for n in names:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            stream = torch.cuda.current_stream()
-            for i in range(args.steps):
-                single(n, i)
-        stream = torch.cuda.current_stream()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        del g
-        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        us = time_graph(lambda i, n=n: single(n, i), args.steps, sh, torch)
         per_kernel[n] = {"mean_us": round(us, 3), "bytes": sb[n], "gbs": round(sb[n] / (us * 1e-6) / 1e9, 1)}
     dom = max(names, key=lambda n: per_kernel[n]["mean_us"])
     achieved = per_kernel[dom]["gbs"]
     traffic, traffic_detail = measured_traffic(dom)
+
+    # batched prefill GEMM on the layers' FFN weights (config-3 shapes)
+    gemm = {}
+    for B in (128, 512):
+        for nm, key, n_out, n_in in (("up 8192x3072", "up", N_FF, N_IN), ("down 3072x8192", "down", N_IN, N_FF)):
+            x3 = torch.from_numpy(synth.normal_f32(synth.seed(3, 2) + B, (B, n_in))).to(dev)
+            o3 = torch.empty((B, n_out), device=dev)
+            us = time_graph(lambda i, key=key, n_in=n_in, n_out=n_out, x3=x3, o3=o3: qd.q8_0_gemm_batched(
+                layers[i % LAYERS][key], n_in, n_out, x3, out=o3, stream=sh[0]), 64, sh, torch)
+            flops = 2.0 * B * n_out * n_in
+            byts = q8_bytes(n_out, n_in) + 4 * B * (n_in + n_out)
+            tf = flops / (us * 1e-6) / 1e12
+            attain = min(BF16_PEAK_TFLOPS, flops / byts * HBM_PEAK_GBS / 1e3)
+            gemm[f"q8_0 {nm} B{B}"] = {"mean_us": round(us, 3), "tflops": round(tf, 1),
+                                        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                                        "frac_roofline": round(tf / attain, 4),
+                                        "bound": "mfma" if attain >= BF16_PEAK_TFLOPS else "hbm"}
+            del x3, o3
 
     total_bytes = sum(sb.values())
     ms_per_step = wall / args.steps * 1e3
@@ -505,16 +679,19 @@ def main():
             "layers_rotated": LAYERS,
             "bytes_per_step": total_bytes,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "device_ms_per_step": round(device_ms / args.steps, 5),
             "kernels": per_kernel,
-            "launch": "hip graph per layer (3 kernels), replayed",
+            "launch": f"one hip graph of {args.steps} steps (3 kernels each), replayed once",
             "eager_ms_per_step": round(wall_eager / args.steps * 1e3, 5),
         },
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "bytes per launch", "traffic_detail": traffic_detail},
+        "batched_gemm": {"unit": "TFLOP/s", "peak_bf16_tflops": BF16_PEAK_TFLOPS,
+                         "launch": "64 graph-replayed launches over the rotated layers", "shapes": gemm},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w_host, x_host)
+        line["cpu_baseline"], line["cpu_baseline_single_thread"] = cpu_baseline(w_host, x_host)
     print(json.dumps(line), flush=True)
 
 

@@ -225,6 +225,8 @@ hipError_t launch_attention(const float* q, const float* k_cache, const float* v
 
 hipError_t launch_empty(hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+// loads_per_lane in {1, 2, 4, 8, 16}; bytes % 16 == 0
+hipError_t launch_stream_read(const void* src, int64_t bytes, int loads_per_lane, uint32_t* sink, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -194,6 +194,30 @@ __global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst,
         dst[i] = src[i];
 }
 
+// Plain streaming read (the HBM read ceiling the weight-streaming kernels are
+// measured against): a workgroup reads 4 KB * U contiguous bytes, each lane U
+// non-temporal 16-byte loads issued before any use.  The loaded words are
+// folded by XOR and written only in the (practically impossible) case that a
+// lane's fold equals a fixed constant, so the loads cannot be removed while
+// the kernel writes essentially nothing.
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, int64_t n,
+                                                          uint32_t* __restrict__ sink)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int64_t base = (int64_t)blockIdx.x * (256 * U) + threadIdx.x;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * 256;
+        v[u] = i < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i)) : u32x4{0, 0, 0, 0};
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
 }  // namespace
@@ -267,6 +291,22 @@ hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s)
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, int loads_per_lane, uint32_t* sink, hipStream_t s)
+{
+    const int64_t n = bytes / 16;
+    const unsigned blocks = grid_for(n, 256 * loads_per_lane);
+    const uint4* p = static_cast<const uint4*>(src);
+    switch (loads_per_lane) {
+        case 1: hipLaunchKernelGGL(stream_read_kernel<1>, dim3(blocks), dim3(256), 0, s, p, n, sink); break;
+        case 2: hipLaunchKernelGGL(stream_read_kernel<2>, dim3(blocks), dim3(256), 0, s, p, n, sink); break;
+        case 4: hipLaunchKernelGGL(stream_read_kernel<4>, dim3(blocks), dim3(256), 0, s, p, n, sink); break;
+        case 8: hipLaunchKernelGGL(stream_read_kernel<8>, dim3(blocks), dim3(256), 0, s, p, n, sink); break;
+        default: hipLaunchKernelGGL(stream_read_kernel<16>, dim3(blocks), dim3(256), 0, s, p, n, sink); break;
+    }
     count_launch();
     return hipGetLastError();
 }

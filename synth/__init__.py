@@ -21,6 +21,10 @@ themselves give no values):
 """
 from __future__ import annotations
 
+import ctypes
+import os
+import subprocess
+
 import numpy as np
 
 Q8_0_BLOCK_BYTES = 34
@@ -93,21 +97,48 @@ def q6k_weights(seed: int, n_out: int, n_in: int, lo: float = 1e-4, hi: float = 
     return blk.reshape(-1)
 
 
-def fnv1a64(raw: bytes | np.ndarray, n_in: int, n_out: int) -> int:
+def fnv1a64_py(raw: bytes | np.ndarray, n_in: int, n_out: int) -> int:
     """Content fingerprint for run logs: FNV-1a over the bytes, then n_in and
     n_out each folded in as a whole 64-bit word (the pages' weight_fingerprint
-    in the rustdoc source view of weight_cache.rs)."""
+    in the rustdoc source view of weight_cache.rs).  One multiply per byte in
+    Python: the statement of the hash that pins the compiled fnv1a64."""
     data = np.ascontiguousarray(raw).view(np.uint8).reshape(-1)
     mask = (1 << 64) - 1
     prime = 0x100000001B3
     h = 0xCBF29CE484222325
-    # One multiply per byte in Python: use it on small tensors (tests, logs of
-    # the small workloads) only.
     for byte in data.tobytes():
         h = ((h ^ byte) * prime) & mask
     h = ((h ^ (n_in & mask)) * prime) & mask
     h = ((h ^ (n_out & mask)) * prime) & mask
     return h
+
+
+_FNV_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "fnv1a.c")
+_FNV_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynthfnv.so")
+_fnv = None
+
+
+def build_fnv(force: bool = False) -> str:
+    """Compile fnv1a.c with gcc (in-tree, next to this file)."""
+    if force or not os.path.exists(_FNV_LIB) or os.path.getmtime(_FNV_LIB) < os.path.getmtime(_FNV_SRC):
+        tmp = _FNV_LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-o", tmp, _FNV_SRC], check=True)
+        os.replace(tmp, _FNV_LIB)
+    return _FNV_LIB
+
+
+def fnv1a64(raw: bytes | np.ndarray, n_in: int, n_out: int) -> int:
+    """The same fingerprint as fnv1a64_py, computed by the compiled fnv1a.c
+    (tensors of tens of MB in the benchmark logs)."""
+    global _fnv
+    if _fnv is None:
+        lib = ctypes.CDLL(build_fnv())
+        lib.synth_fnv1a64.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint64, ctypes.c_uint64]
+        lib.synth_fnv1a64.restype = ctypes.c_uint64
+        _fnv = lib
+    data = np.ascontiguousarray(np.ascontiguousarray(raw).view(np.uint8).reshape(-1))
+    return int(_fnv.synth_fnv1a64(data.ctypes.data_as(ctypes.c_void_p), data.size, n_in & ((1 << 64) - 1),
+                                  n_out & ((1 << 64) - 1)))
 
 
 def seed(workload: int, index: int) -> int:
