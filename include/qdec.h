@@ -47,14 +47,16 @@
  *     complete, for every weight before capturing.
  *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in of
  *     1024..8192 in the supported steps) splits x, q8_0_gemv_topk keeps its
- *     candidate lists, and q8_0_gemm_batched (on its pipelined path:
- *     n_in % 64 == 0, n_out % 8 == 0, output tiles of 128 x 128 that fill
- *     the chip, if need be with K split over up to 8 slices) rounds x to bf16
- *     and keeps the slices' partial products (as do both batched GEMMs on
- *     their other K-split shapes), in a library-owned device buffer, one per
+ *     candidate lists, and q8_0_gemm_batched (on its DMA-fed path:
+ *     n_in % 64 == 0 and even n_out, K split over up to 8 slices when the
+ *     output has few 128 x 128 tiles) rounds x to bf16 and keeps the slices'
+ *     partial products (as do both batched GEMMs on their other K-split
+ *     shapes), in a library-owned device buffer, one per
  *     (device, stream), made (or grown) on the first such call on that stream
  *     and freed by qdec_clear_cache.  Calls on one stream share it in
- *     stream order; calls on different streams never share one.  A stream
+ *     stream order; calls on different streams never share one.  When a
+ *     stream's buffer grows, the old one is kept (not freed) until
+ *     qdec_clear_cache, because a graph captured earlier may still use it.  A stream
  *     capture cannot allocate it, so a capture on a stream that has none takes
  *     the VALU kernels (same results to the f32 tolerance), or for the GEMMs
  *     the register-staged kernel with its K slices added by f32 atomics (same
@@ -114,7 +116,8 @@ QDEC_API int q8_0_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch
 /* Down-projection with residual ([cuda_lane] try_q4k_soa_ffn_block_residual):
  * out[b][i] = residual[b][i] + sum_j deq(W)[i][j] * x[b][j].
  * residual is device f32 batch x n_out; out may be the same buffer as
- * residual (in-place update).  Other conditions as q8_0_gemv. */
+ * residual (in-place update); residual must not overlap x (QDEC_EINVAL).
+ * Other conditions as q8_0_gemv. */
 QDEC_API int q8_0_gemv_residual(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
                        const float* x, const float* residual, float* out,
                        hipStream_t stream);
@@ -262,11 +265,15 @@ QDEC_API int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64
 QDEC_API int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream);
 
 /* Free every repacked copy made from w (all types and shapes) on the current
- * device.  Returns QDEC_EINVAL if there was none.  Waits for the device. */
+ * device.  Returns QDEC_EINVAL if there was none.  Waits for the device.
+ * A HIP graph captured from calls on w reads these copies: after this call
+ * such a graph must not be replayed again (capture it anew). */
 QDEC_API int qdec_release(const void* w);
 
 /* Free every repacked copy and every workspace on every device ([cuda_lane]
- * clear_weight_cache, "tests / model swap").  Waits for the devices. */
+ * clear_weight_cache, "tests / model swap").  Waits for the devices.  Every
+ * graph captured from library calls is invalid afterwards (it holds the
+ * addresses of copies and workspaces); capture again after new calls. */
 QDEC_API void qdec_clear_cache(void);
 
 /* Number of repacked copies currently held ([cuda_lane] weight_cache_len). */
@@ -299,6 +306,20 @@ QDEC_API int qdec_empty_kernel(hipStream_t stream);
 /* Plain device copy of `bytes` bytes (bytes % 16 == 0, both pointers 16-byte
  * aligned): the known-size reference kernel for HBM byte counters. */
 QDEC_API int qdec_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+/* Plain streaming read of `bytes` bytes of device memory at src (bytes % 16
+ * == 0, src 16-byte aligned): each lane issues loads_per_lane (1, 2, 4, 8 or
+ * 16) non-temporal 16-byte loads before using any of them, a workgroup of 256
+ * lanes covering 4 KB * loads_per_lane contiguous bytes.  The HBM read
+ * ceiling the weight-streaming kernels are compared with: a measurement
+ * probe beside qdec_empty_kernel (the pages time only an empty submit,
+ * [QTensorEngine] bench_empty_submit_roundtrip; no operation of theirs
+ * corresponds to it).  sink: device
+ * memory of at least 4 bytes, not overlapping src, written only if the XOR
+ * of a lane's loaded words equals a fixed constant (its contents carry no
+ * meaning; the write keeps the loads from being removed). */
+QDEC_API int qdec_stream_read(const void* src, int64_t bytes, int loads_per_lane, uint32_t* sink,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -4,7 +4,9 @@ for AMD MI355X (gfx950).
 Argument marshalling only.  Every function takes torch tensors that live on the
 GPU, passes their device pointers and the current HIP stream to the C ABI of the
 same name, and raises QdecError on a non-zero status.  All arithmetic runs in
-the library's HIP kernels; there is no CPU path.  The library must have been
+the library's HIP kernels; there is no CPU path.  Weights passed to the
+library stay allocated until ``release`` or ``clear_cache`` (see ``_track``).
+The library must have been
 built (``python quantized_decode_ggml_amd/_build.py`` or
 ``__graft_entry__.build()``); importing this package without it raises.
 """
@@ -13,7 +15,6 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-import weakref
 
 import torch
 
@@ -55,6 +56,7 @@ _SIGS = {
     "q4k_dequantize": [_P, _I, _I, _P, _P],
     "qdec_empty_kernel": [_P],
     "qdec_copy": [_P, _P, _I, _P],
+    "qdec_stream_read": [_P, _I, ctypes.c_int, _P, _P],
 }
 for _name, _args in _SIGS.items():
     getattr(lib, _name).argtypes = _args
@@ -89,30 +91,24 @@ def _check(status: int):
 
 # The library caches a repacked copy per weight pointer and trusts the caller to
 # release it before the bytes behind the pointer change.  Torch frees and reuses
-# device addresses freely, so the binding releases a weight's copies when the
-# tensor object that was passed in is garbage-collected.
-_tracked: dict[int, weakref.finalize] = {}
-
-
-def _release_quietly(ptr: int):
-    f = _tracked.get(ptr)
-    if f is not None and not f.alive:
-        _tracked.pop(ptr, None)
-    lib.qdec_release(ptr)
+# device addresses, so the binding keeps the storage of every weight it has
+# passed to the library alive until release() or clear_cache(): its address
+# cannot be handed to another tensor while a copy made from it exists, and a
+# captured graph that reads the copy stays valid however the caller's tensor
+# objects and views come and go.  Nothing is freed from a garbage-collection
+# callback (which could run in the middle of a stream capture).
+_pinned: dict[int, object] = {}
 
 
 def _track(*weights):
-    """After a successful call: release each weight's repacked copies when the
-    tensor object dies."""
+    """After a successful call: keep each weight's storage alive while the
+    library may hold a copy made from it."""
     for t in weights:
         if t is None or isinstance(t, int):
             continue
         ptr = t.data_ptr()
-        f = _tracked.get(ptr)
-        if f is None or not f.alive:
-            f = weakref.finalize(t, _release_quietly, ptr)
-            f.atexit = False
-            _tracked[ptr] = f
+        if ptr not in _pinned:
+            _pinned[ptr] = t.untyped_storage()
 
 
 def _ptr(t) -> int | None:
@@ -292,18 +288,20 @@ def prepare(w, qtype, n_in, n_out, stream=None):
 
 
 def release(w):
+    """Free the library's copies of w (graphs captured from calls on w must
+    not be replayed afterwards) and stop keeping its storage alive."""
     ptr = _ptr(w)
-    f = _tracked.pop(ptr, None)
-    if f is not None:
-        f.detach()
-    _check(lib.qdec_release(ptr))
+    try:
+        _check(lib.qdec_release(ptr))
+    finally:
+        _pinned.pop(ptr, None)
 
 
 def clear_cache():
-    for f in list(_tracked.values()):
-        f.detach()
-    _tracked.clear()
+    """Free every copy and workspace (invalidates every captured graph that
+    used the library) and every storage the binding kept alive."""
     lib.qdec_clear_cache()
+    _pinned.clear()
 
 
 def cache_len() -> int:
@@ -348,3 +346,8 @@ def empty_kernel(stream=None):
 
 def copy(dst, src, nbytes, stream=None):
     _check(lib.qdec_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
+
+
+def stream_read(src, nbytes, loads_per_lane, sink, stream=None):
+    """Plain streaming read of nbytes of src (the HBM read ceiling probe)."""
+    _check(lib.qdec_stream_read(_ptr(src), nbytes, int(loads_per_lane), _ptr(sink), _stream(stream)))

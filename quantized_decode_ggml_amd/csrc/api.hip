@@ -169,8 +169,11 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
 // (device, stream): calls on one stream are ordered, so they can share it;
 // calls on different streams never do.  A buffer grows on demand outside
 // stream capture; a capturing stream whose buffer is missing or too small gets
-// none, and the caller then takes the VALU kernels.
+// none, and the caller then takes the VALU kernels.  A buffer that a larger
+// one replaces is not freed: a graph captured earlier may still hold its
+// address, so it stays on the retired list until qdec_clear_cache.
 std::map<std::pair<int, uintptr_t>, Entry> g_ws;
+std::vector<std::pair<int, Entry>> g_ws_retired;
 
 int stream_workspace(hipStream_t s, int64_t bytes, void** out)
 {
@@ -192,8 +195,9 @@ int stream_workspace(hipStream_t s, int64_t bytes, void** out)
     if (capture != hipStreamCaptureStatusNone) return QDEC_OK;
     if (fail_alloc_hook()) return fail(QDEC_ENOMEM, "workspace allocation refused (QDEC_FAIL_ALLOC=1)");
     if (ent.buf) {
-        (void)hipDeviceSynchronize();   // the old buffer may still be read by queued kernels
-        destroy(ent);
+        // queued kernels and captured graphs may still use the old buffer
+        g_ws_retired.emplace_back(dev, ent);
+        ent = Entry{};
     }
     e = hipMalloc(&ent.buf, (size_t)bytes);
     if (e != hipSuccess) {
@@ -258,7 +262,11 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
         if (overlaps(outs[k], batch * rows[k] * 4, x, batch * n_in * 4))
             return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
     }
-    if (mode == kResidual) QDEC_TRY(check_ptr(fn, "residual", residual, 4));
+    if (mode == kResidual) {
+        QDEC_TRY(check_ptr(fn, "residual", residual, 4));
+        if (overlaps(residual, batch * rows[0] * 4, x, batch * n_in * 4))
+            return fail(QDEC_EINVAL, "%s: residual overlaps x", fn);
+    }
     Q8GemvProblem p{};
     p.mode = mode;
     p.nseg = nw;
@@ -683,6 +691,12 @@ void qdec_clear_cache(void)
         destroy(kv.second);
     }
     g_ws.clear();
+    for (auto& kv : g_ws_retired) {
+        if (have_dev) (void)hipSetDevice(kv.first);
+        (void)hipDeviceSynchronize();
+        destroy(kv.second);
+    }
+    g_ws_retired.clear();
     if (have_dev) (void)hipSetDevice(cur);
 }
 
@@ -743,6 +757,20 @@ int qdec_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream)
     QDEC_TRY(check_ptr(fn, "src", src, 16));
     if (overlaps(dst, bytes, src, bytes)) return fail(QDEC_EINVAL, "%s: buffers overlap", fn);
     return finish(launch_copy(dst, src, bytes, stream), fn);
+}
+
+int qdec_stream_read(const void* src, int64_t bytes, int loads_per_lane, uint32_t* sink, hipStream_t stream)
+{
+    const char* fn = "qdec_stream_read";
+    if (bytes <= 0 || bytes % 16 != 0 || bytes / 16 > (int64_t)UINT32_MAX * 256)
+        return fail(QDEC_EINVAL, "%s: bytes=%lld must be a positive multiple of 16", fn, (long long)bytes);
+    if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8 &&
+        loads_per_lane != 16)
+        return fail(QDEC_EINVAL, "%s: loads_per_lane=%d not 1, 2, 4, 8 or 16", fn, loads_per_lane);
+    QDEC_TRY(check_ptr(fn, "src", src, 16));
+    QDEC_TRY(check_ptr(fn, "sink", sink, 4));
+    if (overlaps(sink, 4, src, bytes)) return fail(QDEC_EINVAL, "%s: sink overlaps src", fn);
+    return finish(launch_stream_read(src, bytes, loads_per_lane, sink, stream), fn);
 }
 
 }  // extern "C"

@@ -15,21 +15,22 @@
 // single-token path; bf16 keeps the f32 exponent range, and the error per
 // product is at most about 2*2^-9 relative.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C over a slice
-// of K; each of its four waves computes 64 x 64 with 4 x 4 MFMA 16x16x32
-// tiles.  K advances 64 at a time (two Q8_0 blocks).  Both operands are staged
-// in LDS as bf16 rows (K contiguous, padded by 8 elements against bank
-// conflicts), double-buffered: the global loads of step k+1 are in flight
-// while step k runs on MFMA.
-//
-// Parallelism: with few output tiles (the prefill batch is 128 or 512 rows) K
-// is split into S slices so that the grid has at least one workgroup per CU;
-// the slices add their partial tiles into the output with fire-and-forget f32
-// atomics (a fill kernel zeroes the output first).  Each atomic costs far more
-// than a store, so S stays at the smallest value that fills the CUs.  Block
-// ids go to the XCDs round-robin, which spreads the m-tiles that share a
-// weight tile over all L2s (measured faster than grouping consecutive tiles
-// on one XCD).
+// Two kernels:
+//  - gemm_q8_dma (Q8_0 weights, K % 64 == 0, even N, with a workspace): every
+//    operand streamed into LDS by DMA, eight waves per workgroup, B fragments
+//    dequantised in registers (described at the kernel).  With few output
+//    tiles K is split into slices whose partial products a small kernel sums
+//    in slice order.
+//  - gemm_bf16_kernel (dense f32 weights, and Q8_0 shapes off the DMA path or
+//    without a workspace): a 256-thread workgroup computes a 128 x 128 tile of
+//    C over a slice of K, four waves of 64 x 64 with 4 x 4 MFMA 16x16x32 tiles;
+//    both operands register-staged into LDS as bf16 rows (K contiguous, padded
+//    by 8 elements against bank conflicts), double-buffered.  Its K slices
+//    write partial products to the workspace when there is one, else add them
+//    into a zeroed output with f32 atomics.
+// Block ids go to the XCDs round-robin; with the tile index n-fastest the m
+// tiles that share a weight tile land on one XCD whenever the n-tile count is
+// a multiple of 8.
 #include "qdec_internal.h"
 
 namespace qdec {
@@ -229,28 +230,32 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a)
     }
 }
 
-// ----------------------------------------------------------- pipelined --
-// Q8_0 GEMM for grids that fill the chip without K splits (>= 256 tiles of
-// 128 x 128, K % 64 == 0, n_out % 8 == 0).  The register-staged kernel above
-// waits a full memory latency every 64 k (one K step of prefetch); here every
-// operand streams global->LDS by DMA (global_load_lds, 16 bytes a lane) into a
-// ring of P = 4 super-stages of 64 k, so three super-stages are in flight
-// while one is consumed:
-//   x  : bf16 rows (rounded once into the workspace by x_to_bf16), 128 bytes
-//        of a row per 8 lanes, chunk c of row r stored at c ^ (r & 7) against
-//        LDS bank conflicts;
-//   W  : raw int8 rows, 64 bytes each;
-//   d  : the block-major scale plane, one 16-byte load per lane covering two
-//        blocks x 128 rows.
-// Each 32-k compute stage dequantises its W half-tile from LDS into one of
-// three bf16 buffers (two stages ahead of the MFMAs that read it), loads the
-// A and B fragments of the next stage while the current stage's MFMAs run,
-// and ends with one barrier.  The scheduling fences interleave LDS reads,
-// MFMAs and the dequantisation VALU work; all waits on the DMA counter are
-// explicit (vmcnt counts whole super-stages of PER instructions).
+// ------------------------------------------------------------ DMA-fed --
+// Q8_0 GEMM with every operand streamed global -> LDS by DMA
+// (global_load_lds), for K % 64 == 0 and even N.  A 512-thread workgroup
+// (eight waves, two per SIMD) computes a 128 x 128 tile of C over a K slice:
+// wave w takes k-half w/4 of every 64-k stage and the 128 x 32 block of
+// output columns 32*(w%4), i.e. 8 x 2 MFMA 16x16x32 tiles whose B fragments
+// it dequantises itself from the int8 bytes in LDS (each weight is
+// dequantised once per workgroup; nothing is written back to LDS).  The two
+// k-halves are added through LDS at the end.
+//
+// Ring of P = 4 stages, one LDS array per stage so that the compiler's
+// wait-count tracking tells the DMAs into one stage from reads of another:
+//   X (16 KB): x in bf16 (rounded once into the workspace by x_to_bf16), row r
+//              of the tile at byte 128 r, 16-byte chunk c at position c ^ (r & 7);
+//   W (8 KB) : raw int8 rows, 64 bytes each, chunk c at position c ^ ((r >> 1) & 3);
+//   D        : the stage's 256 scales (2 blocks x 128 rows) from the
+//              block-major scale plane, four bytes per lane.
+// Every lane of every wave issues the same four DMA instructions per stage
+// (a DMA under a branch defeats the compiler's wait tracking), so the vmcnt
+// waits are compile-time constants.  Stage s: issue the DMAs of stage s+3,
+// read the fragments of stage s+1 and dequantise its B while the MFMAs of
+// stage s run, wait until this wave's share of stage s+2 has landed, barrier.
+// Each LDS read is one pointer step from its stage array (a 32-bit offset
+// computed once), which keeps the access provably inside that array.
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ inline void dma16(const void* g, lds_void* l) { __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0); }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int N>
 __device__ inline void wait_vm()
@@ -259,15 +264,16 @@ __device__ inline void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-struct PipeArgs {
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+struct DmaArgs {
     const __bf16* xb;      // M x K bf16 (workspace)
-    const int8_t* q;       // N x K
-    const uint16_t* dT;    // (K/32) x N
-    float* out;            // M x N
+    const int8_t* q;       // N x K int8 q plane
+    const uint16_t* dT;    // (K/32) x N scales, block-major
+    float* out;            // M x N, or the slice partials part[slice][M][N]
     int64_t M, N, K, ntiles;
-    int64_t kslice;        // K per split (multiple of 64)
-    int splits;            // > 1: slice s writes its partial tiles to part[s][M][N]
-    float* part;           // splits * M * N f32 (workspace), summed by sum_slices
+    int64_t kslice;        // K per slice (multiple of 64)
+    int splits;
 };
 
 __global__ __launch_bounds__(256) void x_to_bf16(const float4* __restrict__ x, bf16x4* __restrict__ xb, int64_t n4)
@@ -276,186 +282,174 @@ __global__ __launch_bounds__(256) void x_to_bf16(const float4* __restrict__ x, b
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) xb[i] = to_bf16x4(x[i]);
 }
 
-constexpr int kPipeStages = 4;
+constexpr int kDmaStages = 4;
+constexpr int kDmaSlot = 16384 + 8192 + 768;   // X | W | D (512 B of scales + 256 B overflow)
 
-#define QDEC_RING(name, type, n)                                                                        \
-    __shared__ __attribute__((aligned(1024))) type name##0[n], name##1[n], name##2[n], name##3[n]
-#define QDEC_PICK(name, u) ((u) == 0 ? name##0 : (u) == 1 ? name##1 : (u) == 2 ? name##2 : name##3)
-
-__global__ __launch_bounds__(256) void gemm_q8_pipe(PipeArgs a)
+__global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
 {
-    constexpr int PBM = 128, PBN = 128, P = kPipeStages;
-    constexpr int WGN = 2, NWAVE = 4, TM = 4, TN = 4;          // 2 x 2 waves of 64 x 64
-    constexpr int XI = PBM * 128 / 1024, XPW = XI / NWAVE;    // x: 8 rows x 128 B per instruction
-    constexpr int WI = PBN * 64 / 1024, WPW = WI / NWAVE;     // W: 16 rows x 64 B per instruction
-    constexpr int PER = XPW + WPW + 1;                         // DMA instructions per super-stage and wave
-    static_assert(XI % NWAVE == 0 && WI % NWAVE == 0 && PBN * 4 <= 1024, "tile split");
-    QDEC_RING(XR, __bf16, PBM * 64);
-    QDEC_RING(WR, int8_t, PBN * 64);
-    QDEC_RING(DR, uint16_t, 512);
-    __shared__ __attribute__((aligned(1024))) __bf16 WB0[PBN * 32], WB1[PBN * 32], WB2[PBN * 32];
-
-    // block id -> (k slice, n tile, m tile), k fastest
+    constexpr int P = kDmaStages, U = 2 * P, BM = 128, BN = 128;
+    __shared__ __attribute__((aligned(1024))) char S0[kDmaSlot], S1[kDmaSlot], S2[kDmaSlot], S3[kDmaSlot];
+#define QDEC_SLOT(u) ((u) == 0 ? S0 : (u) == 1 ? S1 : (u) == 2 ? S2 : S3)
     const int64_t id = blockIdx.x;
     const int64_t slice = id % a.splits, tile = id / a.splits;
-    const int64_t n0 = (tile % a.ntiles) * PBN, m0 = (tile / a.ntiles) * PBM;
+    const int64_t n0 = (tile % a.ntiles) * BN, m0 = (tile / a.ntiles) * BM;
     const int64_t kbeg = slice * a.kslice;
     const int64_t klen = kbeg + a.kslice < a.K ? a.kslice : a.K - kbeg;
+    const int ns = (int)(klen >> 6);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int nk = (int)(klen >> 5);  // 32-k compute stages of this slice
-    const int ns = nk >> 1;           // 64-k super-stages
+    const int wk = wave >> 2, wn = wave & 3;
 
-    // x rows: instruction i of this wave covers tile rows 8(wave*XPW + i) ..+7;
-    // lane -> row + lane/8, its 16 bytes land at LDS chunk lane%8, which holds
-    // global chunk (lane%8) ^ (row & 7)
-    const __bf16* xsrc[XPW];
+    // DMA sources at stage 0 of this slice (stage st adds 64 st elements)
+    const __bf16* xsrc[2];
 #pragma unroll
-    for (int i = 0; i < XPW; ++i) {
-        const int r = 8 * (wave * XPW + i) + (lane >> 3);
+    for (int i = 0; i < 2; ++i) {
+        const int r = (i * 8 + wave) * 8 + (lane >> 3);        // chunk slot (8i + wave)*64 + lane
         const int c = (lane & 7) ^ (r & 7);
         int64_t gr = m0 + r;
-        gr = gr < a.M ? gr : a.M - 1;                          // edge rows repeat the last row
+        gr = gr < a.M ? gr : a.M - 1;                          // rows past M repeat the last (never stored)
         xsrc[i] = a.xb + gr * a.K + kbeg + c * 8;
     }
-    int wi[WPW];
-    const int8_t* wsrc[WPW];
-#pragma unroll
-    for (int i = 0; i < WPW; ++i) {
-        wi[i] = wave * WPW + i;
-        const int r = wi[i] * 16 + (lane >> 2);
+    const int8_t* wsrc;
+    {
+        const int r = wave * 16 + (lane >> 2);                 // chunk slot wave*64 + lane
+        const int c = (lane & 3) ^ ((r >> 1) & 3);
         int64_t gn = n0 + r;
         gn = gn < a.N ? gn : a.N - 1;
-        wsrc[i] = a.q + gn * a.K + kbeg + (lane & 3) * 16;
+        wsrc = a.q + gn * a.K + kbeg + c * 16;
     }
-    // scales: lane l < 32 loads 8 rows of block 2s + l/16 (rows 8(l%16)..); lanes
-    // 32..63 repeat the load into the unused upper half of the slot
-    const int dl = lane & 31;
-    const int dblk = dl >> 4, drow = (dl & 15) * 8;
-    int64_t gdr = n0 + drow;
-    gdr = gdr + 8 <= a.N ? gdr : a.N - 8;                     // n_out % 8 == 0: only whole groups past the edge
-    const uint16_t* dsrc = a.dT + (kbeg / 32 + dblk) * a.N + gdr;
+    // scales: word w*16 + L holds block (L%16)/8, rows 16(w + L/16) + 2(L%8)
+    // + {0,1}: lanes L >= 16 write the words of the next waves, with the same
+    // values those waves write (words past 127 land in the overflow)
+    const uint16_t* dsrc;
+    {
+        const int vw = wave + (lane >> 4), vl = lane & 15;
+        int64_t gn = n0 + vw * 16 + 2 * (vl & 7);
+        gn = gn < a.N - 1 ? gn : a.N - 2;                      // N even: pairs never straddle the edge
+        dsrc = a.dT + (kbeg / 32 + (vl >> 3)) * a.N + gn;
+    }
+    auto issue = [&](int st, int u) {
+        const int sc = st < ns ? st : ns - 1;                  // past the end: reload the last stage
+        char* sb = QDEC_SLOT(u);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(xsrc[i] + (int64_t)sc * 64, (lds_void*)(sb + (i * 8 + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(wsrc + (int64_t)sc * 64, (lds_void*)(sb + 16384 + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dsrc + (int64_t)sc * 2 * a.N, (lds_void*)(sb + 24576 + wave * 64), 4, 0, 0);
+    };
+    // fragment offsets inside a stage array (bytes)
+    uint32_t xoff[8], woff[2], doff[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = i * 16 + (lane & 15);
+        xoff[i] = r * 128 + (((uint32_t)wk * 4 + (lane >> 4)) ^ (r & 7)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t r = wn * 32 + j * 16 + (lane & 15);
+        const uint32_t kb = wk * 32 + (lane >> 4) * 8;         // byte of the 64-byte row
+        woff[j] = 16384 + r * 64 + ((kb >> 4) ^ ((r >> 1) & 3)) * 16 + (kb & 8);
+        doff[j] = 24576 + 2 * ((r >> 4) * 32 + wk * 16 + (r & 15));
+    }
+    bf16x8 fa[2][8], fb[2][2];
+    u32x2 fq[2][2];
+    uint16_t fd[2][2];
+    auto frags = [&](int u, int f) {
+        const char* sb = QDEC_SLOT(u);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            fq[f][j] = *reinterpret_cast<const u32x2*>(sb + woff[j]);
+            fd[f][j] = *reinterpret_cast<const uint16_t*>(sb + doff[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[f][i] = *reinterpret_cast<const bf16x8*>(sb + xoff[i]);
+    };
+    // B fragment j of set f: 8 weights d * q of one row, exact in f32, rounded to bf16
+    auto deq = [&](int f, int j) -> bf16x8 {
+        const float d = fp16_bits_to_f32(fd[f][j]);
+        const uint32_t w[2] = {fq[f][j][0], fq[f][j][1]};
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)(d * (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xff));
+        return v;
+    };
+    f32x4 acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int st, int slot) {
-        const int sc = st < ns ? st : ns - 1;                  // past the end: reload the last super-stage
-        __bf16* xd = QDEC_PICK(XR, slot);
-        int8_t* wd = QDEC_PICK(WR, slot);
-        uint16_t* dd = QDEC_PICK(DR, slot);
-#pragma unroll
-        for (int i = 0; i < XPW; ++i) dma16(xsrc[i] + (int64_t)sc * 64, (lds_void*)(xd + (wave * XPW + i) * 512));
-#pragma unroll
-        for (int i = 0; i < WPW; ++i) dma16(wsrc[i] + (int64_t)sc * 64, (lds_void*)(wd + wi[i] * 1024));
-        dma16(dsrc + (int64_t)(2 * sc) * a.N, (lds_void*)dd);
-    };
-    auto wbuf = [&](int k) -> __bf16* { return k == 0 ? WB0 : k == 1 ? WB1 : WB2; };
-    // dequantisation: thread t takes row t/2 and 16 weights (half t%2) of the
-    // 32-k half of the super-stage
-    const int wr = threadIdx.x >> 1, wh = threadIdx.x & 1;
-    auto dequant = [&](int t, int slot, int wbk) {
-        __bf16* wb = wbuf(wbk);
-        const int h2 = t & 1;
-        const uint4 qv = *reinterpret_cast<const uint4*>(QDEC_PICK(WR, slot) + wr * 64 + h2 * 32 + wh * 16);
-        const float dd = fp16_bits_to_f32(QDEC_PICK(DR, slot)[h2 * PBN + wr]);
-        const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bf16x8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = (__bf16)(dd * (float)(int8_t)((w[2 * h + (e >> 2)] >> (8 * (e & 3))) & 0xff));
-            const int c = (wh * 2 + h) ^ ((wr >> 1) & 3);
-            *reinterpret_cast<bf16x8*>(&wb[wr * 32 + c * 8]) = v;
-        }
-    };
-    bf16x8 fa[2][TM], fb[2][TN];
-    auto frags = [&](int t, int slot, int wbk, int f) {
-        const __bf16* xs = QDEC_PICK(XR, slot);
-        const __bf16* wb = wbuf(wbk);
-        const int h2 = t & 1;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = (wm * TM + i) * 16 + (lane & 15);
-            const int c = (h2 * 4 + (lane >> 4)) ^ (r & 7);
-            fa[f][i] = *reinterpret_cast<const bf16x8*>(&xs[r * 64 + c * 8]);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int r = (wn * TN + j) * 16 + (lane & 15);
-            const int c = (lane >> 4) ^ ((r >> 1) & 3);
-            fb[f][j] = *reinterpret_cast<const bf16x8*>(&wb[r * 32 + c * 8]);
-        }
-    };
-    f32x4 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // prologue: super-stages 0..P-2 in flight; 0 and 1 landed
+    // prologue: stages 0..P-2 in flight; 0 and 1 landed everywhere; stage 0's
+    // fragments read and dequantised
 #pragma unroll
     for (int st = 0; st < P - 1; ++st) issue(st, st);
-    wait_vm<PER * (P - 3)>();
+    wait_vm<4 * (P - 3)>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    dequant(0, 0, 0);
-    dequant(1, 0, 1);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the bf16 tiles are written
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    frags(0, 0, 0, 0);
-    // compute stage t (u = t mod 24, so every ring index is a compile-time constant)
-    auto body = [&](const int t, const int u) {
-        if ((u & 1) == 0) issue(t / 2 + P - 1, (u / 2 + P - 1) % P);
+    frags(0, 0);
+    fb[0][0] = deq(0, 0);
+    fb[0][1] = deq(0, 1);
+    auto body = [&](const int s, const int u) {
+        issue(s + P - 1, (u + P - 1) % P);
+        const int f = u & 1;
+        frags((u + 1) % P, f ^ 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[u & 1][i], fb[u & 1][j], acc[i][j], 0, 0, 0);
-        dequant(t + 2, ((u + 2) / 2) % P, (u + 2) % 3);
-        frags(t + 1, ((u + 1) / 2) % P, (u + 1) % 3, (u + 1) & 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // LDS reads of the dequantisation
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // fragment reads
-#pragma unroll
-        for (int k = 0; k < TM * TN - 2; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);    // VALU between MFMAs
-        }
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);        // LDS writes
-        // end of stage t: super-stage (t+3)/2 must have landed
-        if ((u & 1) == 0) wait_vm<PER * (P - 2)>();
-        else wait_vm<PER * (P - 3)>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+        fb[f ^ 1][0] = deq(f ^ 1, 0);
+        fb[f ^ 1][1] = deq(f ^ 1, 1);
+        // this wave's share of stage s+2 has landed; the barrier makes every
+        // wave's share visible and frees stage s-1's array for reuse
+        wait_vm<4 * (P - 3)>();
+        wait_lgkm0();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    int t0 = 0;
-    for (; t0 + 24 <= nk; t0 += 24) {
+    int s0 = 0;
+    for (; s0 + U <= ns; s0 += U) {
 #pragma unroll
-        for (int u = 0; u < 24; ++u) body(t0 + u, u);
+        for (int u = 0; u < U; ++u) body(s0 + u, u);
     }
 #pragma unroll
-    for (int u = 0; u < 24; ++u)
-        if (t0 + u < nk) body(t0 + u, u);
-    wait_vm<0>();   // no DMA may still be writing LDS when the workgroup ends
+    for (int u = 0; u < U; ++u)
+        if (s0 + u < ns) body(s0 + u, u);
+    wait_vm<0>();   // no DMA may still be writing LDS when it is reused or the workgroup ends
+    __syncthreads();
 
+    // the two k-halves: waves wk = 1 write their 128 x 32 partial tile (16 KB
+    // each, one stage array per wave) and waves wk = 0 add it
+    auto red = [&](int idx) -> f32x4* { return reinterpret_cast<f32x4*>(QDEC_SLOT(wn)) + idx; };
+    if (wk == 1) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t n = n0 + (wn * TN + j) * 16 + (lane & 15);
+            for (int j = 0; j < 2; ++j) *red((i * 2 + j) * 64 + lane) = acc[i][j];
+    }
+    __syncthreads();
+    if (wk == 1) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] += *red((i * 2 + j) * 64 + lane);
+    // D layout of the 16x16 MFMA: lane holds column lane % 16, rows 4 (lane / 16) + e
+    float* dst = a.out + (a.splits > 1 ? slice * a.M * a.N : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + wn * 32 + j * 16 + (lane & 15);
             if (n >= a.N) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t m = m0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + e;
-                if (m >= a.M) continue;
-                if (a.splits == 1) a.out[m * a.N + n] = acc[i][j][e];
-                else a.part[(slice * a.M + m) * a.N + n] = acc[i][j][e];
+                const int64_t m = m0 + i * 16 + (lane >> 4) * 4 + e;
+                if (m < a.M) dst[m * a.N + n] = acc[i][j][e];
             }
         }
     }
+#undef QDEC_SLOT
 }
 
 // out = sum over the K slices of their partial products, slice 0 first (a
@@ -480,39 +474,21 @@ __global__ __launch_bounds__(256) void sum_slices(const float* __restrict__ part
     }
 }
 
-#undef QDEC_RING
-#undef QDEC_PICK
-
-// The pipelined kernel holds 124 KB of LDS, so one workgroup per CU: its grid
-// should be whole rounds of 256 workgroups.  K splits (slices >= 512 deep and
-// multiples of 64) bring small grids up; each slice writes its M*N partial
-// products to the workspace and a small kernel sums them (f32 atomics into a
-// zeroed output cost ~12 us per 4M), up to 4M partial values.  Up to 4
-// splits the grid must reach 256 workgroups; the 8-way split is also taken at
-// 192 (three quarters of a round, one workgroup per CU).  Measured:
-// 128x8192x3072 split 4: 32.0 us (36.1 unpipelined); 512x8192x3072: 52.7 us
-// (74.5); 128x3072x8192 split 8 (192 workgroups, 3.1M atomics): 30.1 us
-// against 36.3 unpipelined; 512x3072x8192 split 4 (6.3M atomics, 1.5
-// rounds): 84 us against 70.5 unpipelined, and split 2 (192 workgroups):
-// 72.3, so neither is taken.
-int pipe_splits(int64_t M, int64_t N, int64_t K)
+// The DMA-fed kernel holds ~135 KB of LDS: one workgroup per CU.  K is split
+// into up to 8 slices (whole 64-k stages, at least 8 per slice) until the grid
+// reaches about 192 workgroups; more slices cost more in partial products than
+// the extra CUs give (measured: 128x8192x3072 split 3: 23.7 us, split 4: 24.7;
+// 512x3072x8192 split 2: 47.3 us, split 4: 54.8).
+int dma_splits(int64_t M, int64_t N, int64_t K)
 {
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t stages = K / 64;
     int s = 1;
-    while (s < 8 && tiles * s < 256 && K % (64 * 2 * s) == 0 && K / (2 * s) >= 512) s *= 2;
+    while (s < 8 && tiles * (s + 1) <= 192 && stages / (s + 1) >= 8) ++s;
     return s;
 }
 
-bool pipe_ok(int64_t M, int64_t N, int64_t K)
-{
-    if (K % 64 != 0 || N % 8 != 0 || N < 128) return false;
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    const int s = pipe_splits(M, N, K);
-    const int64_t wg = tiles * s;
-    const int64_t rounds = (wg + 255) / 256;
-    const bool full = (wg >= 256 || (s == 8 && wg >= 192)) && 4 * wg >= 3 * rounds * 256;   // >= 75% of the last round busy
-    return full && (s == 1 || M * N * s <= (int64_t)1 << 22);
-}
+bool dma_ok(int64_t N, int64_t K) { return K % 64 == 0 && N % 2 == 0 && N >= 2; }
 
 __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, int64_t n4, float* __restrict__ tail,
                                                    int64_t ntail)
@@ -580,13 +556,16 @@ int64_t reg_part_bytes(int64_t M, int64_t N, int64_t K)
 }  // namespace
 
 // x rounded to bf16, then (with a K split) the slices' partial products.
-static int64_t pipe_x_bytes(int64_t n_in, int64_t batch) { return align_up(batch * n_in * 2, kAlign); }
+static int64_t dma_x_bytes(int64_t n_in, int64_t batch) { return align_up(batch * n_in * 2, kAlign); }
+
+// K per slice of the DMA-fed kernel: whole 64-k stages, the last slice shorter.
+static int64_t dma_kslice(int64_t K, int splits) { return (K / 64 + splits - 1) / splits * 64; }
 
 int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
 {
-    if (!pipe_ok(batch, n_out, n_in)) return reg_part_bytes(batch, n_out, n_in);
-    const int s = pipe_splits(batch, n_out, n_in);
-    return pipe_x_bytes(n_in, batch) + (s > 1 ? (int64_t)s * batch * n_out * 4 : 0);
+    if (!dma_ok(n_out, n_in)) return reg_part_bytes(batch, n_out, n_in);
+    const int s = dma_splits(batch, n_out, n_in);
+    return dma_x_bytes(n_in, batch) + (s > 1 ? (int64_t)s * batch * n_out * 4 : 0);
 }
 
 int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
@@ -597,34 +576,35 @@ int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                             float* out, void* workspace, hipStream_t s)
 {
-    if (workspace && pipe_ok(batch, n_out, n_in)) {
+    if (workspace && dma_ok(n_out, n_in)) {
         const int64_t n4 = batch * n_in / 4;   // n_in % 64 == 0
         int64_t blocks = (n4 + 255) / 256;
         if (blocks > 2048) blocks = 2048;
         hipLaunchKernelGGL(x_to_bf16, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(x),
                            static_cast<bf16x4*>(workspace), n4);
         count_launch();
-        PipeArgs p{};
+        DmaArgs p{};
         p.xb = static_cast<const __bf16*>(workspace);
         p.q = w.q;
         p.dT = w.dT;
-        p.out = out;
         p.M = batch;
         p.N = n_out;
         p.K = n_in;
         p.ntiles = (n_out + 127) / 128;
-        p.splits = pipe_splits(batch, n_out, n_in);
-        p.kslice = n_in / p.splits;
-        p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pipe_x_bytes(n_in, batch));
+        const int splits = dma_splits(batch, n_out, n_in);
+        p.kslice = dma_kslice(n_in, splits);
+        p.splits = (int)((n_in + p.kslice - 1) / p.kslice);
+        float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + dma_x_bytes(n_in, batch));
+        p.out = p.splits > 1 ? part : out;
         const int64_t grid = ((batch + 127) / 128) * p.ntiles * p.splits;
-        hipLaunchKernelGGL(gemm_q8_pipe, dim3((unsigned)grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(gemm_q8_dma, dim3((unsigned)grid), dim3(512), 0, s, p);
         count_launch();
         if (p.splits > 1) {
             const int64_t mn = batch * n_out;
             int64_t sb = (mn / 4 + 255) / 256;
             if (sb > 2048) sb = 2048;
             if (sb < 1) sb = 1;
-            hipLaunchKernelGGL(sum_slices, dim3((unsigned)sb), dim3(256), 0, s, p.part, p.splits, mn, out);
+            hipLaunchKernelGGL(sum_slices, dim3((unsigned)sb), dim3(256), 0, s, part, p.splits, mn, out);
             count_launch();
         }
         return hipGetLastError();
@@ -634,9 +614,9 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
     a.q = w.q;
     a.d = w.d;
     a.out = out;
-    // a workspace given for a shape off the pipelined path holds the slices'
+    // a workspace given for a shape off the DMA-fed path holds the slices'
     // partial products (q8_gemm_workspace_bytes sized it)
-    a.part = workspace && a.splits > 1 && !pipe_ok(batch, n_out, n_in) ? static_cast<float*>(workspace) : nullptr;
+    a.part = workspace && a.splits > 1 && !dma_ok(n_out, n_in) ? static_cast<float*>(workspace) : nullptr;
     return launch(a, true, s);
 }
 

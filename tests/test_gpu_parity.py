@@ -348,12 +348,19 @@ def test_launch_counter_witness(qd):
     assert qd.launch_count() >= before + 2
 
 
-# The DMA-pipelined Q8_0 GEMM (>= 256 workgroups of 128 x 128 tiles with up to
-# 4 K splits, n_in % 64 == 0, n_out % 8 == 0): x rounded to bf16 in the stream
-# workspace, then the kernel (2 launches), plus the zero fill when K is split.
+# The DMA-fed Q8_0 GEMM (n_in % 64 == 0, even n_out): x rounded to bf16 in the
+# stream workspace, then the kernel (2 launches), plus the slice sum when K is
+# split (while the grid of 128 x 128 tiles stays at most 192 workgroups and each
+# slice keeps 8 or more 64-k stages).  Ragged M and N tiles, one-stage K, odd
+# tile counts and uneven slices are included; odd n_out takes the
+# register-staged kernel (1 launch, no split at this size).
 @pytest.mark.parametrize("n_out,n_in,batch,launches", [(2048, 256, 2048, 2), (2040, 192, 2000, 2),
                                                        (4096, 64, 1000, 2), (2048, 2048, 512, 3),
-                                                       (3072, 4096, 128, 3)])   # 24 tiles, 8-way split
+                                                       (3072, 4096, 128, 3),    # 24 tiles, 8-way split
+                                                       (130, 128, 3, 2), (202, 640, 77, 2),
+                                                       (66, 1024, 300, 3),      # 3 tiles, 2 slices
+                                                       (1000, 1600, 9, 3),      # 8 tiles, 3 uneven slices
+                                                       (129, 128, 5, 1)])       # odd n_out
 def test_q8_0_gemm_pipelined(qd, n_out, n_in, batch, launches):
     raw = q8_weights(7100 + n_in, n_out, n_in)
     x = synth.normal_f32(7101 + batch, (batch, n_in))
@@ -369,8 +376,8 @@ def test_q8_0_gemm_pipelined(qd, n_out, n_in, batch, launches):
 
 
 def test_q8_0_gemm_pipelined_long_k_sampled(qd):
-    """n_in = 1600: 50 compute stages, past one 24-stage unrolled block and
-    into the tail; rows sampled against the oracle."""
+    """n_in = 1600: 25 stages of 64, three 8-stage unrolled blocks and a
+    one-stage tail; rows sampled against the oracle."""
     n_out, n_in, batch = 4096, 1600, 1024            # 32 x 8 tiles
     raw = q8_weights(7110, n_out, n_in)
     x = synth.normal_f32(7111, (batch, n_in))
