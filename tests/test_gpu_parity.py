@@ -410,3 +410,45 @@ def test_q8_0_gemm_capture_without_workspace(qd):
     ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
     check_f32(host(out), ref, S, "gemm captured", rel=BF16_REL, abs_=0.0)
     del g
+
+
+def test_graph_replay_after_workspace_growth(qd):
+    """A graph captured on a stream holds the address of that stream's
+    workspace.  An eager call that grows the workspace afterwards retires the
+    old buffer instead of freeing it, so every replay still reads valid memory
+    and matches the oracle (eager work and syncs between the replays)."""
+    s = torch.cuda.Stream()
+    n_out, n_in, batch = 256, 256, 128                 # DMA-fed GEMM: x in bf16 in the workspace
+    raw = q8_weights(8400, n_out, n_in)
+    x = synth.normal_f32(8401, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    out = torch.empty((batch, n_out), device=xd.device)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    with torch.cuda.stream(s):
+        qd.q8_0_gemm_batched(w, n_in, n_out, xd, out=out)     # makes the small workspace
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qd.q8_0_gemm_batched(w, n_in, n_out, xd, out=out)
+    # a much larger product on the same stream grows its workspace
+    big_out, big_in, big_b = 4096, 4096, 512
+    raw_b = q8_weights(8402, big_out, big_in)
+    xb = synth.normal_f32(8403, (big_b, big_in))
+    wb, xbd = dev(raw_b), dev(xb)
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            ob = qd.q8_0_gemm_batched(wb, big_in, big_out, xbd)
+            junk = torch.randn(8 << 20, device=xd.device)     # fresh allocations on the device
+        s.synchronize()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_f32(host(out), ref, S, f"replay {rep} after workspace growth", rel=BF16_REL, abs_=0.0)
+        del junk
+    rb, Sb = oracle.q8_0_gemv_f64(raw_b, big_in, big_out, xb.astype(np.float64))
+    got = host(ob).astype(np.float64)
+    assert np.all(np.abs(got - rb) <= BF16_REL * Sb)
+    del g
+
