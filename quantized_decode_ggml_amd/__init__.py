@@ -45,6 +45,7 @@ _SIGS = {
     "qdec_attention_decode": [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P],
     "q6k_dequantize": [_P, _I, _I, _P, _P],
     "q8_0_gemv_topk": [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P],
+    "q8_0_gemv_topk_noalloc": [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P],
     "qdec_rmsnorm": [_P, _I, _I, _P, ctypes.c_float, _P, _P],
     "q8_0_rmsnorm_qkv": [_P, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P],
     "q8_0_attn_out_ffn": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_float, _P, _P],
@@ -188,6 +189,15 @@ def q8_0_gemv_topk(w, n_in, n_out, x, k, logits=None, top_idx=None, top_val=None
     _check(lib.q8_0_gemv_topk(_ptr(w), n_in, n_out, batch, _ptr(x), k, _ptr(logits), _ptr(top_idx),
                               _ptr(top_val), _stream(stream)))
     _track(w)
+    return top_idx, top_val, logits
+
+
+def q8_0_gemv_topk_noalloc(w, n_in, n_out, x, k, logits, top_idx, top_val, stream=None):
+    """q8_0_gemv_topk without any device allocation: w must be prepared, and the
+    outputs are the caller's (no tensor is created here)."""
+    batch = _batch(x, n_in)
+    _check(lib.q8_0_gemv_topk_noalloc(_ptr(w), n_in, n_out, batch, _ptr(x), k, _ptr(logits), _ptr(top_idx),
+                                      _ptr(top_val), _stream(stream)))
     return top_idx, top_val, logits
 
 

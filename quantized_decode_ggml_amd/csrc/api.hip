@@ -102,7 +102,7 @@ hipError_t launch_copy_of(int type, const void* w, int64_t n_in, int64_t n_out, 
 // copy that a stream capture cannot make or wait for is reported as absent
 // (*out = nullptr, QDEC_OK) instead of as an error.
 int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s, const void** out,
-             bool wait = false, bool optional = false)
+             bool wait = false, bool optional = false, bool noalloc = false)
 {
     *out = nullptr;
     int dev = 0;
@@ -117,6 +117,12 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_cache.find(key);
     if (it == g_cache.end()) {
+        // the allocation-free entry point never makes a copy
+        if (noalloc) {
+            if (optional) return QDEC_OK;
+            return fail(QDEC_EINVAL, "weight %p has no repacked copy: call qdec_prepare first (this entry point "
+                                     "allocates nothing)", w);
+        }
         // a repack allocates device memory, which a captured graph cannot do
         if (capture != hipStreamCaptureStatusNone) {
             if (optional) return QDEC_OK;
@@ -250,10 +256,12 @@ int finish(hipError_t e, const char* what)
     return QDEC_OK;
 }
 
+// fixed_ws: a caller-provided workspace of at least q8_mfma_workspace_bytes
+// (the allocation-free entry point); with noalloc no repacked copy is made.
 int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw, int64_t n_in,
                    const int64_t* rows, int64_t batch, const float* x, const float* residual,
                    float* const* outs, int nout, hipStream_t s, const float* norm_w = nullptr,
-                   float eps = 0.0f)
+                   float eps = 0.0f, void* fixed_ws = nullptr, bool noalloc = false)
 {
     for (int k = 0; k < nw; ++k) QDEC_TRY(check_ptr(fn, "weight", ws[k], 2));
     QDEC_TRY(check_ptr(fn, "x", x, 16));
@@ -272,7 +280,7 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
     p.nseg = nw;
     for (int k = 0; k < nw; ++k) {
         const void* buf = nullptr;
-        QDEC_TRY(repacked(ws[k], QDEC_TYPE_Q8_0, n_in, rows[k], s, &buf));
+        QDEC_TRY(repacked(ws[k], QDEC_TYPE_Q8_0, n_in, rows[k], s, &buf, false, false, noalloc));
         p.w[k] = q8_view(buf, n_in, rows[k]);
         p.rows[k] = rows[k];
         p.out[k] = outs[k < nout ? k : 0];
@@ -295,12 +303,12 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
         bool have = true;
         for (int k = 0; k < nw && have; ++k) {
             const void* tb = nullptr;
-            QDEC_TRY(repacked(ws[k], kTypeQ8_0Tiled, n_in, rows[k], s, &tb, false, true));
+            QDEC_TRY(repacked(ws[k], kTypeQ8_0Tiled, n_in, rows[k], s, &tb, false, true, noalloc));
             if (tb) tiles[k] = q8t_view(tb, n_in, rows[k]);
             else have = false;
         }
-        void* wsp = nullptr;
-        if (have) QDEC_TRY(stream_workspace(s, q8_mfma_workspace_bytes(n_in), &wsp));
+        void* wsp = fixed_ws;
+        if (have && !wsp && !noalloc) QDEC_TRY(stream_workspace(s, q8_mfma_workspace_bytes(n_in), &wsp));
         if (have && wsp) return finish(launch_q8_0_gemv_mfma(p, tiles, wsp, s), fn);
     }
     return finish(launch_q8_0_gemv(p, s), fn);
@@ -324,6 +332,40 @@ int q8_normed_product(GemvMode mode, const char* fn, const void* const* ws, int 
         return fail(QDEC_EINVAL, "%s: scratch overlaps the input", fn);
     QDEC_TRY(finish(launch_rmsnorm(x, n_in, batch, norm_w, eps, scratch, s), fn));
     return q8_gemv_common(mode, fn, ws, nw, n_in, rows, batch, scratch, nullptr, outs, nout, s);
+}
+
+// ------------------------------------------------- allocation-free scratch --
+// The scratch of q8_0_gemv_topk_noalloc: one static device array, which every
+// GPU the library runs on holds (its own copy) until the process ends.  In
+// host code `scratch` only names the symbol; its device address on each GPU
+// comes from hipGetSymbolAddress, taken once per device (with that device
+// current) on the entry point's first call there and kept.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)QDEC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+int noalloc_scratch(void** out)
+{
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(QDEC_EUNSUPPORTED, "device %d out of range for the static scratch", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(QDEC_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        e != hipSuccess ? hipGetErrorString(e) : "null address");
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return QDEC_OK;
 }
 
 }  // namespace
@@ -435,6 +477,38 @@ int q8_0_gemv_topk(const void* w, int64_t n_in, int64_t n_out, int64_t batch, co
         if (!wsp) return fail(QDEC_EINVAL, "%s: top-k workspace vanished", fn);
     }
     return finish(launch_topk(logits, n_out, batch, (int)k, wsp, top_idx, top_val, stream), fn);
+}
+
+int q8_0_gemv_topk_noalloc(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, int64_t k,
+                           float* logits, int32_t* top_idx, float* top_val, hipStream_t stream)
+{
+    const char* fn = "q8_0_gemv_topk_noalloc";
+    QDEC_TRY(check_dims(fn, n_in, n_out, batch, 32, QDEC_GEMV_MAX_BATCH));
+    if (k < 1 || k > QDEC_TOPK_MAX || k > n_out)
+        return fail(QDEC_EINVAL, "%s: k=%lld outside [1, min(n_out, %d)]", fn, (long long)k, QDEC_TOPK_MAX);
+    // scratch layout: the split activations of the matrix-core projection
+    // (3..8 batch rows), then the top-k candidate lists
+    const int64_t proj = batch >= 3 ? align_up(q8_mfma_workspace_bytes(n_in), kAlign) : 0;
+    const int64_t need = proj + topk_workspace_bytes(n_out, batch, (int)k);
+    if (need > kNoAllocScratchBytes)
+        return fail(QDEC_EINVAL, "%s: needs %lld bytes of scratch, above the %lld-byte static array (fewer batch "
+                    "rows, a smaller k or a smaller n_out fit)", fn, (long long)need, (long long)kNoAllocScratchBytes);
+    QDEC_TRY(check_ptr(fn, "top_idx", top_idx, 4));
+    QDEC_TRY(check_ptr(fn, "top_val", top_val, 4));
+    QDEC_TRY(check_ptr(fn, "logits", logits, 4));
+    const int64_t lb = batch * n_out * 4, tb = batch * k * 4;
+    if (overlaps(top_idx, tb, top_val, tb) || overlaps(top_idx, tb, logits, lb) || overlaps(top_val, tb, logits, lb) ||
+        overlaps(top_idx, tb, x, batch * n_in * 4) || overlaps(top_val, tb, x, batch * n_in * 4))
+        return fail(QDEC_EINVAL, "%s: top_idx, top_val, logits and x must not overlap", fn);
+    void* sp = nullptr;
+    QDEC_TRY(noalloc_scratch(&sp));
+    const void* ws[1] = {w};
+    const int64_t rows[1] = {n_out};
+    float* outs[1] = {logits};
+    QDEC_TRY(q8_gemv_common(kPlain, fn, ws, 1, n_in, rows, batch, x, nullptr, outs, 1, stream, nullptr, 0.0f,
+                            proj > 0 ? sp : nullptr, true));
+    void* tk = need > proj ? static_cast<char*>(sp) + proj : nullptr;
+    return finish(launch_topk(logits, n_out, batch, (int)k, tk, top_idx, top_val, stream), fn);
 }
 
 int qdec_rmsnorm(const float* x, int64_t n, int64_t batch, const float* w, float eps, float* out, hipStream_t stream)
