@@ -84,6 +84,7 @@ int64_t copy_bytes(int type, int64_t n_in, int64_t n_out)
 {
     return type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out)
          : type == kTypeQ8_0Tiled ? q8t_plane_bytes(n_in, n_out)
+         : type == kTypeQ4KTiled ? q4kt_plane_bytes(n_in, n_out)
          : type == QDEC_TYPE_Q6_K ? q6k_plane_bytes(n_in, n_out)
                                   : q4k_plane_bytes(n_in, n_out);
 }
@@ -93,6 +94,7 @@ hipError_t launch_copy_of(int type, const void* w, int64_t n_in, int64_t n_out, 
     const uint8_t* raw = static_cast<const uint8_t*>(w);
     return type == QDEC_TYPE_Q8_0 ? launch_repack_q8_0(raw, n_in, n_out, dst, s)
          : type == kTypeQ8_0Tiled ? launch_repack_q8_0_tiled(raw, n_in, n_out, dst, s)
+         : type == kTypeQ4KTiled ? launch_repack_q4k_tiled(raw, n_in, n_out, dst, s)
          : type == QDEC_TYPE_Q6_K ? launch_repack_q6k(raw, n_in, n_out, dst, s)
                                   : launch_repack_q4k(raw, n_in, n_out, dst, s);
 }
@@ -655,6 +657,12 @@ int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const fl
     QDEC_TRY(check_ptr(fn, "out", out, 4));
     if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4)) return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
     const void* buf = nullptr;
+    if (q4k_mfma_supported(n_in, batch)) {
+        // one row on the matrix cores, from the fragment-tiled copy; inside a
+        // capture that copy may be missing, and the VALU kernel then runs
+        QDEC_TRY(repacked(w, kTypeQ4KTiled, n_in, n_out, stream, &buf, false, true));
+        if (buf) return finish(launch_q4k_gemv_mfma(q4kt_view(buf, n_in, n_out), n_in, n_out, x, out, stream), fn);
+    }
     QDEC_TRY(repacked(w, QDEC_TYPE_Q4_K, n_in, n_out, stream, &buf));
     return finish(launch_q4k_gemv(q4k_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
 }
@@ -722,8 +730,11 @@ int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream
     const void* buf = nullptr;
     QDEC_TRY(repacked(w, type, n_in, n_out, stream, &buf, true));
     // Q8_0 weights also get the fragment-tiled copy of the batched matrix-core
-    // GEMV, so that graphs captured later can use it
+    // GEMV, Q4_K weights that of the one-row matrix-core GEMV, so that graphs
+    // captured later can use them
     if (type == QDEC_TYPE_Q8_0) QDEC_TRY(repacked(w, kTypeQ8_0Tiled, n_in, n_out, stream, &buf, true));
+    if (type == QDEC_TYPE_Q4_K && q4k_mfma_supported(n_in, 1))
+        QDEC_TRY(repacked(w, kTypeQ4KTiled, n_in, n_out, stream, &buf, true));
     return QDEC_OK;
 }
 
@@ -776,11 +787,11 @@ void qdec_clear_cache(void)
 
 int64_t qdec_cache_len(void)
 {
-    // one per (weight, public type, shape): the tiled copy a Q8_0 weight also
-    // gets for the batched matrix-core GEMV is not counted separately
+    // one per (weight, public type, shape): the tiled copies Q8_0 and Q4_K
+    // weights also get for the matrix-core GEMVs are not counted separately
     std::lock_guard<std::mutex> lock(g_mu);
     int64_t n = 0;
-    for (const auto& kv : g_cache) n += kv.first.type != kTypeQ8_0Tiled;
+    for (const auto& kv : g_cache) n += kv.first.type != kTypeQ8_0Tiled && kv.first.type != kTypeQ4KTiled;
     return n;
 }
 

@@ -372,6 +372,7 @@ __global__ __launch_bounds__(256) void q4k_gemv_general(Q4KArgs a)
 }
 
 using KernelFn = void (*)(Q4KArgs);
+using KernelFnT = void (*)(Q4KTView, const float*, int64_t, int64_t, float*);
 
 template <int B, int R>
 KernelFn pick_split(int nch64)
@@ -455,7 +456,254 @@ KernelFn pick_b1_split(int nch64)
     }
 }
 
+// ------------------------------------------------------ matrix cores --
+// One batch row on the integer matrix cores.  A 512-byte tile of the tiled
+// copy is 16 rows x one 64-weight chunk c of the row (low nibbles: sub-block
+// 2c, high nibbles: 2c+1), one K = 64 step of v_mfma_i32_16x16x64_i8: a lane's
+// 8 bytes, masked to their low and high nibbles, are its 16 B operand bytes
+// as they stand (the nibbles 0..15 are int8 values).
+// x is written as a fixed-point number per sub-block b of 32 values:
+// X_k = trunc(x_k * 2^(30 - e_b)), |x_k| < 2^e_b for every k of the block, so
+// |X_k| < 2^30 and x_k = X_k 2^(e_b - 30) + eps_k, |eps_k| < 2^(e_b - 30) (zero
+// whenever |x_k| >= 2^(e_b - 6): the 24-bit significand then fits).  X_k has
+// the signed base-256 digits X = a3 2^24 + a2 2^16 + a1 2^8 + a0, a_j in
+// -128..127 (the bytes of X + 0x80808080, each less 0x80), each an int8.  The
+// A operand's rows are (half h, digit j) = 4h + j: digit j of the sub-block
+// 2c + h values, zero on the other half's k-slots, so the MFMA returns in
+// exact int32, per weight row r and sub-block 2c + h, D_j = sum_k q_k a_j,k
+// (|D_j| <= 32*15*128); rows 8..15 repeat rows 0..7.  Lane r + 16h then forms
+// sum_k q_k X_k = (256 D3 + D2) 2^16 + (256 D1 + D0) (both brackets exact
+// integers below 2^24, one rounding in the fma) and accumulates, as in the
+// factored Q4_K form,
+//     (d sc) * (2^(e_b - 30) sum_k q_k X_k) - (dmin m) * sum_k x_k,
+// d sc exact (11 x 6 significant bits), the power-of-two scaling exact, sum_k
+// x_k the f32 sum of the sub-block's 32 values in a fixed order.
+// A workgroup is RG 16-row groups, each with K split over KS waves of T
+// chunks (T % 4 == 0, so a wave starts on a super-block; T even, for the
+// tile pairs below).  Each thread loads 4 values of x (a quad; two when
+// n_in/4 > threads) and waits for them, then issues every weight load of its
+// wave (T tiles, per tile pair the scale words, per super-block d|dmin);
+// while those are in flight the workgroup writes to LDS the A operands of
+// every chunk (512 bytes: rows 0..7 x 4 k-groups x 16 bytes) and, per
+// sub-block, the sum of x and e_b - 30, found with DPP over the sub-block's 8
+// consecutive quads.
+// Error per output, beyond the f32 rounding of the VALU kernel: at most
+// 2^(e_b - 30) <= 2^-29 max_b |x| per x value, times sum_k d sc q_k.
+template <int KS, int T, int RG>
+__global__ __launch_bounds__(64 * KS * RG) void q4k_gemv_mfma(Q4KTView w, const float* __restrict__ x,
+                                                              int64_t n_in, int64_t n_out, float* __restrict__ out)
+{
+    static_assert(T % 4 == 0 && T >= 4 && T <= 16 && KS * RG <= 16, "T chunks per wave, KS * RG waves");
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int n = 64 * T * KS;     // n_in
+    constexpr int NT = 64 * KS * RG;   // threads
+    constexpr int NQ = n / 4;          // quads of x
+    constexpr int QK = (NQ + NT - 1) / NT;
+    static_assert(QK <= 4, "quads per thread");
+    // A operands (512 bytes a chunk); per sub-block the sum of x and e_b - 30
+    __shared__ __attribute__((aligned(16))) uint8_t lds[8 * n];
+    __shared__ float2 xsc[n / 32];
+    __shared__ float red[RG][KS][16];
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wv / KS, kw = wv % KS;
+    const int64_t groups = q4kt_groups(n_out);
+    const int64_t Gw = (int64_t)blockIdx.x * RG + rg;          // this wave's row group
+    const int64_t G = Gw < groups ? Gw : groups - 1;           // a spare wave reads the last one
+    const int64_t nch = n_in >> 6, nsb = n_in >> 8;
+    const int c0 = kw * T;   // first chunk of this wave, a multiple of 4
+
+    // quads i = tid + k NT of x, live for whole waves (NQ % 64 == 0)
+    float4 xv[QK];
+#pragma unroll
+    for (int k = 0; k < QK; ++k)
+        xv[k] = 64 * wv + k * NT < NQ ? reinterpret_cast<const float4*>(x)[tid + k * NT]
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    // x first: every workgroup reads it, and behind the weight requests of
+    // the whole grid it would land late
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    // every weight load of this wave: the tiles, per tile pair the scale
+    // words of row lane % 16 for tile 2p + lane / 32, per super-block d|dmin
+    u32x2 qv[T];
+    uint32_t smv[T / 2], dmv[T / 4];
+    {
+        const u32x2* qt = reinterpret_cast<const u32x2*>(w.q) + (G * nch + c0) * 64 + lane;
+        const uint32_t* st = w.sm + (G * nch + c0 + (lane >> 5)) * 16 + (lane & 15);
+        const uint32_t* dt = w.dm + (G * nsb + c0 / 4) * 16 + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            qv[t] = __builtin_nontemporal_load(qt + t * 64);
+            if (t % 2 == 0) smv[t / 2] = __builtin_nontemporal_load(st + t * 16);
+            if (t % 4 == 0) dmv[t / 4] = __builtin_nontemporal_load(dt + (t / 4) * 16);
+        }
+    }
+    asm volatile("" ::: "memory");
+    // A operands, sums and scales of x: quad i holds values 4i .. 4i + 3, of
+    // sub-block i / 8, chunk c = i / 16, half h, k-group g, half-run hr
+#pragma unroll
+    for (int k = 0; k < QK; ++k) {
+        if (64 * wv + k * NT >= NQ) break;
+        const int i = tid + k * NT;
+        const float v[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+        uint32_t amax = max(max(__builtin_bit_cast(uint32_t, v[0]) & 0x7fffffffu,
+                                __builtin_bit_cast(uint32_t, v[1]) & 0x7fffffffu),
+                            max(__builtin_bit_cast(uint32_t, v[2]) & 0x7fffffffu,
+                                __builtin_bit_cast(uint32_t, v[3]) & 0x7fffffffu));
+        float sum = ((v[0] + v[1]) + v[2]) + v[3];
+        // over the sub-block's 8 quads (8 consecutive lanes): lane ^ 1, lane ^ 2
+        // (quad permutes), then lane i <-> 7 - i (half-row mirror)
+        amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
+        amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
+        amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x141, 0xF, 0xF, false));
+        sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));
+        sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
+        sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0x141, 0xF, 0xF, false));
+        // amax = m 2^e with 0.5 <= m < 1, so every |x| < 2^e (e = 0 for zeros)
+        const int e_b = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
+        // X = trunc(x 2^(30 - e)), |X| < 2^30; its signed base-256 digits are
+        // the bytes of X + 0x80808080, each less 0x80
+        uint32_t y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = (uint32_t)(int)__builtin_amdgcn_ldexpf(v[e], 30 - e_b) + 0x80808080u;
+        // transpose: word j = digit j of the 4 values
+        uint32_t wd[4];
+        {
+            const uint32_t t01l = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
+            const uint32_t t01h = __builtin_amdgcn_perm(y[1], y[0], 0x07030602u);
+            const uint32_t t23l = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
+            const uint32_t t23h = __builtin_amdgcn_perm(y[3], y[2], 0x07030602u);
+            wd[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u) ^ 0x80808080u;
+            wd[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u) ^ 0x80808080u;
+            wd[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u) ^ 0x80808080u;
+            wd[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u) ^ 0x80808080u;
+        }
+        // A row 4h + j, k-group g of chunk c: bytes 8h + 4hr take digit j of
+        // the quad, bytes 8(1 - h) + 4hr zeros
+        const int c = i >> 4, h = (i >> 3) & 1, g = (i >> 1) & 3, hr = i & 1;
+        uint8_t* cell = lds + 512 * c + 16 * (4 * (4 * h) + g) + 4 * hr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<uint32_t*>(cell + 64 * j + 8 * h) = wd[j];
+            *reinterpret_cast<uint32_t*>(cell + 64 * j + 8 - 8 * h) = 0u;
+        }
+        // a non-finite x makes its sub-block's sum, and so the output, NaN
+        if ((i & 7) == 0)
+            xsc[i >> 3] = make_float2(amax < 0x7f800000u ? sum : __builtin_nanf(""),
+                                      __builtin_bit_cast(float, e_b - 30));
+    }
+    __syncthreads();
+
+    // A operand of lane (row m = lane % 16, k-group g = lane / 16): 16 bytes
+    // of row m % 8
+    const int aoff = 512 * c0 + 16 * (4 * (lane & 7) + (lane >> 4));
+    // D side, per tile pair (2p, 2p + 1): the results of both MFMAs have
+    // rows 8..15 (lanes 32..63) equal to rows 0..7 (lanes 0..31); a lane swap
+    // puts tile 2p in lanes 0..31 and tile 2p + 1 in lanes 32..63, so lane
+    // r + 16 hd + 32 tp holds sub-block 2c + hd of row r, c = c0 + 2p + tp
+    const int hd = (lane >> 4) & 1, tp = lane >> 5, sh = 8 * hd;
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < T / 2; ++p) {
+        i32x4 D[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int t = 2 * p + k;
+            const i32x4 A = *reinterpret_cast<const i32x4*>(lds + aoff + 512 * t);
+            const i32x4 B = {(int)(qv[t][0] & 0x0f0f0f0fu), (int)(qv[t][1] & 0x0f0f0f0fu),
+                             (int)((qv[t][0] >> 4) & 0x0f0f0f0fu), (int)((qv[t][1] >> 4) & 0x0f0f0f0fu)};
+            D[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+        }
+        int Dp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // lanes 32..63 of D[0] (equal to its lanes 0..31) trade places with
+            // lanes 0..31 of D[1]
+            const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)D[0][e], (unsigned)D[1][e], false, false);
+            Dp[e] = (int)sw[0];
+        }
+        const int c = c0 + 2 * p + tp;
+        const float u = __builtin_fmaf((float)(Dp[3] * 256 + Dp[2]), 65536.0f, (float)(Dp[1] * 256 + Dp[0]));
+        const uint32_t dm = dmv[p / 2];
+        const float d = fp16_bits_to_f32((uint16_t)(dm & 0xffff));
+        const float dmin = fp16_bits_to_f32((uint16_t)(dm >> 16));
+        const uint32_t smh = smv[p] >> sh;
+        const float sc = (float)(smh & 0xffu), mn = (float)((smh >> 16) & 0xffu);
+        const float2 xb = xsc[2 * c + hd];
+        // u 2^(e_b - 30) is exact (in range for any normal x); d sc is exact
+        acc = __builtin_fmaf(d * sc, __builtin_amdgcn_ldexpf(u, __builtin_bit_cast(int, xb.y)), acc);
+        acc = __builtin_fmaf(-(dmin * mn), xb.x, acc);
+    }
+    // row r: its sub-block halves and tiles in lanes r + 16 hd + 32 tp, then
+    // the KS waves of its group in order
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if constexpr (KS > 1) {
+        if (lane < 16) red[rg][kw][lane] = acc;
+        __syncthreads();
+        if (kw != 0) return;
+        if (lane < 16) {
+            float s2 = red[rg][0][lane];
+#pragma unroll
+            for (int k = 1; k < KS; ++k) s2 += red[rg][k][lane];
+            acc = s2;
+        }
+    }
+    const int64_t row = Gw * 16 + lane;
+    if (lane < 16 && Gw < groups && row < n_out) out[row] = acc;
+}
+
+// K split: n_in = 64 KS T, T = 8, 12 or 16 chunks a wave: 1024 on 2 waves,
+// 2048 .. 4096 on 4, 6144 and 8192 on 8.  Two row groups share a workgroup
+// (and its x operands) when that still leaves 256 workgroups.
+bool q4k_mfma_shape(int64_t n_in, int* ks, int* t)
+{
+    switch (n_in) {
+        case 1024: *ks = 2; *t = 8; return true;
+        case 2048: *ks = 4; *t = 8; return true;
+        case 3072: *ks = 4; *t = 12; return true;
+        case 4096: *ks = 4; *t = 16; return true;
+        case 6144: *ks = 8; *t = 12; return true;
+        case 8192: *ks = 8; *t = 16; return true;
+        default: return false;
+    }
+}
+
+template <int KS, int T>
+KernelFnT q4k_mfma_pick(int rg)
+{
+    return rg == 2 ? q4k_gemv_mfma<KS, T, 2> : q4k_gemv_mfma<KS, T, 1>;
+}
+
 }  // namespace
+
+bool q4k_mfma_supported(int64_t n_in, int64_t batch)
+{
+    int ks = 0, t = 0;
+    return batch == 1 && q4k_mfma_shape(n_in, &ks, &t);
+}
+
+hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+                                hipStream_t s)
+{
+    int ks = 0, t = 0;
+    if (!q4k_mfma_shape(n_in, &ks, &t)) return hipErrorNotSupported;
+    const int64_t groups = q4kt_groups(n_out);
+    const int rg = groups >= 512 ? 2 : 1;
+    KernelFnT fn = ks == 2 ? q4k_mfma_pick<2, 8>(rg)
+                 : ks == 4 ? (t == 8 ? q4k_mfma_pick<4, 8>(rg) : t == 12 ? q4k_mfma_pick<4, 12>(rg)
+                                                                         : q4k_mfma_pick<4, 16>(rg))
+                           : (t == 12 ? q4k_mfma_pick<8, 12>(rg) : q4k_mfma_pick<8, 16>(rg));
+    if (64LL * ks * t != n_in) return hipErrorNotSupported;
+    hipLaunchKernelGGL(fn, dim3((unsigned)((groups + rg - 1) / rg)), dim3(64 * ks * rg), 0, s, w, x, n_in, n_out,
+                       out);
+    count_launch();
+    return hipGetLastError();
+}
 
 hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                            float* out, hipStream_t s)

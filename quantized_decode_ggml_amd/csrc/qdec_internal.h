@@ -116,6 +116,42 @@ inline Q6KView q6k_view(const void* base, int64_t n_in, int64_t n_out)
 // Cache type of the tiled copy (internal; the public types are the GGML ids).
 constexpr int kTypeQ8_0Tiled = 0x108;
 
+// Fragment-tiled Q4_K matrix (the one-row matrix-core GEMV's copy): rows in
+// groups of 16 (the last padded with zero rows), 64-weight chunks c (chunk c
+// = nibble bytes 32(c%4)..+31 of super-block c/4: low nibbles sub-block 2c,
+// high nibbles 2c+1 of the row).  For group G:
+//   q  : 512-byte tile (G*nch + c), lane l's 8 bytes at 8l = row 16G + l%16,
+//        nibble bytes 32(c%4) + 8(l/16) .. +7 of super-block c/4;
+//   sm : 64-byte tile (G*nch + c), word r = sc[2p] | sc[2p+1] << 8 | m[2p] << 16
+//        | m[2p+1] << 24 of row 16G + r, p = c%4 (the 6-bit values unpacked);
+//   dm : 64-byte tile (G*nsb + sb), word r = d | dmin << 16 (fp16 bits).
+// 148 bytes per 256 weights, as the row-major Q4_K copy.
+constexpr int kTypeQ4KTiled = 0x10C;
+
+struct Q4KTView {
+    const uint8_t* q;
+    const uint32_t* sm;
+    const uint32_t* dm;
+};
+
+__host__ __device__ inline int64_t q4kt_groups(int64_t n_out) { return (n_out + 15) / 16; }
+
+inline int64_t q4kt_plane_bytes(int64_t n_in, int64_t n_out)
+{
+    const int64_t g = q4kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
+    return align_up(g * nch * 512, kAlign) + align_up(g * nch * 64, kAlign) + align_up(g * nsb * 64, kAlign);
+}
+
+inline Q4KTView q4kt_view(const void* base, int64_t n_in, int64_t n_out)
+{
+    const char* p = static_cast<const char*>(base);
+    const int64_t g = q4kt_groups(n_out), nch = n_in / 64;
+    const int64_t off_sm = align_up(g * nch * 512, kAlign);
+    const int64_t off_dm = off_sm + align_up(g * nch * 64, kAlign);
+    return Q4KTView{reinterpret_cast<const uint8_t*>(p), reinterpret_cast<const uint32_t*>(p + off_sm),
+                    reinterpret_cast<const uint32_t*>(p + off_dm)};
+}
+
 inline int64_t q4k_plane_bytes(int64_t n_in, int64_t n_out)
 {
     const int64_t nsb = n_out * (n_in / 256);
@@ -143,6 +179,7 @@ hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, vo
 hipError_t launch_repack_q8_0_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst,
                                     hipStream_t s);
 hipError_t launch_repack_q6k(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s);
+hipError_t launch_repack_q4k_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s);
 hipError_t launch_dequant_q6k(Q6KView w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
 hipError_t launch_q6k_gemv(Q6KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
                            hipStream_t s);
@@ -189,6 +226,12 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
 
 hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                            float* out, hipStream_t s);
+// One batch row on the integer matrix cores from the tiled copy (n_in one of
+// 1024, 2048, 3072, 4096, 6144, 8192); q4k_mfma_supported says whether it
+// takes the shape.
+bool q4k_mfma_supported(int64_t n_in, int64_t batch);
+hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+                                hipStream_t s);
 
 // Batched GEMM over a Q8_0 copy.  With a workspace of q8_gemm_workspace_bytes,
 // on shapes the pipelined kernel takes x is first rounded to bf16 there and the

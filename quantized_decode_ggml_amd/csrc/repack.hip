@@ -100,6 +100,44 @@ __global__ __launch_bounds__(256) void repack_q4k_kernel(const uint16_t* __restr
         dst[k] = make_uint4(words[4 + 4 * k], words[5 + 4 * k], words[6 + 4 * k], words[7 + 4 * k]);
 }
 
+// One thread per (row, super-block) of the tiled Q4_K copy, rows padded to a
+// multiple of 16 with zeros (d = dmin = 0, so padding weights are 0): the
+// super-block's four 32-byte nibble chunks go to the 8-byte slots r, r+16,
+// r+32, r+48 of four tiles, its unpacked scale/min words to the sm tiles and
+// d|dmin to the dm tile.
+__global__ __launch_bounds__(256) void repack_q4k_tiled_kernel(const uint16_t* __restrict__ raw, int64_t n_out,
+                                                               int64_t nsb, int64_t nthreads,
+                                                               uint2* __restrict__ qp, uint32_t* __restrict__ smp,
+                                                               uint32_t* __restrict__ dmp)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nthreads) return;
+    const int64_t row = t / nsb, sb = t % nsb;
+    const int64_t G = row >> 4, r = row & 15, nch = nsb * 4;
+    uint32_t words[36] = {};
+    if (row < n_out) {
+        const uint16_t* src = raw + (row * nsb + sb) * (kQ4KBytes / 2);
+#pragma unroll
+        for (int k = 0; k < 36; ++k) words[k] = (uint32_t)src[2 * k] | ((uint32_t)src[2 * k + 1] << 16);
+    }
+    dmp[(G * nsb + sb) * 16 + r] = words[0];
+    uint8_t sbytes[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) sbytes[k] = (uint8_t)(words[1 + k / 4] >> (8 * (k % 4)));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int64_t c = sb * 4 + p;
+        uint32_t sc0, m0, sc1, m1;
+        unpack_scale_min(sbytes, 2 * p, sc0, m0);
+        unpack_scale_min(sbytes, 2 * p + 1, sc1, m1);
+        smp[(G * nch + c) * 16 + r] = sc0 | (sc1 << 8) | (m0 << 16) | (m1 << 24);
+        // nibble bytes 32p + 8g .. +7 are words 4 + 8p + 2g, +1
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            qp[(G * nch + c) * 64 + r + 16 * g] = make_uint2(words[4 + 8 * p + 2 * g], words[5 + 8 * p + 2 * g]);
+    }
+}
+
 // One thread per (row, Q8_0 block) of the tiled copy, rows padded to a
 // multiple of 16 with zeros: the block's 32 weights go to the four 8-byte
 // slots of its tile that the lanes r, r+16, r+32, r+48 load, its scale to the
@@ -242,6 +280,18 @@ hipError_t launch_repack_q4k(const uint8_t* raw, int64_t n_in, int64_t n_out, vo
     hipLaunchKernelGGL(repack_q4k_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t*>(raw), nblocks, const_cast<uint8_t*>(v.qs),
                        const_cast<uint32_t*>(v.dm), const_cast<uint32_t*>(v.sm));
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_repack_q4k_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s)
+{
+    const Q4KTView v = q4kt_view(dst, n_in, n_out);
+    const int64_t nsb = n_in / 256, nthreads = q4kt_groups(n_out) * 16 * nsb;
+    hipLaunchKernelGGL(repack_q4k_tiled_kernel, dim3(grid_for(nthreads, 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(raw), n_out, nsb, nthreads,
+                       reinterpret_cast<uint2*>(const_cast<uint8_t*>(v.q)), const_cast<uint32_t*>(v.sm),
+                       const_cast<uint32_t*>(v.dm));
     count_launch();
     return hipGetLastError();
 }

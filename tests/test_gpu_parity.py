@@ -192,6 +192,57 @@ def test_q4k_gemv(qd, n_out, n_in, batch):
     check_f32(out, ref, S, f"q4k {n_out}x{n_in} b{batch}")
 
 
+# One batch row of Q4_K runs on the integer matrix cores for n_in = 1024 ..
+# 8192 (multiples of 1024 that split into 4..16 chunks a wave): x is taken
+# there as a 30-bit fixed-point number per 256 values, so inputs whose
+# magnitudes differ widely within a super-block are its hard cases.
+def _x_kind(kind, seed, n_in):
+    x = synth.normal_f32(seed, (1, n_in))
+    if kind == "outliers":      # one value 1e4 times larger in every super-block
+        x[0, 17::256] *= 1e4
+    elif kind == "spread":      # magnitudes over 2^-40 .. 2^40 within each block
+        x *= np.exp2(np.linspace(-40, 40, n_in, dtype=np.float32)).reshape(8, -1).T.reshape(1, -1)[:, :n_in]
+    elif kind == "zeros":       # whole zero super-blocks and powers of two
+        x[0, :256] = 0
+        x[0, 256:512] = np.exp2(np.arange(256) % 16 - 8.0) * np.where(np.arange(256) % 3, 1, -1)
+    elif kind == "tiny":
+        x *= np.float32(1e-30)
+    elif kind == "huge":
+        x *= np.float32(1e30)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("n_in", [1024, 2048, 3072, 4096, 6144, 8192])
+@pytest.mark.parametrize("kind", ["normal", "outliers", "spread", "zeros", "tiny", "huge"])
+def test_q4k_one_row_matrix_core_inputs(qd, n_in, kind):
+    n_out = 37   # ragged: the last 16-row group is partly padding
+    raw = synth.q4k_weights(6200 + n_in, n_out, n_in)
+    x = _x_kind(kind, 6201 + n_in, n_in)
+    out = host(qd.q4k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q4k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q4k one row {kind} {n_out}x{n_in}")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(8197, 2048), (8192, 3072), (3072, 8192), (1000, 6144), (20, 1024)])
+def test_q4k_one_row_matrix_core_grids(qd, n_out, n_in):
+    """Two row groups a workgroup from 512 groups on, with a spare last group
+    (8197 rows: 513 groups), and the single-group grids."""
+    raw = synth.q4k_weights(6220 + n_out, n_out, n_in)
+    x = synth.normal_f32(6221 + n_in, (1, n_in))
+    out = host(qd.q4k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q4k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q4k one row {n_out}x{n_in}")
+
+
+def test_q4k_one_row_nan_propagates(qd):
+    n_out, n_in = 40, 3072
+    raw = synth.q4k_weights(6210, n_out, n_in)
+    x = synth.normal_f32(6211, (1, n_in))
+    x[0, 700] = np.nan
+    out = host(qd.q4k_gemv(dev(raw), n_in, n_out, dev(x)))
+    assert np.all(np.isnan(out)), "a NaN in x must reach every output"
+
+
 # One batch row with x staged in LDS: every width case of the shape table
 # (whole rows per wave up to 4096 columns, K split over waves beyond; SwiGLU
 # and Q4_K take it up to 4096 columns, the register shapes beyond), ragged
