@@ -150,11 +150,14 @@ QDEC_API int q8_0_swiglu(const void* w_gate, const void* w_up, int64_t n_in, int
  * Order: larger logit first; equal logits by smaller index; -0 equals +0
  * (NaN logits, possible only from non-finite inputs, rank by bit pattern).
  * 1 <= k <= min(n_out, QDEC_TOPK_MAX); other conditions as q8_0_gemv.  The
- * candidate lists of n_out > 4096 live in the stream's workspace (see
- * Conventions): a capturing stream must already hold one of at least
- * 2 * batch * ceil(n_out/4096) * k * 8 bytes (make the same call on it once
- * before capturing), else QDEC_EINVAL.  logits, top_idx, top_val and x must
- * not overlap. */
+ * selection takes two launches: one workgroup per 2048 logits (4096 or 8192
+ * when n_out * k is large) keeps its chunk's k largest, then one workgroup per
+ * row merges the row's lists.  The lists live in the stream's workspace (see
+ * Conventions; batch * chunks * k * 8 bytes): a capturing stream must already
+ * hold one that large (make the same call on it once before capturing), else
+ * QDEC_EINVAL.  When ceil(n_out / 8192) * k exceeds 16384 a staged selection
+ * of more launches runs instead.  logits, top_idx, top_val and x must not
+ * overlap. */
 QDEC_API int q8_0_gemv_topk(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
                    const float* x, int64_t k, float* logits, int32_t* top_idx,
                    float* top_val, hipStream_t stream);

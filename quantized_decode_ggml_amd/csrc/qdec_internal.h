@@ -249,9 +249,10 @@ int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch);
 hipError_t launch_f32_gemm(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, void* workspace, hipStream_t s);
 
-// Top-k of batch rows of n_out logits (1 <= k <= 256): the workspace holds two
-// candidate buffers of batch * ceil(n_out / 4096) * k 64-bit keys (none for
-// n_out <= 4096).
+// Top-k of batch rows of n_out logits (1 <= k <= 256).  The workspace holds
+// the candidate lists: batch * chunks * k 64-bit keys for the two-launch
+// select, two buffers for the staged path it falls back to past its merge
+// capacity (none there for a single chunk).
 int64_t topk_workspace_bytes(int64_t n_out, int64_t batch, int k);
 hipError_t launch_topk(const float* logits, int64_t n_out, int64_t batch, int k, void* workspace,
                        int32_t* top_idx, float* top_val, hipStream_t s);

@@ -93,6 +93,27 @@ def test_ties_rank_by_smaller_index(qd):
         assert first < base                       # the first occurrence of the maximum
 
 
+@pytest.mark.parametrize("base,k", [(3, 256), (3, 1), (1, 40)])
+def test_massive_ties(qd, base, k):
+    """Every logit repeats n_out/base times (one value only for base 1): the
+    k-th largest key is found in the index bits, past the value's digits."""
+    n_out, n_in = 12000, 256
+    distinct = q8_weights(9925 + base, base, n_in).reshape(base, -1)
+    raw = np.ascontiguousarray(distinct[np.arange(n_out) % base].reshape(-1))
+    x = synth.normal_f32(9926, (1, n_in))
+    idx = check_topk(qd, raw, n_in, n_out, x, k, f"ties base {base} k={k}")
+    if base == 1:
+        assert np.array_equal(idx[0], np.arange(k))
+
+
+def test_staged_selection_past_the_merge_limit(qd):
+    """ceil(n_out / 8192) * k above 16384: the staged multi-launch selection."""
+    n_out, n_in, k = 530000, 32, 256
+    raw = q8_weights(9927, n_out, n_in)
+    x = synth.normal_f32(9928, (1, n_in))
+    check_topk(qd, raw, n_in, n_out, x, k, "staged")
+
+
 def test_graph_capture_replays(qd):
     n_out, n_in, k = 20000, 1024, 16
     raw = q8_weights(9930, n_out, n_in)
