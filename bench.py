@@ -241,6 +241,18 @@ def ceiling(args):
             del g
 
 
+def calibration_copy(qd, torch, dev):
+    """64 MiB read + 64 MiB written by qdec_copy_kernel, three times: the
+    known-size reference that scales the profiler's HBM byte counters."""
+    nbytes = 64 << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        qd.copy(dst, src, nbytes)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def suite(args):
     """Every workload configuration through the library, one line of JSON each
     (to stdout): mean launch duration of graph-replayed launches on rotated
@@ -254,6 +266,8 @@ def suite(args):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.calibrate:
+        calibration_copy(qd, torch, dev)
 
     def copies_for(nbytes):
         return max(2, -(-(512 << 20) // max(nbytes, 1)))
@@ -507,7 +521,7 @@ def main():
                     help="time the plain streaming-read kernel at the decode products' byte counts")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 64 MiB device copy (untimed), the known-size reference that "
-                         "scales the profiler's HBM byte counters")
+                         "scales the profiler's HBM byte counters (with the step or with --suite)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is a "
@@ -557,14 +571,7 @@ def main():
     sh = [torch.cuda.current_stream()]
     torch.cuda.synchronize()
     if args.calibrate:
-        # 64 MiB read + 64 MiB written by qdec_copy_kernel, three times
-        nbytes = 64 << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            qd.copy(dst, src, nbytes)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(qd, torch, dev)
 
     names = ("qkv", "up", "down_residual")
 
