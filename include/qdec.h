@@ -105,11 +105,9 @@ typedef enum { QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12, QDEC_TYPE_Q6_K = 14 } qd
 /* Q8_0 dequant-GEMV ([cuda_lane] try_q8_0_cuda_gemv, q8_0_gemv_oracle_into):
  * out[b][i] = sum_j deq(W)[i][j] * x[b][j] for 1 <= batch <= 8.
  * n_in % 32 == 0, n_in, n_out >= 1.  f32 accumulation.  Reproducibility: the
- * same inputs give the same bits on every call, except for 3..8 batch rows on
- * the matrix-core path with fewer than 8192 output rows (this call and
- * q8_0_gemv_residual), where K is split over workgroups whose partial sums
- * are added atomically in arbitrary order: the last bits may then change
- * from call to call, always within the f32 bound. */
+ * same inputs give the same bits on every call on a given path (with 3..8
+ * batch rows and fewer than 8192 output rows K is split over workgroups,
+ * whose sums a further small launch adds in a fixed order). */
 QDEC_API int q8_0_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
               const float* x, float* out, hipStream_t stream);
 
@@ -142,8 +140,7 @@ QDEC_API int q8_0_swiglu(const void* w_gate, const void* w_up, int64_t n_in, int
 
 /* Vocabulary projection with on-device top-k ([QTensorEngine]
  * dispatch_output_topk_chunked, and dispatch_output_top1_chunked for k = 1):
- * logits = W x exactly as q8_0_gemv computes them (same kernels; same bits
- * where q8_0_gemv is reproducible),
+ * logits = W x exactly as q8_0_gemv computes them (same kernels, same bits),
  * written to `logits` (device f32, batch x n_out, kept for a sampler), then,
  * per batch row, the k largest logits: top_idx[b*k + r] (int32 vocabulary row)
  * and top_val[b*k + r] = logits[b*n_out + top_idx[b*k + r]], r = 0 first.

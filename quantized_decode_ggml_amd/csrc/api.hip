@@ -310,7 +310,8 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
             else have = false;
         }
         void* wsp = fixed_ws;
-        if (have && !wsp && !noalloc) QDEC_TRY(stream_workspace(s, q8_mfma_workspace_bytes(n_in), &wsp));
+        if (have && !wsp && !noalloc)
+            QDEC_TRY(stream_workspace(s, q8_mfma_workspace_bytes(mode, n_in, rows[0], batch), &wsp));
         if (have && wsp) return finish(launch_q8_0_gemv_mfma(p, tiles, wsp, s), fn);
     }
     return finish(launch_q8_0_gemv(p, s), fn);
@@ -489,8 +490,9 @@ int q8_0_gemv_topk_noalloc(const void* w, int64_t n_in, int64_t n_out, int64_t b
     if (k < 1 || k > QDEC_TOPK_MAX || k > n_out)
         return fail(QDEC_EINVAL, "%s: k=%lld outside [1, min(n_out, %d)]", fn, (long long)k, QDEC_TOPK_MAX);
     // scratch layout: the split activations of the matrix-core projection
-    // (3..8 batch rows), then the top-k candidate lists
-    const int64_t proj = batch >= 3 ? align_up(q8_mfma_workspace_bytes(n_in), kAlign) : 0;
+    // (3..8 batch rows, with its K slices' sums), then the top-k candidate
+    // lists
+    const int64_t proj = batch >= 3 ? align_up(q8_mfma_workspace_bytes(kPlain, n_in, n_out, batch), kAlign) : 0;
     const int64_t need = proj + topk_workspace_bytes(n_out, batch, (int)k);
     if (need > kNoAllocScratchBytes)
         return fail(QDEC_EINVAL, "%s: needs %lld bytes of scratch, above the %lld-byte static array (fewer batch "

@@ -44,11 +44,15 @@
 // its KS waves, NBW blocks each; a wave streams its blocks in straight-line
 // code with loads D blocks ahead, then the waves add their partial sums
 // through LDS.  Where that grid would not fill the chip (fewer than 512 row
-// groups, plain and residual forms), K is also split over workgroups: the
-// x-split launch first sets out = residual (or 0), and each workgroup adds
-// its partial sums with f32 atomics (up to n_in/256 more roundings, in an
-// order that can change between calls: such results are not bitwise
-// reproducible, and stay inside the bound below).
+// groups, plain and residual forms), K is also split over workgroups: each
+// writes its slice's sums to the workspace, and a third small launch adds
+// the slices in slice order and the residual: n_in/1024 - 1 more roundings,
+// in a fixed order, so every result is bitwise reproducible.  (Adding the
+// slices with f32 atomics into an output that the split launch had set to
+// the residual was 1.5-3.5 us faster at batch 4-8 but not reproducible; so
+// were merges by the last slice of each row set, found with a device-scope
+// counter: after a release fence per workgroup, which writes back the whole
+// L2, 3x slower; with write-through stores of the sums, 20-40% slower.)
 #include "gemv_common.h"
 
 namespace qdec {
@@ -66,16 +70,11 @@ constexpr int kParts = 3;
 // holds part p of x[b] (3*batch rows, zero beyond), in NV = ceil(3*batch/16)
 // fragments of 16 rows.  One thread per (block, fragment, lane): 8 bf16 of
 // virtual row 16f + lane % 16 at k = 32*block + 8*(lane/16) .. +7.
-// With the K split over workgroups (partial sums added atomically) the same
-// launch first sets out = residual (or 0) for the ninit = batch * n_out
-// outputs.
 __global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ x, int batch,
                                                       int64_t n_in, int nv, int64_t nslots,
-                                                      u32x4* __restrict__ xs, float* out,
-                                                      const float* residual, int64_t ninit)
+                                                      u32x4* __restrict__ xs)
 {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < ninit) out[t] = residual ? residual[t] : 0.0f;
     if (t >= nslots) return;
     const int l = (int)(t & 63);
     const int64_t bf = t >> 6;
@@ -106,6 +105,25 @@ __global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ 
     xs[t] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
+// The K slices' sums of the split over workgroups, added in slice order (plus
+// the residual): one thread per output; part holds, per (row-group set,
+// slice), RG x batch x 16 sums.
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, int ksplit, int rg_per_set,
+                                                         int batch, int64_t rows, const float* residual,
+                                                         float* out)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)batch * rows) return;
+    const int64_t b = t / rows, row = t % rows;
+    const int64_t g = row / 16, set = g / rg_per_set;
+    const int rg = (int)(g % rg_per_set), r = (int)(row % 16);
+    const int64_t per = (int64_t)rg_per_set * batch * 16;
+    const float* p = part + set * ksplit * per + (rg * batch + b) * 16 + r;
+    float v = p[0];
+    for (int k = 1; k < ksplit; ++k) v += p[k * per];
+    out[t] = residual ? residual[t] + v : v;
+}
+
 // 8 int8 weights -> 8 bf16 (exact).
 __device__ inline bf16x8 q8_to_bf16(u32x2 w)
 {
@@ -126,11 +144,17 @@ struct TileArgs {
     int64_t gend0, gend1, groups;
     int64_t nb;
     int ksplit;   // workgroups per row-group set along K (AT kernels)
+    float* part;  // AT: per (set, slice) the slice's sums, RG x batch x 16 floats
 };
 
+// K split over workgroups (plain and residual): kAtKs waves of kAtNbw blocks
+// per workgroup, kAtRg row groups sharing every x fragment; at most
+// kMaxSlices slices (n_in <= 8192).
+constexpr int kAtKs = 4, kAtNbw = 8, kAtRg = 2, kMaxSlices = 8;
+
 // AT: the workgroup covers KS * NBW blocks of K (slice blockIdx.x % ksplit)
-// and adds its partial sums to the output atomically (plain and residual
-// forms; the output was initialised by the split kernel).
+// and writes its partial sums to the workspace; sum_slices_kernel then adds
+// the slices in slice order and stores the rows (plain and residual forms).
 template <int MODE, int KS, int NBW, int DP, int RG, int NV, bool AT>
 __global__ __launch_bounds__(KS * 64) void q8_0_gemv_mfma(Q8GemvArgs a, TileArgs t, const u32x4* __restrict__ xs)
 {
@@ -271,16 +295,25 @@ __global__ __launch_bounds__(KS * 64) void q8_0_gemv_mfma(Q8GemvArgs a, TileArgs
     __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes done (only wave 0 is left)
     __builtin_amdgcn_wave_barrier();
     const int r = lane & 15;
+    if constexpr (AT) {
+        // this slice's sums; sum_slices_kernel adds the slices in order afterwards
+        float* mine = t.part + (gb * t.ksplit + kp) * (int64_t)(RG * a.batch * 16);
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const int64_t row = (gb * RG + rg) * 16 + r;
-        if (row >= a.total_rows) continue;
-        for (int b = g4; b < a.batch; b += 4) {
-            const float v0 = (fin[rg][0][b][r] + fin[rg][0][a.batch + b][r]) + fin[rg][0][2 * a.batch + b][r];
-            const float v1 = (fin[rg][NM - 1][b][r] + fin[rg][NM - 1][a.batch + b][r]) +
-                             fin[rg][NM - 1][2 * a.batch + b][r];
-            if constexpr (AT) unsafeAtomicAdd(a.out0 + (int64_t)b * a.total_rows + row, v0);
-            else store_row<MODE>(a, row, b, v0, v1);
+        for (int rg = 0; rg < RG; ++rg)
+            for (int b = g4; b < a.batch; b += 4)
+                mine[(rg * a.batch + b) * 16 + r] =
+                    (fin[rg][0][b][r] + fin[rg][0][a.batch + b][r]) + fin[rg][0][2 * a.batch + b][r];
+    } else {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            const int64_t row = (gb * RG + rg) * 16 + r;
+            if (row >= a.total_rows) continue;
+            for (int b = g4; b < a.batch; b += 4) {
+                const float v0 = (fin[rg][0][b][r] + fin[rg][0][a.batch + b][r]) + fin[rg][0][2 * a.batch + b][r];
+                const float v1 = (fin[rg][NM - 1][b][r] + fin[rg][NM - 1][a.batch + b][r]) +
+                                 fin[rg][NM - 1][2 * a.batch + b][r];
+                store_row<MODE>(a, row, b, v0, v1);
+            }
         }
     }
 }
@@ -307,14 +340,13 @@ MfmaFn pick_nbw(int nbw)
     }
 }
 
-// K split over workgroups (plain and residual): kAtKs waves of kAtNbw blocks
-// per workgroup, kAtRg row groups sharing every x fragment.  Taken where the
+// The K split over workgroups (constants above) is taken where the
 // one-workgroup-per-row-group grid would leave compute units idle; measured
 // on 3072x8192 with residual (graph-replayed, both launches): batch 3 / 4 / 8
 // 12.9 / 13.0 / 16.7 -> 10.7 / 10.9 / 13.1 us (4 x 8 x 2 against 4 x 8 x 4,
 // 4 x 16 x 2 and 4 x 8 x 1: 11.7-14.7 us).  On 8192x3072, where two row
 // groups per workgroup already fill the chip, it gained nothing.
-constexpr int kAtKs = 4, kAtNbw = 8, kAtRg = 2;
+
 
 template <int MODE>
 MfmaFn pick_at(int nv)
@@ -357,8 +389,28 @@ bool mfma_shape(int64_t n_in, int* ks, int* nbw)
 
 }  // namespace
 
-// at most two fragments (3 * 8 stacked rows) of 64 lanes x 16 bytes per block
-int64_t q8_mfma_workspace_bytes(int64_t n_in) { return (n_in / 32) * 2 * 64 * 16; }
+// K split over workgroups: plain and residual products whose row groups
+// would leave compute units idle (fewer than 512) and whose K holds 2 to
+// kMaxSlices whole workgroup slices.
+static bool q8_mfma_ksplit(int mode, int64_t n_in, int64_t rows0)
+{
+    const int64_t at_blocks = (int64_t)kAtKs * kAtNbw;
+    const int64_t slices = (n_in / 32) / at_blocks;
+    return (mode == kPlain || mode == kResidual) && (n_in / 32) % at_blocks == 0 && slices >= 2 &&
+           slices <= kMaxSlices && q8t_groups(rows0) / 2 < 256;
+}
+
+// at most two fragments (3 * 8 stacked rows) of 64 lanes x 16 bytes per block,
+// then, with the K split, the slices' sums (batch x padded rows per slice)
+int64_t q8_mfma_workspace_bytes(int mode, int64_t n_in, int64_t rows0, int64_t batch)
+{
+    const int64_t xs = align_up((n_in / 32) * 2 * 64 * 16, kAlign);
+    if (!q8_mfma_ksplit(mode, n_in, rows0)) return xs;
+    const int64_t ksplit = (n_in / 32) / ((int64_t)kAtKs * kAtNbw);
+    const int64_t sets = (q8t_groups(rows0) + kAtRg - 1) / kAtRg;
+    return xs + sets * ksplit * kAtRg * 16 * batch * 4;
+}
+
 
 bool q8_mfma_supported(const Q8GemvProblem& p)
 {
@@ -399,15 +451,15 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
     const int nv = frags_for(p.batch);
     MfmaFn fn = nullptr;
     int64_t blocks = 0;
-    int64_t ninit = 0;
     const int64_t at_blocks = (int64_t)kAtKs * kAtNbw;
-    if ((p.mode == kPlain || p.mode == kResidual) && t.nb % at_blocks == 0 && t.groups / 2 < 256) {
+    if (q8_mfma_ksplit(p.mode, p.n_in, p.rows[0])) {
         // K split over workgroups: x fragments are read by kAtRg row groups
-        // per workgroup and only for its K slice
+        // per workgroup and only for its K slice; the slices' sums go to the
+        // workspace after the x fragments
         t.ksplit = (int)(t.nb / at_blocks);
+        t.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(t.nb * 2 * 64 * 16, kAlign));
         fn = p.mode == kPlain ? pick_at<kPlain>(nv) : pick_at<kResidual>(nv);
         blocks = (t.groups + kAtRg - 1) / kAtRg * t.ksplit;
-        ninit = p.batch * p.rows[0];
         ks = kAtKs;
     } else {
         // two row groups per workgroup while that still gives one workgroup per CU
@@ -424,13 +476,18 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
     if (!fn) return hipErrorNotSupported;
     u32x4* xs = static_cast<u32x4*>(workspace);
     const int64_t nslots = (p.n_in / 32) * nv * 64;
-    const int64_t nthreads = nslots > ninit ? nslots : ninit;
-    hipLaunchKernelGGL(split_x_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, p.x,
-                       (int)p.batch, p.n_in, nv, nslots, xs, a.out0, ninit ? p.residual : nullptr, ninit);
+    hipLaunchKernelGGL(split_x_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, p.x,
+                       (int)p.batch, p.n_in, nv, nslots, xs);
     count_launch();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(ks * 64), 0, s, a, t, xs);
+    count_launch();
+    e = hipGetLastError();
+    if (e != hipSuccess || !t.ksplit) return e;
+    const int64_t nout = p.batch * p.rows[0];
+    hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, s, t.part, t.ksplit,
+                       kAtRg, (int)p.batch, p.rows[0], p.mode == kResidual ? p.residual : nullptr, a.out0);
     count_launch();
     return hipGetLastError();
 }

@@ -1,7 +1,8 @@
 """GPU parity of the matrix-core Q8_0 GEMV path (3..8 batch rows): which path
 runs, every supported width, ragged rows and segments, activations over a wide
-dynamic range (the exact three-part bf16 split of x), graph capture with and
-without a prepared workspace, and a refused workspace allocation.
+dynamic range (the exact three-part bf16 split of x), bitwise reproducibility
+of the K split over workgroups, graph capture with and without a prepared
+workspace, and a refused workspace allocation.
 
 Bar: the f32 bound, |gpu - oracle| <= 1e-5 * S + 1e-6 with S = sum_j |w x|
 from the oracle (SwiGLU: the propagated bound of helpers.swiglu_tol).
@@ -52,10 +53,13 @@ def launches(qd, fn):
     return r, qd.launch_count() - before
 
 
-@pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 2), (3072, 4, 2),
-                                               (3072, 8, 2), (8192, 5, 2), (512, 4, 1), (2560, 8, 1)])
+@pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 3), (3072, 4, 3),
+                                               (3072, 8, 3), (8192, 5, 3), (2048, 8, 3), (1024, 8, 2),
+                                               (512, 4, 1), (2560, 8, 1)])
 def test_path_selection(qd, n_in, batch, expect):
-    """3..8 rows at a supported width: x split + matrix-core kernel (2 launches);
+    """3..8 rows at a supported width: x split + matrix-core kernel, and, where K
+    is split over workgroups (48 rows, n_in a multiple of 1024 from 2048),
+    the ordered sum of the slices (3 launches; 2 at 1024, a single slice);
     otherwise the VALU kernel (1 launch)."""
     n_out = 48
     raw = q8_weights(9000 + n_in, n_out, n_in)
@@ -132,14 +136,14 @@ def test_residual_in_place(qd, batch):
     check_f32(host(buf), ref, S, f"residual in place b{batch}")
 
 
-@pytest.mark.parametrize("n_out,bitwise", [(8192, True), (1024, False)])
-def test_graph_capture_with_workspace(qd, n_out, bitwise):
-    """Warm-up on the capture stream makes its workspace; the captured graph then
-    uses the matrix-core path (2 launches recorded) and every replay, with eager
-    work in between, stays within the bound and, where the result is
-    reproducible (8192 rows: one workgroup per row pair), matches the eager
-    result bit for bit.  Below 8192 rows K is split over workgroups with
-    atomic partial sums, whose order (and so the last bits) may change."""
+@pytest.mark.parametrize("n_out", [8192, 1024])
+def test_graph_capture_with_workspace(qd, n_out):
+    """Warm-up on the capture stream makes its workspace; the captured graph
+    then uses the matrix-core path (2 launches recorded, 3 with the K split
+    over workgroups below 8192 rows) and every replay, with eager work in
+    between, matches the eager result bit for bit (the K slices
+    are added in a fixed order by a third launch)."""
+    bitwise = True
     n_in, batch = 3072, 4
     raw = q8_weights(9600, n_out, n_in)
     x = synth.normal_f32(9601, (batch, n_in))
@@ -156,7 +160,7 @@ def test_graph_capture_with_workspace(qd, n_out, bitwise):
     before = qd.launch_count()
     with torch.cuda.graph(g, stream=s):
         qd.q8_0_gemv(w, n_in, n_out, xd, out=out)
-    assert qd.launch_count() - before == 2
+    assert qd.launch_count() - before == (2 if n_out >= 8192 else 3)
     ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
     for k in range(3):
         out.fill_(float("nan"))
@@ -167,6 +171,34 @@ def test_graph_capture_with_workspace(qd, n_out, bitwise):
         check_f32(got, ref, S, f"replay {k}")
         qd.q8_0_gemv(w, n_in, n_out, xd)          # eager work between replays
     del g
+
+
+@pytest.mark.parametrize("n_out,n_in,mode", [(3072, 8192, "residual"), (1024, 2048, "plain"), (77, 3072, "plain")])
+@pytest.mark.parametrize("batch", [3, 5, 8])
+def test_k_split_bitwise_reproducible(qd, n_out, n_in, mode, batch):
+    """Fewer than 8192 rows: K split over workgroups, the slices added in slice
+    order by a third launch.  Five calls give the same bits, and they match
+    the oracle to the f32 bound."""
+    raw = q8_weights(9650 + n_out, n_out, n_in)
+    x = synth.normal_f32(9651 + batch, (batch, n_in))
+    r = synth.normal_f32(9652 + batch, (batch, n_out))
+    w, xd, rd = dev(raw), dev(x), dev(r)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    runs = []
+    for _ in range(5):
+        if mode == "residual":
+            out, n = launches(qd, lambda: qd.q8_0_gemv_residual(w, n_in, n_out, xd, rd))
+        else:
+            out, n = launches(qd, lambda: qd.q8_0_gemv(w, n_in, n_out, xd))
+        assert n == 3
+        runs.append(host(out))
+    for k in range(1, 5):
+        assert np.array_equal(runs[k].view(np.uint32), runs[0].view(np.uint32)), f"call {k} differs"
+    if mode == "residual":
+        ref, S = oracle.q8_0_gemv_residual(raw, n_in, n_out, x, r)
+    else:
+        ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(runs[0], ref, S, f"k split {mode} {n_out}x{n_in} b{batch}")
 
 
 def test_graph_capture_without_workspace_falls_back(qd):
