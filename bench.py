@@ -434,6 +434,16 @@ def suite(args):
             timed(f"c3 f32_gemm_batched {nm} B{B}",
                   [lambda w=w: qd.f32_gemm_batched(w, n_in, n_out, x3, out=o3) for w in wfs],
                   n_out * n_in * 4 + B * n_in * 4 + B * n_out * 4, flops=2.0 * B * n_out * n_in)
+        # the same weights with their bf16 copies (qdec_prepare): 2 bytes a weight read
+        for w in wfs:
+            qd.prepare(w, qd.TYPE_F32, n_in, n_out)
+        for B in (128, 512):
+            x3, o3 = xdev(synth.seed(3, 12) + B, (B, n_in)), torch.empty((B, n_out), device=dev)
+            timed(f"c3 f32_gemm_batched bf16 copy {nm} B{B}",
+                  [lambda w=w: qd.f32_gemm_batched(w, n_in, n_out, x3, out=o3) for w in wfs],
+                  n_out * n_in * 2 + B * n_in * 4 + B * n_out * 4, flops=2.0 * B * n_out * n_in)
+        for w in wfs:
+            qd.release(w)
         del wfs, wf
     # config 4
     for n_out, n_in in ((8192, 3072), (3072, 8192)):

@@ -93,8 +93,8 @@ typedef enum {
     QDEC_EUNSUPPORTED = -4   /* no kernel for this device or shape */
 } qdec_status;
 
-/* GGML type ids. */
-typedef enum { QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12, QDEC_TYPE_Q6_K = 14 } qdec_type;
+/* GGML type ids (F32: dense f32 weights, for qdec_prepare only). */
+typedef enum { QDEC_TYPE_F32 = 0, QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12, QDEC_TYPE_Q6_K = 14 } qdec_type;
 
 /* Largest batch accepted by the GEMV-shaped calls (decode).  The batched GEMM
  * calls take any batch >= 1. */
@@ -281,8 +281,14 @@ QDEC_API int q8_0_gemm_batched(const void* w, int64_t n_in, int64_t n_out, int64
                       const float* x, float* out, hipStream_t stream);
 
 /* The same contraction over dense f32 row-major weights (n_out x n_in, device
- * memory, used in place -- no repacked copy), bf16 MFMA with f32
- * accumulation.  Any batch >= 1, n_in % 32 == 0. */
+ * memory), bf16 MFMA with f32 accumulation: both operands rounded to bf16
+ * (round to nearest even), as in q8_0_gemm_batched.  Any batch >= 1,
+ * n_in % 32 == 0.  By default W is read in place and rounded as it is loaded.
+ * After qdec_prepare(w, QDEC_TYPE_F32, ...) the call reads the library's bf16
+ * copy of W instead (n_in * n_out * 2 bytes, same rounding, so the same
+ * products; with n_in % 64 == 0 the DMA-fed kernel of q8_0_gemm_batched runs
+ * on it); the copy is never made implicitly, and once it exists W must not
+ * change until qdec_release. */
 QDEC_API int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
                      const float* x, float* out, hipStream_t stream);
 
@@ -290,7 +296,8 @@ QDEC_API int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64
 
 /* Repack w now (load time, not timed), type QDEC_TYPE_Q8_0, QDEC_TYPE_Q4_K or QDEC_TYPE_Q6_K
  * ([cuda_lane] preload_q4k_soa_weights), and wait on the host until the copy
- * is complete.  Idempotent. */
+ * is complete.  Idempotent.  QDEC_TYPE_F32 (w: dense f32, n_in % 32 == 0,
+ * 16-byte aligned) makes the bf16 copy f32_gemm_batched then reads. */
 QDEC_API int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream);
 
 /* Free every repacked copy made from w (all types and shapes) on the current

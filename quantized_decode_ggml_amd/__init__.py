@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libqdec.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qdec.h")
 
 QDEC_OK, QDEC_EINVAL, QDEC_ENOMEM, QDEC_EHIP, QDEC_EUNSUPPORTED = 0, -1, -2, -3, -4
-TYPE_Q8_0, TYPE_Q4_K, TYPE_Q6_K = 8, 12, 14
+TYPE_F32, TYPE_Q8_0, TYPE_Q4_K, TYPE_Q6_K = 0, 8, 12, 14
 GEMV_MAX_BATCH = 8
 TOPK_MAX = 256
 

@@ -82,7 +82,8 @@ void destroy(Entry& e)
 
 int64_t copy_bytes(int type, int64_t n_in, int64_t n_out)
 {
-    return type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out)
+    return type == QDEC_TYPE_F32 ? n_in * n_out * 2
+         : type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out)
          : type == kTypeQ8_0Tiled ? q8t_plane_bytes(n_in, n_out)
          : type == kTypeQ4KTiled ? q4kt_plane_bytes(n_in, n_out)
          : type == QDEC_TYPE_Q6_K ? q6k_plane_bytes(n_in, n_out)
@@ -92,7 +93,8 @@ int64_t copy_bytes(int type, int64_t n_in, int64_t n_out)
 hipError_t launch_copy_of(int type, const void* w, int64_t n_in, int64_t n_out, void* dst, hipStream_t s)
 {
     const uint8_t* raw = static_cast<const uint8_t*>(w);
-    return type == QDEC_TYPE_Q8_0 ? launch_repack_q8_0(raw, n_in, n_out, dst, s)
+    return type == QDEC_TYPE_F32 ? launch_to_bf16(static_cast<const float*>(w), n_in * n_out, dst, s)
+         : type == QDEC_TYPE_Q8_0 ? launch_repack_q8_0(raw, n_in, n_out, dst, s)
          : type == kTypeQ8_0Tiled ? launch_repack_q8_0_tiled(raw, n_in, n_out, dst, s)
          : type == kTypeQ4KTiled ? launch_repack_q4k_tiled(raw, n_in, n_out, dst, s)
          : type == QDEC_TYPE_Q6_K ? launch_repack_q6k(raw, n_in, n_out, dst, s)
@@ -714,21 +716,27 @@ int f32_gemm_batched(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
     if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4) ||
         overlaps(out, batch * n_out * 4, w, n_out * n_in * 4))
         return fail(QDEC_EINVAL, "%s: out overlaps an input", fn);
-    // K-split partial products go to the stream's workspace; a capture on a
-    // stream without one adds them with atomics instead
+    // the bf16 copy is used when qdec_prepare made it (it is never made here:
+    // it doubles the weight's footprint and binds the caller not to change W)
+    const void* wb = nullptr;
+    QDEC_TRY(repacked(w, QDEC_TYPE_F32, n_in, n_out, stream, &wb, false, /*optional*/ true, /*noalloc*/ true));
+    // x in bf16 and K-split partial products go to the stream's workspace; a
+    // capture on a stream without one large enough takes the register-staged
+    // kernel, which adds its K slices with atomics
     void* wsp = nullptr;
-    const int64_t need = f32_gemm_workspace_bytes(n_in, n_out, batch);
+    const int64_t need = f32_gemm_workspace_bytes(n_in, n_out, batch, wb != nullptr);
     if (need > 0) QDEC_TRY(stream_workspace(stream, need, &wsp));
-    return finish(launch_f32_gemm(w, n_in, n_out, batch, x, out, wsp, stream), fn);
+    return finish(launch_f32_gemm(w, wb, n_in, n_out, batch, x, out, wsp, stream), fn);
 }
 
 int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t stream)
 {
     const char* fn = "qdec_prepare";
-    if (type != QDEC_TYPE_Q8_0 && type != QDEC_TYPE_Q4_K && type != QDEC_TYPE_Q6_K)
+    if (type != QDEC_TYPE_F32 && type != QDEC_TYPE_Q8_0 && type != QDEC_TYPE_Q4_K && type != QDEC_TYPE_Q6_K)
         return fail(QDEC_EINVAL, "%s: unknown type %d", fn, type);
-    QDEC_TRY(check_dims(fn, n_in, n_out, 1, type == QDEC_TYPE_Q8_0 ? 32 : 256, 0));
-    QDEC_TRY(check_ptr(fn, "weight", w, 2));
+    const bool blk32 = type == QDEC_TYPE_Q8_0 || type == QDEC_TYPE_F32;
+    QDEC_TRY(check_dims(fn, n_in, n_out, 1, blk32 ? 32 : 256, 0));
+    QDEC_TRY(check_ptr(fn, "weight", w, type == QDEC_TYPE_F32 ? 16 : 2));
     const void* buf = nullptr;
     QDEC_TRY(repacked(w, type, n_in, n_out, stream, &buf, true));
     // Q8_0 weights also get the fragment-tiled copy of the batched matrix-core

@@ -21,8 +21,10 @@
 //    dequantised in registers (described at the kernel).  With few output
 //    tiles K is split into slices whose partial products a small kernel sums
 //    in slice order.
-//  - gemm_bf16_kernel (dense f32 weights, and Q8_0 shapes off the DMA path or
-//    without a workspace): a 256-thread workgroup computes a 128 x 128 tile of
+//    The same kernel also reads the bf16 copy of a dense f32 weight (made by
+//    qdec_prepare) the way it reads x: nothing to dequantise, K % 64 == 0.
+//  - gemm_bf16_kernel (dense f32 weights without that copy, and Q8_0 shapes
+//    off the DMA path or without a workspace): a 256-thread workgroup computes a 128 x 128 tile of
 //    C over a slice of K, four waves of 64 x 64 with 4 x 4 MFMA 16x16x32 tiles;
 //    both operands register-staged into LDS as bf16 rows (K contiguous, padded
 //    by 8 elements against bank conflicts), double-buffered.  Its K slices
@@ -268,8 +270,9 @@ __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 struct DmaArgs {
     const __bf16* xb;      // M x K bf16 (workspace)
-    const int8_t* q;       // N x K int8 q plane
-    const uint16_t* dT;    // (K/32) x N scales, block-major
+    const int8_t* q;       // N x K int8 q plane (Q8_0 weights)
+    const uint16_t* dT;    // (K/32) x N scales, block-major (Q8_0 weights)
+    const __bf16* wb;      // N x K bf16 (the bf16 copy of dense f32 weights)
     float* out;            // M x N, or the slice partials part[slice][M][N]
     int64_t M, N, K, ntiles;
     int64_t kslice;        // K per slice (multiple of 64)
@@ -283,12 +286,19 @@ __global__ __launch_bounds__(256) void x_to_bf16(const float4* __restrict__ x, b
 }
 
 constexpr int kDmaStages = 4;
-constexpr int kDmaSlot = 16384 + 8192 + 768;   // X | W | D (512 B of scales + 256 B overflow)
+// X | W | D: Q8_0 int8 rows and 512 B of scales (+ 256 B overflow); bf16 rows
+template <bool BF16W>
+constexpr int dma_slot() { return BF16W ? 16384 + 16384 : 16384 + 8192 + 768; }
 
-__global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
+// BF16W: the weights are bf16 rows laid out like x (no scales, nothing to
+// dequantise: the B fragments are read as they stand), two DMAs a stage for
+// them in place of the int8 rows and the scales, so every stage still has four.
+template <bool BF16W>
+__global__ __launch_bounds__(512) void gemm_dma(DmaArgs a)
 {
     constexpr int P = kDmaStages, U = 2 * P, BM = 128, BN = 128;
-    __shared__ __attribute__((aligned(1024))) char S0[kDmaSlot], S1[kDmaSlot], S2[kDmaSlot], S3[kDmaSlot];
+    constexpr int SLOT = dma_slot<BF16W>();
+    __shared__ __attribute__((aligned(1024))) char S0[SLOT], S1[SLOT], S2[SLOT], S3[SLOT];
 #define QDEC_SLOT(u) ((u) == 0 ? S0 : (u) == 1 ? S1 : (u) == 2 ? S2 : S3)
     const int64_t id = blockIdx.x;
     const int64_t slice = id % a.splits, tile = id / a.splits;
@@ -310,8 +320,18 @@ __global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
         gr = gr < a.M ? gr : a.M - 1;                          // rows past M repeat the last (never stored)
         xsrc[i] = a.xb + gr * a.K + kbeg + c * 8;
     }
-    const int8_t* wsrc;
-    {
+    const int8_t* wsrc = nullptr;
+    const __bf16* wbsrc[2] = {nullptr, nullptr};
+    if constexpr (BF16W) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (i * 8 + wave) * 8 + (lane >> 3);    // as x, over the weight rows
+            const int c = (lane & 7) ^ (r & 7);
+            int64_t gn = n0 + r;
+            gn = gn < a.N ? gn : a.N - 1;
+            wbsrc[i] = a.wb + gn * a.K + kbeg + c * 8;
+        }
+    } else {
         const int r = wave * 16 + (lane >> 2);                 // chunk slot wave*64 + lane
         const int c = (lane & 3) ^ ((r >> 1) & 3);
         int64_t gn = n0 + r;
@@ -321,8 +341,8 @@ __global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
     // scales: word w*16 + L holds block (L%16)/8, rows 16(w + L/16) + 2(L%8)
     // + {0,1}: lanes L >= 16 write the words of the next waves, with the same
     // values those waves write (words past 127 land in the overflow)
-    const uint16_t* dsrc;
-    {
+    const uint16_t* dsrc = nullptr;
+    if constexpr (!BF16W) {
         const int vw = wave + (lane >> 4), vl = lane & 15;
         int64_t gn = n0 + vw * 16 + 2 * (vl & 7);
         gn = gn < a.N - 1 ? gn : a.N - 2;                      // N even: pairs never straddle the edge
@@ -334,8 +354,15 @@ __global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_global_load_lds(xsrc[i] + (int64_t)sc * 64, (lds_void*)(sb + (i * 8 + wave) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(wsrc + (int64_t)sc * 64, (lds_void*)(sb + 16384 + wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(dsrc + (int64_t)sc * 2 * a.N, (lds_void*)(sb + 24576 + wave * 64), 4, 0, 0);
+        if constexpr (BF16W) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                __builtin_amdgcn_global_load_lds(wbsrc[i] + (int64_t)sc * 64,
+                                                 (lds_void*)(sb + 16384 + (i * 8 + wave) * 1024), 16, 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds(wsrc + (int64_t)sc * 64, (lds_void*)(sb + 16384 + wave * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dsrc + (int64_t)sc * 2 * a.N, (lds_void*)(sb + 24576 + wave * 64), 4, 0, 0);
+        }
     };
     // fragment offsets inside a stage array (bytes)
     uint32_t xoff[8], woff[2], doff[2];
@@ -347,9 +374,14 @@ __global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const uint32_t r = wn * 32 + j * 16 + (lane & 15);
-        const uint32_t kb = wk * 32 + (lane >> 4) * 8;         // byte of the 64-byte row
-        woff[j] = 16384 + r * 64 + ((kb >> 4) ^ ((r >> 1) & 3)) * 16 + (kb & 8);
-        doff[j] = 24576 + 2 * ((r >> 4) * 32 + wk * 16 + (r & 15));
+        if constexpr (BF16W) {
+            woff[j] = 16384 + r * 128 + (((uint32_t)wk * 4 + (lane >> 4)) ^ (r & 7)) * 16;
+            doff[j] = 0;
+        } else {
+            const uint32_t kb = wk * 32 + (lane >> 4) * 8;     // byte of the 64-byte row
+            woff[j] = 16384 + r * 64 + ((kb >> 4) ^ ((r >> 1) & 3)) * 16 + (kb & 8);
+            doff[j] = 24576 + 2 * ((r >> 4) * 32 + wk * 16 + (r & 15));
+        }
     }
     bf16x8 fa[2][8], fb[2][2];
     u32x2 fq[2][2];
@@ -358,8 +390,12 @@ __global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
         const char* sb = QDEC_SLOT(u);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            fq[f][j] = *reinterpret_cast<const u32x2*>(sb + woff[j]);
-            fd[f][j] = *reinterpret_cast<const uint16_t*>(sb + doff[j]);
+            if constexpr (BF16W) {
+                fb[f][j] = *reinterpret_cast<const bf16x8*>(sb + woff[j]);
+            } else {
+                fq[f][j] = *reinterpret_cast<const u32x2*>(sb + woff[j]);
+                fd[f][j] = *reinterpret_cast<const uint16_t*>(sb + doff[j]);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) fa[f][i] = *reinterpret_cast<const bf16x8*>(sb + xoff[i]);
@@ -387,8 +423,10 @@ __global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     frags(0, 0);
-    fb[0][0] = deq(0, 0);
-    fb[0][1] = deq(0, 1);
+    if constexpr (!BF16W) {
+        fb[0][0] = deq(0, 0);
+        fb[0][1] = deq(0, 1);
+    }
     auto body = [&](const int s, const int u) {
         issue(s + P - 1, (u + P - 1) % P);
         const int f = u & 1;
@@ -399,8 +437,10 @@ __global__ __launch_bounds__(512) void gemm_q8_dma(DmaArgs a)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
-        fb[f ^ 1][0] = deq(f ^ 1, 0);
-        fb[f ^ 1][1] = deq(f ^ 1, 1);
+        if constexpr (!BF16W) {
+            fb[f ^ 1][0] = deq(f ^ 1, 0);
+            fb[f ^ 1][1] = deq(f ^ 1, 1);
+        }
         // this wave's share of stage s+2 has landed; the barrier makes every
         // wave's share visible and frees stage s-1's array for reuse
         wait_vm<4 * (P - 3)>();
@@ -568,9 +608,23 @@ int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
     return dma_x_bytes(n_in, batch) + (s > 1 ? (int64_t)s * batch * n_out * 4 : 0);
 }
 
-int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch)
+hipError_t launch_to_bf16(const float* src, int64_t count, void* dst, hipStream_t s)
 {
-    return reg_part_bytes(batch, n_out, n_in);
+    const int64_t n4 = count / 4;   // count % 4 == 0 (n_in % 32 == 0)
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(x_to_bf16, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(src),
+                       static_cast<bf16x4*>(dst), n4);
+    count_launch();
+    return hipGetLastError();
+}
+
+int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch, bool bf16_copy)
+{
+    if (!bf16_copy || n_in % 64) return reg_part_bytes(batch, n_out, n_in);
+    const int s = dma_splits(batch, n_out, n_in);
+    return dma_x_bytes(n_in, batch) + (s > 1 ? (int64_t)s * batch * n_out * 4 : 0);
 }
 
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
@@ -597,7 +651,7 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
         float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + dma_x_bytes(n_in, batch));
         p.out = p.splits > 1 ? part : out;
         const int64_t grid = ((batch + 127) / 128) * p.ntiles * p.splits;
-        hipLaunchKernelGGL(gemm_q8_dma, dim3((unsigned)grid), dim3(512), 0, s, p);
+        hipLaunchKernelGGL(gemm_dma<false>, dim3((unsigned)grid), dim3(512), 0, s, p);
         count_launch();
         if (p.splits > 1) {
             const int64_t mn = batch * n_out;
@@ -620,9 +674,43 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
     return launch(a, true, s);
 }
 
-hipError_t launch_f32_gemm(const float* wf, int64_t n_in, int64_t n_out, int64_t batch,
+hipError_t launch_f32_gemm(const float* wf, const void* wbf16, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, void* workspace, hipStream_t s)
 {
+    if (wbf16 && workspace && n_in % 64 == 0) {
+        // the weight's bf16 copy (qdec_prepare): the DMA-fed kernel reads it
+        // as it reads x
+        const int64_t n4 = batch * n_in / 4;
+        int64_t blocks = (n4 + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        hipLaunchKernelGGL(x_to_bf16, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(x),
+                           static_cast<bf16x4*>(workspace), n4);
+        count_launch();
+        DmaArgs p{};
+        p.xb = static_cast<const __bf16*>(workspace);
+        p.wb = static_cast<const __bf16*>(wbf16);
+        p.M = batch;
+        p.N = n_out;
+        p.K = n_in;
+        p.ntiles = (n_out + 127) / 128;
+        const int splits = dma_splits(batch, n_out, n_in);
+        p.kslice = dma_kslice(n_in, splits);
+        p.splits = (int)((n_in + p.kslice - 1) / p.kslice);
+        float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + dma_x_bytes(n_in, batch));
+        p.out = p.splits > 1 ? part : out;
+        const int64_t grid = ((batch + 127) / 128) * p.ntiles * p.splits;
+        hipLaunchKernelGGL(gemm_dma<true>, dim3((unsigned)grid), dim3(512), 0, s, p);
+        count_launch();
+        if (p.splits > 1) {
+            const int64_t mn = batch * n_out;
+            int64_t sb = (mn / 4 + 255) / 256;
+            if (sb > 2048) sb = 2048;
+            if (sb < 1) sb = 1;
+            hipLaunchKernelGGL(sum_slices, dim3((unsigned)sb), dim3(256), 0, s, part, p.splits, mn, out);
+            count_launch();
+        }
+        return hipGetLastError();
+    }
     GemmArgs a = plan(batch, n_out, n_in);
     a.x = x;
     a.wf = wf;

@@ -244,11 +244,19 @@ hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, const f
 int64_t q8_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch);
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                             float* out, void* workspace, hipStream_t s);
-// Dense f32 weights: the register-staged kernel, with the K-slice partials in
-// a workspace of f32_gemm_workspace_bytes when there is one, as above.
-int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch);
-hipError_t launch_f32_gemm(const float* w, int64_t n_in, int64_t n_out, int64_t batch,
+// Dense f32 weights.  With the weight's bf16 copy (wbf16, made by
+// qdec_prepare), n_in % 64 == 0 and a workspace of f32_gemm_workspace_bytes(...,
+// true), the DMA-fed kernel reads that copy (x rounded to bf16 and the K-slice
+// partials in the workspace); else the register-staged kernel rounds W as it
+// loads it, with the K-slice partials in a workspace of
+// f32_gemm_workspace_bytes(..., false) when there is one, as above.  Both
+// contract bf16(W) with bf16(x) in f32.
+int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch, bool bf16_copy);
+hipError_t launch_f32_gemm(const float* w, const void* wbf16, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, void* workspace, hipStream_t s);
+// dst[i] = bf16(src[i]) (round to nearest even), count % 4 == 0: the bf16 copy
+// of a dense f32 weight.
+hipError_t launch_to_bf16(const float* src, int64_t count, void* dst, hipStream_t s);
 
 // Top-k of batch rows of n_out logits (1 <= k <= 256).  The workspace holds
 // the candidate lists: batch * chunks * k 64-bit keys for the two-launch

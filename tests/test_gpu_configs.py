@@ -125,15 +125,24 @@ def test_config3_batched_gemm_q8_0(qd, batch, which):
     check_every_output(out, ref, S, f"q8_0 gemm {which} B{batch}")
 
 
+@pytest.mark.parametrize("bf16_copy", [False, True])
 @pytest.mark.parametrize("batch", [128, 512])
 @pytest.mark.parametrize("which", ["up", "down"])
-def test_config3_batched_gemm_dense_f32(qd, batch, which):
+def test_config3_batched_gemm_dense_f32(qd, batch, which, bf16_copy):
+    """W read in place, and W's bf16 copy (qdec_prepare) on the DMA-fed kernel."""
     n_out, n_in = (8192, 3072) if which == "up" else (3072, 8192)
     w = synth.normal_f32(synth.seed(3, 10 + (which == "down")), (n_out, n_in), 0.02)
     x = synth.normal_f32(synth.seed(3, 12) + batch, (batch, n_in))
-    out = host(qd.f32_gemm_batched(dev(w), n_in, n_out, dev(x)))
+    wd = dev(w)
+    if bf16_copy:
+        qd.prepare(wd, qd.TYPE_F32, n_in, n_out)
+    try:
+        out = host(qd.f32_gemm_batched(wd, n_in, n_out, dev(x)))
+    finally:
+        if bf16_copy:
+            qd.release(wd)
     ref, S = oracle.f32_gemm_f64(w, n_in, n_out, x)
-    check_every_output(out, ref, S, f"f32 gemm {which} B{batch}")
+    check_every_output(out, ref, S, f"f32 gemm {which} B{batch}{' bf16 copy' if bf16_copy else ''}")
 
 
 @pytest.mark.parametrize("shape", [(8192, 3072), (3072, 8192)])

@@ -317,6 +317,28 @@ def test_f32_gemm_batched(qd, n_out, n_in, batch):
     check_f32(out, ref, S, "gemm f32", rel=BF16_REL, abs_=0.0)
 
 
+@pytest.mark.parametrize("n_out,n_in,batch", [(16, 64, 1), (130, 96, 3), (256, 512, 128), (200, 576, 130),
+                                              (128, 3072, 129), (301, 64, 512), (1, 128, 2)])
+def test_f32_gemm_batched_bf16_copy(qd, n_out, n_in, batch):
+    """After qdec_prepare(F32) the call reads the library's bf16 copy (the
+    DMA-fed kernel when n_in % 64 == 0; 96 stays on the register-staged one):
+    the same bf16 products, so the same bound; after release W is read again."""
+    w = synth.normal_f32(7110 + n_in, (n_out, n_in), 0.02)
+    x = synth.normal_f32(7111 + batch, (batch, n_in))
+    wd, xd = dev(w), dev(x)
+    ref, S = oracle.f32_gemm(w, n_in, n_out, x)
+    qd.prepare(wd, qd.TYPE_F32, n_in, n_out)
+    try:
+        out = host(qd.f32_gemm_batched(wd, n_in, n_out, xd))
+        check_f32(out, ref, S, "gemm f32 bf16 copy", rel=BF16_REL, abs_=0.0)
+        again = host(qd.f32_gemm_batched(wd, n_in, n_out, xd))
+        assert np.array_equal(out, again), "the bf16-copy path is not reproducible"
+    finally:
+        qd.release(wd)
+    out = host(qd.f32_gemm_batched(wd, n_in, n_out, xd))
+    check_f32(out, ref, S, "gemm f32 after release", rel=BF16_REL, abs_=0.0)
+
+
 # --------------------------------------------------- library behaviour --
 
 def test_non_default_stream(qd):
