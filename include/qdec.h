@@ -165,17 +165,18 @@ QDEC_API int q8_0_gemv_topk(const void* w, int64_t n_in, int64_t n_out, int64_t 
  * q8_0_gemv_topk (same logits bits and the same top_idx/top_val), but it calls
  * no hipMalloc, hipFree or other allocating routine:
  *   - w must already have its repacked copies (qdec_prepare), else QDEC_EINVAL;
- *   - its scratch (the split activations of the 3..8-row matrix-core
- *     projection, then the top-k candidate lists) is one static device array
- *     of QDEC_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends;
- *     calls needing more (large batch x k x n_out) are rejected with
- *     QDEC_EINVAL before any launch.  128256 logits fit for every batch and k.
+ *   - its scratch (the K slices' sums of the 3..8-row matrix-core
+ *     projection where it splits K, then the top-k candidate lists) is one
+ *     static device array of QDEC_NOALLOC_SCRATCH_BYTES per GPU, held until
+ *     the process ends; calls needing more (large batch x k x n_out, or
+ *     3..8 rows of a wide n_in) are rejected with QDEC_EINVAL before any
+ *     launch.  128256 logits of n_in <= 3072 fit for every batch and k.
  * Every call on one GPU uses that GPU's one array: calls that overlap in time
  * on one GPU (on different streams, or from different host threads) race and
  * must not be made; calls ordered on one stream are safe.  Nothing carries
  * over from one call to the next (every scratch byte read is written first
  * in the same call). */
-#define QDEC_NOALLOC_SCRATCH_BYTES (8 << 20)
+#define QDEC_NOALLOC_SCRATCH_BYTES (16 << 20)
 QDEC_API int q8_0_gemv_topk_noalloc(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
                                     const float* x, int64_t k, float* logits, int32_t* top_idx,
                                     float* top_val, hipStream_t stream);

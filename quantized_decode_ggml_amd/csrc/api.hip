@@ -311,10 +311,14 @@ int q8_gemv_common(GemvMode mode, const char* fn, const void* const* ws, int nw,
             if (tb) tiles[k] = q8t_view(tb, n_in, rows[k]);
             else have = false;
         }
-        void* wsp = fixed_ws;
-        if (have && !wsp && !noalloc)
-            QDEC_TRY(stream_workspace(s, q8_mfma_workspace_bytes(mode, n_in, rows[0], batch), &wsp));
-        if (have && wsp) return finish(launch_q8_0_gemv_mfma(p, tiles, wsp, s), fn);
+        // the K slices' sums (none when every workgroup covers whole rows)
+        int64_t flat = rows[0];
+        if (mode == kQKV)
+            for (int k = 1; k < nw; ++k) flat += rows[k];
+        const int64_t need = q8_mfma_workspace_bytes(mode, n_in, flat, batch);
+        void* wsp = need > 0 ? fixed_ws : nullptr;
+        if (have && need > 0 && !wsp && !noalloc) QDEC_TRY(stream_workspace(s, need, &wsp));
+        if (have && (need == 0 || wsp)) return finish(launch_q8_0_gemv_mfma(p, tiles, wsp, s), fn);
     }
     return finish(launch_q8_0_gemv(p, s), fn);
 }
@@ -491,9 +495,8 @@ int q8_0_gemv_topk_noalloc(const void* w, int64_t n_in, int64_t n_out, int64_t b
     QDEC_TRY(check_dims(fn, n_in, n_out, batch, 32, QDEC_GEMV_MAX_BATCH));
     if (k < 1 || k > QDEC_TOPK_MAX || k > n_out)
         return fail(QDEC_EINVAL, "%s: k=%lld outside [1, min(n_out, %d)]", fn, (long long)k, QDEC_TOPK_MAX);
-    // scratch layout: the split activations of the matrix-core projection
-    // (3..8 batch rows, with its K slices' sums), then the top-k candidate
-    // lists
+    // scratch layout: the K slices' sums of the matrix-core projection (3..8
+    // batch rows, when it splits K), then the top-k candidate lists
     const int64_t proj = batch >= 3 ? align_up(q8_mfma_workspace_bytes(kPlain, n_in, n_out, batch), kAlign) : 0;
     const int64_t need = proj + topk_workspace_bytes(n_out, batch, (int)k);
     if (need > kNoAllocScratchBytes)

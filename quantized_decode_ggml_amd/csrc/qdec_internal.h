@@ -216,11 +216,12 @@ hipError_t launch_rmsnorm(const float* x, int64_t n, int64_t batch, const float*
                           hipStream_t s);
 
 // Matrix-core path for 3..8 batch rows (gemv_q8_0_mfma.hip).  It reads the
-// fragment-tiled copies of the segments and needs a device workspace of
-// q8_mfma_workspace_bytes(mode, n_in, rows of the first segment, batch)
-// bytes for the split activations (and the K slices' sums), owned by the
-// caller and used in stream order.
-int64_t q8_mfma_workspace_bytes(int mode, int64_t n_in, int64_t rows0, int64_t batch);
+// fragment-tiled copies of the segments; where it splits K over workgroups
+// it needs a device workspace of q8_mfma_workspace_bytes(mode, n_in, flat
+// rows, batch) bytes for the slices' sums (0: none), owned by the caller and
+// used in stream order.  Flat rows: the sum of the QKV segments, else the
+// rows of the first matrix.
+int64_t q8_mfma_workspace_bytes(int mode, int64_t n_in, int64_t rows, int64_t batch);
 bool q8_mfma_supported(const Q8GemvProblem& p);
 hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, void* workspace,
                                  hipStream_t s);

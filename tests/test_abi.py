@@ -86,3 +86,18 @@ def test_python_wrapper_raises():
         qd.q8_0_gemv(Fake(FAKE, 1), 33, 4, Fake(FAKE, 33), out=Fake(FAKE * 2, 4), stream=0)
     assert ei.value.status == qd.QDEC_EINVAL
     assert "multiple of 32" in str(ei.value)
+
+
+@pytest.mark.parametrize("n_in,batch,k,fits", [(3072, 8, 256, True), (3072, 5, 40, True), (3072, 3, 1, True),
+                                               (1024, 8, 256, True), (8192, 8, 256, False)])
+def test_noalloc_scratch_covers_the_vocabulary(n_in, batch, k, fits):
+    """q8_0_gemv_topk_noalloc sizes its static scratch before anything else:
+    128256 logits of n_in <= 3072 fit for every batch and k (the matrix-core
+    projection's K-slice sums plus the candidate lists); 8 rows of 8192
+    columns do not, and are refused by the size check itself."""
+    W, X, LOG, IDX, VAL = 0x40000000, 0x1000000, 0x10000000, 0x20000000, 0x30000000
+    before = qd.launch_count()
+    rc = qd.lib.q8_0_gemv_topk_noalloc(W, n_in, 128256, batch, X, k, LOG, IDX, VAL, None)
+    assert rc != qd.QDEC_OK          # no GPU here: a call that fits fails later, at the device
+    assert ("static array" in qd.last_error()) == (not fits), qd.last_error()
+    assert qd.launch_count() == before

@@ -17,8 +17,9 @@ from helpers import check_f32, q8_weights, swiglu_tol, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-# widths the matrix-core path takes (n_in / 32 blocks split over 4 or 8 waves)
-MFMA_WIDTHS = [1024, 2048, 3072, 4096, 6144, 8192]
+# widths the matrix-core path takes (n_in a multiple of 256 up to 8192): every
+# K slice size (8, 16, 24, 32 blocks) and one slice per row at 256
+MFMA_WIDTHS = [256, 768, 1024, 2048, 2560, 3072, 4096, 6144, 8192]
 
 
 @pytest.fixture(scope="module")
@@ -53,14 +54,15 @@ def launches(qd, fn):
     return r, qd.launch_count() - before
 
 
-@pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 3), (3072, 4, 3),
-                                               (3072, 8, 3), (8192, 5, 3), (2048, 8, 3), (1024, 8, 2),
-                                               (512, 4, 1), (2560, 8, 1)])
+@pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 2), (3072, 4, 2),
+                                               (3072, 8, 2), (8192, 5, 2), (2048, 8, 2), (1024, 8, 2),
+                                               (512, 4, 2), (2560, 8, 2), (256, 6, 1), (2080, 8, 1),
+                                               (9216, 4, 1)])
 def test_path_selection(qd, n_in, batch, expect):
-    """3..8 rows at a supported width: x split + matrix-core kernel, and, where K
-    is split over workgroups (48 rows, n_in a multiple of 1024 from 2048),
-    the ordered sum of the slices (3 launches; 2 at 1024, a single slice);
-    otherwise the VALU kernel (1 launch)."""
+    """3..8 rows at a supported width (n_in % 256 == 0, up to 8192): the
+    matrix-core kernel, plus the ordered sum of its K slices where K is split
+    over workgroups (2 launches; 48 rows always split K from 512 columns,
+    256 columns is one slice); otherwise the VALU kernel (1 launch)."""
     n_out = 48
     raw = q8_weights(9000 + n_in, n_out, n_in)
     x = synth.normal_f32(9001 + batch, (batch, n_in))
@@ -139,10 +141,9 @@ def test_residual_in_place(qd, batch):
 @pytest.mark.parametrize("n_out", [8192, 1024])
 def test_graph_capture_with_workspace(qd, n_out):
     """Warm-up on the capture stream makes its workspace; the captured graph
-    then uses the matrix-core path (2 launches recorded, 3 with the K split
-    over workgroups below 8192 rows) and every replay, with eager work in
-    between, matches the eager result bit for bit (the K slices
-    are added in a fixed order by a third launch)."""
+    then uses the matrix-core path (2 launches recorded: the kernel and the
+    ordered sum of its K slices) and every replay, with eager work in
+    between, matches the eager result bit for bit."""
     bitwise = True
     n_in, batch = 3072, 4
     raw = q8_weights(9600, n_out, n_in)
@@ -160,7 +161,7 @@ def test_graph_capture_with_workspace(qd, n_out):
     before = qd.launch_count()
     with torch.cuda.graph(g, stream=s):
         qd.q8_0_gemv(w, n_in, n_out, xd, out=out)
-    assert qd.launch_count() - before == (2 if n_out >= 8192 else 3)
+    assert qd.launch_count() - before == 2
     ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
     for k in range(3):
         out.fill_(float("nan"))
@@ -176,9 +177,9 @@ def test_graph_capture_with_workspace(qd, n_out):
 @pytest.mark.parametrize("n_out,n_in,mode", [(3072, 8192, "residual"), (1024, 2048, "plain"), (77, 3072, "plain")])
 @pytest.mark.parametrize("batch", [3, 5, 8])
 def test_k_split_bitwise_reproducible(qd, n_out, n_in, mode, batch):
-    """Fewer than 8192 rows: K split over workgroups, the slices added in slice
-    order by a third launch.  Five calls give the same bits, and they match
-    the oracle to the f32 bound."""
+    """K split over workgroups, the slices added in slice order by a second
+    launch.  Five calls give the same bits, and they match the oracle to the
+    f32 bound."""
     raw = q8_weights(9650 + n_out, n_out, n_in)
     x = synth.normal_f32(9651 + batch, (batch, n_in))
     r = synth.normal_f32(9652 + batch, (batch, n_out))
@@ -190,7 +191,7 @@ def test_k_split_bitwise_reproducible(qd, n_out, n_in, mode, batch):
             out, n = launches(qd, lambda: qd.q8_0_gemv_residual(w, n_in, n_out, xd, rd))
         else:
             out, n = launches(qd, lambda: qd.q8_0_gemv(w, n_in, n_out, xd))
-        assert n == 3
+        assert n == 2
         runs.append(host(out))
     for k in range(1, 5):
         assert np.array_equal(runs[k].view(np.uint32), runs[0].view(np.uint32)), f"call {k} differs"
@@ -223,6 +224,69 @@ def test_graph_capture_without_workspace_falls_back(qd):
         g.replay()
         check_f32(host(out), ref, S, f"fallback replay {k}")
     del g
+
+
+@pytest.mark.parametrize("mode", ["plain", "residual", "qkv", "swiglu"])
+def test_one_slice_per_row_needs_no_workspace(qd, mode):
+    """28672 rows x 1024 columns fill the chip with one K slice per row: the
+    workgroups store the rows themselves (1 launch), so a capture on a stream
+    that has no workspace still takes the matrix-core kernel; replays match
+    the eager result bit for bit and the oracle to the f32 bound."""
+    n_in, batch = 1024, 5
+    n_out = 28672 if mode != "qkv" else 14336
+    raws = [q8_weights(9720 + k, n_out, n_in) for k in range(3 if mode == "qkv" else 2 if mode == "swiglu" else 1)]
+    x = synth.normal_f32(9725, (batch, n_in))
+    r = synth.normal_f32(9726, (batch, n_out))
+    ws = [dev(w) for w in raws]
+    for w in ws:
+        qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    xd, rd = dev(x), dev(r)
+
+    def call(**kw):
+        if mode == "plain":
+            return qd.q8_0_gemv(ws[0], n_in, n_out, xd, **kw)
+        if mode == "residual":
+            return qd.q8_0_gemv_residual(ws[0], n_in, n_out, xd, rd, **kw)
+        if mode == "swiglu":
+            return qd.q8_0_swiglu(ws[0], ws[1], n_in, n_out, xd, **kw)
+        return qd.q8_0_qkv(ws[0], ws[1], ws[2], n_in, n_out, n_out, xd, *kw.get("outs", ()))
+
+    eager, n = launches(qd, call)
+    assert n == 1
+    eager = [host(t) for t in eager] if mode == "qkv" else [host(eager)]
+    outs = [torch.empty((batch, n_out), device="cuda") for _ in eager]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    before = qd.launch_count()
+    with torch.cuda.graph(g, stream=s):
+        if mode == "qkv":
+            call(outs=outs)
+        else:
+            call(out=outs[0])
+    assert qd.launch_count() - before == 1
+    for k in range(2):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        for o, e in zip(outs, eager):
+            assert np.array_equal(host(o).view(np.uint32), e.view(np.uint32)), f"replay {k}"
+    del g
+    if mode == "plain":
+        ref, S = oracle.q8_0_gemv(raws[0], n_in, n_out, x)
+        check_f32(eager[0], ref, S, "one slice plain")
+    elif mode == "residual":
+        ref, S = oracle.q8_0_gemv_residual(raws[0], n_in, n_out, x, r)
+        check_f32(eager[0], ref, S, "one slice residual")
+    elif mode == "swiglu":
+        ref = oracle.q8_0_swiglu(raws[0], raws[1], n_in, n_out, x)
+        err = np.abs(eager[0].astype(np.float64) - ref["out"])
+        assert (err <= swiglu_tol(ref)).all(), f"worst err/tol {np.max(err / swiglu_tol(ref)):.3g}"
+    else:
+        refs, ss = oracle.q8_0_qkv(raws[0], raws[1], raws[2], n_in, n_out, n_out, x)
+        for e, ref, S, key in zip(eager, refs, ss, "qkv"):
+            check_f32(e, ref, S, f"one slice {key}")
 
 
 def test_capture_with_pending_repack_is_rejected(qd):

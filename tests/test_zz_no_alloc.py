@@ -34,9 +34,9 @@ def _noalloc(qd, w, n_in, n_out, x, k, logits, idx, val, stream):
 
 
 # (n_out, n_in, batch, k, seed); 3..8 rows take the matrix-core projection,
-# whose split activations live in the scratch (n_out >= 8192 keeps it free of
-# the atomic K split, so the logits are reproducible bit for bit); more than
-# 4096 logits use the candidate lists in the scratch
+# whose K slices' sums live in the scratch (added in a fixed order, so the
+# logits are reproducible bit for bit); more than 4096 logits use the
+# candidate lists in the scratch
 @pytest.mark.parametrize("cases", [[(50000, 3072, 4, 40, 91), (3000, 1024, 2, 7, 92)],
                                    [(40000, 3072, 8, 256, 93), (9000, 2048, 3, 1, 94)]])
 def test_noalloc_matches_allocating_entry_point(qd, cases):
