@@ -37,8 +37,8 @@
 //
 // Layout of the work: the weights come from the fragment-tiled copy (one
 // contiguous 512-byte tile per 16 rows x 32 k, scales alongside), so every
-// wave load is contiguous.  A workgroup is eight waves, one 16-row group each
-// (x 2 matrices for SwiGLU), over one K slice of NBW blocks; all eight share
+// wave load is contiguous.  A workgroup is four waves, one 16-row group each
+// (x 2 matrices for SwiGLU), over one K slice of NBW blocks; all four share
 // the x fragments of that slice, which the workgroup builds once in LDS: every
 // thread loads 8 values of one batch row, splits them and writes the three
 // parts' fragments.  The x loads go out first, then each wave's first D
@@ -68,8 +68,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kParts = 3;
 
-constexpr int kWaves = 8;   // row groups (one per wave) of a workgroup
-constexpr int kDepth = 8;   // blocks a wave keeps in flight ahead of the one computed
+constexpr int kWaves = 4;   // row groups (one per wave) of a workgroup
+constexpr int kDepth = 6;   // blocks a wave keeps in flight ahead of the one computed
 
 // x = hi + mid + lo (see above): the top 16 bits of each part's f32 pattern.
 __device__ inline void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo)
@@ -277,7 +277,11 @@ __global__ __launch_bounds__(kWaves * 64) void q8_0_gemv_mfma(Q8GemvArgs a, Tile
 }
 
 // Output (b, row) of a K-split product: the slices' sums in slice order, then
-// the epilogue.  One thread per output, rows fastest.
+// the epilogue.  One thread per output, rows fastest.  Every slice's sum is
+// loaded before the first add (a load-add loop would wait out one memory
+// latency per slice).
+constexpr int kMaxSlices = 32;   // n_in <= 8192 in slices of at least 8 blocks
+
 template <int MODE>
 __global__ __launch_bounds__(256) void sum_slices_kernel(Q8GemvArgs a, const float* __restrict__ part, int ksplit)
 {
@@ -290,12 +294,20 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(Q8GemvArgs a, const flo
     const int w = (int)(g % kWaves), r = (int)(row & 15);
     const int64_t per = (int64_t)kWaves * NM * a.batch * 16;
     const float* p = part + set * ksplit * per + ((int64_t)w * NM * a.batch + b) * 16 + r;
-    float v0 = p[0], v1 = NM == 2 ? p[a.batch * 16] : 0.f;
-    for (int k = 1; k < ksplit; ++k) {
-        v0 += p[k * per];
-        if constexpr (NM == 2) v1 += p[k * per + a.batch * 16];
+    float v[NM][kMaxSlices];
+#pragma unroll
+    for (int k = 0; k < kMaxSlices; ++k)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) v[m][k] = k < ksplit ? p[k * per + m * a.batch * 16] : 0.f;
+    float s[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        s[m] = v[m][0];
+#pragma unroll
+        for (int k = 1; k < kMaxSlices; ++k)
+            if (k < ksplit) s[m] += v[m][k];
     }
-    store_row<MODE>(a, row, b, v0, v1);
+    store_row<MODE>(a, row, b, s[0], s[NM - 1]);
 }
 
 using MfmaFn = void (*)(Q8GemvArgs, TileArgs);
@@ -333,8 +345,12 @@ int64_t flat_rows(const Q8GemvProblem& p)
 
 // Blocks per K slice: the largest of 32, 24, 16, 8 that divides the row's
 // n_in / 32 blocks and still gives at least kMinGrid workgroups (else 8, the
-// most slices).  One slice per row needs no second launch.
-constexpr int64_t kMinGrid = 224;
+// most slices).  One slice per row needs no second launch.  Measured
+// (graph-replayed, both launches, 3072x8192 with residual / SwiGLU 2x8192x3072
+// at 8 rows): 8 waves, 6-8 blocks in flight, >= 224 workgroups 12.2 / 15.8 us;
+// 16 in flight 13.1 / 18.1; 4 waves, >= 448 workgroups 11.0-11.4 / 15.4-16.7
+// (4-8 in flight); 4 waves, >= 1024: 13.8 / 18.6; 2 waves 15.7-17.6 / 22-23.
+constexpr int64_t kMinGrid = 448;
 
 int slice_blocks(int64_t n_in, int64_t rows)
 {
@@ -396,6 +412,7 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
     const int64_t rows = flat_rows(p);
     const int nbw = slice_blocks(p.n_in, rows);
     t.ksplit = (int)(t.nb / nbw);
+    if (t.ksplit > kMaxSlices) return hipErrorNotSupported;
     if (t.ksplit > 1) {
         if (!workspace) return hipErrorInvalidValue;
         t.part = static_cast<float*>(workspace);
