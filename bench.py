@@ -517,6 +517,37 @@ def time_graph(launch, n, stream_holder, torch, warm=3):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def vendor_gemm(args):
+    """Reference point for the batched GEMM: the vendor bf16 GEMM (torch.matmul
+    on bf16 operands, which ROCm routes to hipBLASLt) at the config-3 shapes,
+    C = A W^T with bf16 output (half the output bytes of the library's f32).
+    Timed eagerly (events around 200 launches rotating over 8 weights; each
+    launch takes longer than its host call); not part of the product path."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    for M in (128, 512):
+        for N, K in ((8192, 3072), (3072, 8192)):
+            a = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=g)
+            ws = [torch.randn(N, K, device=dev, dtype=torch.bfloat16, generator=g) * 0.02 for _ in range(8)]
+            out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+            for i in range(20):
+                torch.matmul(a, ws[i % 8].t(), out=out)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(200):
+                torch.matmul(a, ws[i % 8].t(), out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 200
+            print(json.dumps({"vendor_gemm": "torch.matmul bf16 (hipBLASLt)", "M": M, "N": N, "K": K,
+                              "mean_us": round(us, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1),
+                              "pct_bf16_peak": round(100 * 2.0 * M * N * K / us / 1e6 / BF16_PEAK_TFLOPS, 2)}),
+                  flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -529,6 +560,9 @@ def main():
                     help="with --suite: time only the workloads whose name starts with this prefix (e.g. 'c3')")
     ap.add_argument("--ceiling", action="store_true",
                     help="time the plain streaming-read kernel at the decode products' byte counts")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor bf16 GEMM (torch.matmul, hipBLASLt) at the batched-GEMM shapes, "
+                         "as a reference point")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 64 MiB device copy (untimed), the known-size reference that "
                          "scales the profiler's HBM byte counters (with the step or with --suite)")
@@ -546,6 +580,9 @@ def main():
         return
     if args.ceiling:
         ceiling(args)
+        return
+    if args.vendor_gemm:
+        vendor_gemm(args)
         return
 
     import torch

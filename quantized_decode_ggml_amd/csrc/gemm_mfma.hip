@@ -285,10 +285,13 @@ __global__ __launch_bounds__(256) void x_to_bf16(const float4* __restrict__ x, b
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) xb[i] = to_bf16x4(x[i]);
 }
 
-constexpr int kDmaStages = 4;
+// Stages of the LDS ring (as many as the 160 KB of LDS hold), each slot
 // X | W | D: Q8_0 int8 rows and 512 B of scales (+ 256 B overflow); bf16 rows
+constexpr int kDmaStagesQ8 = 4, kDmaStagesBf16 = 4;
 template <bool BF16W>
 constexpr int dma_slot() { return BF16W ? 16384 + 16384 : 16384 + 8192 + 768; }
+template <bool BF16W>
+constexpr int dma_stages() { return BF16W ? kDmaStagesBf16 : kDmaStagesQ8; }
 
 // BF16W: the weights are bf16 rows laid out like x (no scales, nothing to
 // dequantise: the B fragments are read as they stand), two DMAs a stage for
@@ -296,10 +299,12 @@ constexpr int dma_slot() { return BF16W ? 16384 + 16384 : 16384 + 8192 + 768; }
 template <bool BF16W>
 __global__ __launch_bounds__(512) void gemm_dma(DmaArgs a)
 {
-    constexpr int P = kDmaStages, U = 2 * P, BM = 128, BN = 128;
+    constexpr int P = dma_stages<BF16W>(), U = 2 * P, BM = 128, BN = 128;
+    static_assert(P >= 4 && P <= 6, "ring of 4..6 stage arrays");
     constexpr int SLOT = dma_slot<BF16W>();
-    __shared__ __attribute__((aligned(1024))) char S0[SLOT], S1[SLOT], S2[SLOT], S3[SLOT];
-#define QDEC_SLOT(u) ((u) == 0 ? S0 : (u) == 1 ? S1 : (u) == 2 ? S2 : S3)
+    constexpr int SLOT4 = P > 4 ? SLOT : 16, SLOT5 = P > 5 ? SLOT : 16;
+    __shared__ __attribute__((aligned(1024))) char S0[SLOT], S1[SLOT], S2[SLOT], S3[SLOT], S4[SLOT4], S5[SLOT5];
+#define QDEC_SLOT(u) ((u) == 0 ? S0 : (u) == 1 ? S1 : (u) == 2 ? S2 : (u) == 3 ? S3 : (u) == 4 ? S4 : S5)
     const int64_t id = blockIdx.x;
     const int64_t slice = id % a.splits, tile = id / a.splits;
     const int64_t n0 = (tile % a.ntiles) * BN, m0 = (tile / a.ntiles) * BM;
