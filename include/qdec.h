@@ -336,6 +336,18 @@ QDEC_API const char* qdec_last_error(void);
  * the GPU path ran; [QTensorEngine] gemm_parity_probe). */
 QDEC_API uint64_t qdec_launch_count(void);
 
+/* Host-side extent check, no device needed: for an n_out x n_in product at
+ * `batch` rows, work out every launch plan the library would choose (the
+ * 3..8-row matrix-core GEMV in its plain, residual, SwiGLU and QKV forms;
+ * the batched GEMMs on Q8_0 weights and on dense f32 weights with and
+ * without their bf16 copy, each with and without a workspace) and check that
+ * the last element each kernel instance reads or writes lies inside the
+ * buffers it is given (weights, x, workspace).  The launchers run the same
+ * checks and refuse a failing plan.  QDEC_OK, QDEC_EINVAL for invalid
+ * dimensions (n_in % 32 != 0, ...), QDEC_EUNSUPPORTED naming the overrun
+ * otherwise (a library bug). */
+QDEC_API int qdec_check_plans(int64_t n_in, int64_t n_out, int64_t batch);
+
 /* One empty kernel on `stream` (launch-latency probe, the analogue of
  * [QTensorEngine] bench_empty_submit_roundtrip). */
 QDEC_API int qdec_empty_kernel(hipStream_t stream);

@@ -58,6 +58,7 @@ _SIGS = {
     "qdec_empty_kernel": [_P],
     "qdec_copy": [_P, _P, _I, _P],
     "qdec_stream_read": [_P, _I, ctypes.c_int, _P, _P],
+    "qdec_check_plans": [_I, _I, _I],
 }
 for _name, _args in _SIGS.items():
     getattr(lib, _name).argtypes = _args
@@ -312,6 +313,13 @@ def clear_cache():
     used the library) and every storage the binding kept alive."""
     lib.qdec_clear_cache()
     _pinned.clear()
+
+
+def check_plans(n_in, n_out, batch):
+    """Host-side extent check of every launch plan for this shape (no device
+    needed); raises QdecError naming the overrun if a plan would leave its
+    buffers."""
+    _check(lib.qdec_check_plans(n_in, n_out, batch))
 
 
 def cache_len() -> int:

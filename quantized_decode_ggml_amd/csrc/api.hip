@@ -751,6 +751,51 @@ int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream
     return QDEC_OK;
 }
 
+int qdec_check_plans(int64_t n_in, int64_t n_out, int64_t batch)
+{
+    const char* fn = "qdec_check_plans";
+    QDEC_TRY(check_dims(fn, n_in, n_out, batch, 32, 0));
+    auto bad = [&](const std::string& why) { return fail(QDEC_EUNSUPPORTED, "%s: %s", fn, why.c_str()); };
+    // the 3..8-row matrix-core GEMV in each of its forms (QKV: the rows as
+    // q, a quarter of them as k and as v, all but the last segment whole
+    // 16-row groups), with the workspace each would be given
+    if (batch >= 3 && batch <= QDEC_GEMV_MAX_BATCH) {
+        const int64_t q16 = n_out / 16 * 16, kv16 = n_out / 64 * 16;
+        for (GemvMode mode : {kPlain, kResidual, kSwiGLU, kQKV}) {
+            Q8GemvProblem p{};
+            p.mode = mode;
+            p.n_in = n_in;
+            p.batch = batch;
+            p.nseg = 1;
+            p.rows[0] = n_out;
+            if (mode == kQKV) {
+                if (q16 == 0 || kv16 == 0) continue;
+                p.nseg = 3;
+                p.rows[0] = q16;
+                p.rows[1] = kv16;
+                p.rows[2] = n_out - q16 + kv16;
+            }
+            if (!q8_mfma_supported(p)) continue;
+            int64_t flat = p.rows[0];
+            if (mode == kQKV) flat += p.rows[1] + p.rows[2];
+            const std::string why = q8_mfma_plan_check(p, q8_mfma_workspace_bytes(mode, n_in, flat, batch));
+            if (!why.empty()) return bad(why);
+        }
+    }
+    // the batched GEMMs, with and without a workspace (a capture on a stream
+    // that has none), dense f32 with and without its bf16 copy
+    for (bool ws : {true, false}) {
+        std::string why = q8_gemm_plan_check(n_in, n_out, batch, ws ? q8_gemm_workspace_bytes(n_in, n_out, batch) : 0);
+        if (!why.empty()) return bad(why);
+        for (bool copy : {true, false}) {
+            why = f32_gemm_plan_check(n_in, n_out, batch, copy,
+                                      ws ? f32_gemm_workspace_bytes(n_in, n_out, batch, copy) : 0);
+            if (!why.empty()) return bad(why);
+        }
+    }
+    return QDEC_OK;
+}
+
 int qdec_release(const void* w)
 {
     int dev = 0;

@@ -33,6 +33,9 @@
 // Block ids go to the XCDs round-robin; with the tile index n-fastest the m
 // tiles that share a weight tile land on one XCD whenever the n-tile count is
 // a multiple of 8.
+#include <cstdio>
+#include <string>
+
 #include "qdec_internal.h"
 
 namespace qdec {
@@ -632,9 +635,82 @@ int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch, boo
     return dma_x_bytes(n_in, batch) + (s > 1 ? (int64_t)s * batch * n_out * 4 : 0);
 }
 
+// Host-side extent checks of the plans below: the last element each kernel
+// instance reads or writes, worked out again from the plan and the kernels'
+// index formulas, against the extents of x, W, the scale plane, the
+// workspace and out.  "" when every access stays inside.
+static std::string gemm_over(const char* what, int64_t end, int64_t size)
+{
+    char why[256];
+    std::snprintf(why, sizeof why, "batched GEMM plan: %s ends at %lld, extent %lld", what, (long long)end,
+                  (long long)size);
+    return std::string(why);
+}
+
+static std::string dma_plan_check(int64_t M, int64_t N, int64_t K, bool q8, int64_t ws_bytes)
+{
+    if (K % 64 || (q8 && (N % 2 || N < 2))) return gemm_over("K % 64 / even N", K, 0);
+    const int splits = dma_splits(M, N, K);
+    const int64_t kslice = dma_kslice(K, splits), nsl = (K + kslice - 1) / kslice;
+    if (kslice <= 0 || kslice % 64) return gemm_over("K slice", kslice, K);
+    if (nsl > splits) return gemm_over("slices", nsl, splits);
+    // the last slice starts inside K and its stages end exactly at K
+    const int64_t kbeg = (nsl - 1) * kslice, klen = K - kbeg;
+    if (klen <= 0 || klen > kslice || klen % 64) return gemm_over("last slice", kbeg + klen, K);
+    const int64_t ns = klen / 64;
+    // x (bf16, workspace) and W rows: row clamped to M-1 / N-1, the last
+    // stage's chunk 7 (bf16) or 3 (int8) of the last slice
+    const int64_t x_end = (M - 1) * K + kbeg + (ns - 1) * 64 + 7 * 8 + 8;
+    if (x_end > M * K) return gemm_over("x (bf16)", x_end, M * K);
+    if (2 * M * K > dma_x_bytes(K, M)) return gemm_over("x in the workspace (bytes)", 2 * M * K, dma_x_bytes(K, M));
+    const int64_t w_end = (N - 1) * K + kbeg + (ns - 1) * 64 + (q8 ? 3 * 16 + 16 : 7 * 8 + 8);
+    if (w_end > N * K) return gemm_over("W rows", w_end, N * K);
+    if (q8) {
+        // block-major scales: block kbeg/32 + 1 + 2 (ns - 1) of row pair N-2, N-1
+        const int64_t d_end = (kbeg / 32 + 1 + 2 * (ns - 1)) * N + (N - 2) + 2;
+        if (d_end > (K / 32) * N) return gemm_over("scale plane", d_end, (K / 32) * N);
+    }
+    const int64_t grid = ((M + 127) / 128) * ((N + 127) / 128) * nsl;
+    if (grid > INT32_MAX) return gemm_over("grid", grid, INT32_MAX);
+    if (nsl > 1) {
+        const int64_t need = dma_x_bytes(K, M) + nsl * M * N * 4;
+        if (need > ws_bytes) return gemm_over("slice partials (bytes)", need, ws_bytes);
+    } else if (dma_x_bytes(K, M) > ws_bytes) {
+        return gemm_over("workspace (bytes)", dma_x_bytes(K, M), ws_bytes);
+    }
+    return std::string();
+}
+
+static std::string reg_plan_check(int64_t M, int64_t N, int64_t K, int64_t ws_bytes)
+{
+    const GemmArgs a = plan(M, N, K);
+    if (a.kslice <= 0 || a.kslice % BK) return gemm_over("K slice", a.kslice, K);
+    if ((int64_t)(a.splits - 1) * a.kslice >= K || (int64_t)a.splits * a.kslice < K)
+        return gemm_over("slices x K slice", (int64_t)a.splits * a.kslice, K);
+    if (a.mtiles * a.ntiles * a.splits > INT32_MAX) return gemm_over("grid", a.mtiles * a.ntiles * a.splits, INT32_MAX);
+    // partials go to the workspace when there is one (else atomics into out)
+    if (a.splits > 1 && ws_bytes > 0 && (int64_t)a.splits * M * N * 4 > ws_bytes)
+        return gemm_over("slice partials (bytes)", (int64_t)a.splits * M * N * 4, ws_bytes);
+    return std::string();
+}
+
+std::string q8_gemm_plan_check(int64_t n_in, int64_t n_out, int64_t batch, int64_t ws_bytes)
+{
+    if (ws_bytes > 0 && dma_ok(n_out, n_in)) return dma_plan_check(batch, n_out, n_in, true, ws_bytes);
+    return reg_plan_check(batch, n_out, n_in, ws_bytes);
+}
+
+std::string f32_gemm_plan_check(int64_t n_in, int64_t n_out, int64_t batch, bool bf16_copy, int64_t ws_bytes)
+{
+    if (bf16_copy && ws_bytes > 0 && n_in % 64 == 0) return dma_plan_check(batch, n_out, n_in, false, ws_bytes);
+    return reg_plan_check(batch, n_out, n_in, ws_bytes);
+}
+
 hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch, const float* x,
                             float* out, void* workspace, hipStream_t s)
 {
+    if (!q8_gemm_plan_check(n_in, n_out, batch, workspace ? q8_gemm_workspace_bytes(n_in, n_out, batch) : 0).empty())
+        return hipErrorInvalidConfiguration;
     if (workspace && dma_ok(n_out, n_in)) {
         const int64_t n4 = batch * n_in / 4;   // n_in % 64 == 0
         int64_t blocks = (n4 + 255) / 256;
@@ -682,6 +758,10 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
 hipError_t launch_f32_gemm(const float* wf, const void* wbf16, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, void* workspace, hipStream_t s)
 {
+    const bool copy = wbf16 != nullptr;
+    if (!f32_gemm_plan_check(n_in, n_out, batch, copy,
+                             workspace ? f32_gemm_workspace_bytes(n_in, n_out, batch, copy) : 0).empty())
+        return hipErrorInvalidConfiguration;
     if (wbf16 && workspace && n_in % 64 == 0) {
         // the weight's bf16 copy (qdec_prepare): the DMA-fed kernel reads it
         // as it reads x

@@ -55,6 +55,9 @@
 // (x traffic 2-4x the weight bytes at 6-8 rows); and a K split whose slices
 // were added with f32 atomics, or merged by the last workgroup of a row set
 // behind a device-scope release fence, which writes back the whole L2.)
+#include <cstdio>
+#include <string>
+
 #include "gemv_common.h"
 
 namespace qdec {
@@ -364,6 +367,55 @@ int slice_blocks(int64_t n_in, int64_t rows)
 
 }  // namespace
 
+// Host-side extent check of a launch plan: the last element each kernel
+// instance reads or writes, worked out again from the plan and the kernels'
+// index formulas, against the extents of the buffers the launch is given (the
+// tiled planes of every segment, x, the workspace).  Returns an empty string
+// when every access stays inside, else what overruns.  A failing plan is a
+// library bug: the launch is refused rather than run.
+std::string q8_mfma_plan_check(const Q8GemvProblem& p, int64_t ws_bytes)
+{
+    char why[256];
+    auto over = [&](const char* what, int64_t end, int64_t size) {
+        std::snprintf(why, sizeof why, "3..8-row GEMV plan: %s ends at %lld, extent %lld", what, (long long)end,
+                      (long long)size);
+        return std::string(why);
+    };
+    const int64_t nb = p.n_in / 32, rows = flat_rows(p);
+    const int nbw = slice_blocks(p.n_in, rows);
+    const int64_t ksplit = nb / nbw;
+    if (nbw != 8 && nbw != 16 && nbw != 24 && nbw != 32) return over("slice blocks", nbw, 32);
+    if (ksplit * nbw != nb) return over("slices x slice blocks", ksplit * nbw, nb);
+    if (ksplit > kMaxSlices) return over("slices", ksplit, kMaxSlices);
+    const int nv = frags_for(p.batch), nm = p.mode == kSwiGLU ? 2 : 1;
+    if (3 * p.batch > 16 * nv) return over("stacked x rows", 3 * p.batch, 16 * nv);
+    // x: item (b, i, o) of the last slice reads floats b*n_in + 32*(blk0 + i) + 8*o .. +7
+    const int64_t x_end = (p.batch - 1) * p.n_in + ((ksplit - 1) * nbw + nbw - 1) * 32 + 3 * 8 + 8;
+    if (x_end > p.batch * p.n_in) return over("x", x_end, p.batch * p.n_in);
+    // tiles and scales: the last group of each segment (loads clamp the row
+    // group to the last one), every block of the last slice
+    for (int k = 0; k < (p.mode == kSwiGLU ? 2 : p.nseg); ++k) {
+        const int64_t segrows = p.mode == kSwiGLU ? p.rows[0] : p.rows[k];
+        const int64_t g = q8t_groups(segrows), tiles = g * nb;
+        const int64_t q_end = ((g - 1) * nb + (ksplit - 1) * nbw + nbw - 1) * 512 + 8 * 63 + 8;
+        const int64_t d_end = (((g - 1) * nb + (ksplit - 1) * nbw + nbw - 1) * 16 + 15 + 1) * 2;
+        if (q_end > tiles * 512) return over("weight tiles", q_end, tiles * 512);
+        if (d_end > tiles * 32) return over("tile scales", d_end, tiles * 32);
+    }
+    if (ksplit > 1) {
+        // partial sums of the last (set, slice, wave), and the slice-sum reads
+        const int64_t sets = (q8t_groups(rows) + kWaves - 1) / kWaves;
+        const int64_t per = (int64_t)kWaves * nm * p.batch * 16;
+        const int64_t w_end = (sets * ksplit - 1) * per + (int64_t)(kWaves - 1) * nm * p.batch * 16 +
+                              ((nm - 1) * p.batch + p.batch - 1) * 16 + 16;
+        const int64_t r_end = (sets - 1) * ksplit * per + ((int64_t)(kWaves - 1) * nm * p.batch + p.batch - 1) * 16 +
+                              15 + (ksplit - 1) * per + (nm - 1) * p.batch * 16 + 1;
+        if (w_end * 4 > ws_bytes) return over("slice sums written (bytes)", w_end * 4, ws_bytes);
+        if (r_end * 4 > ws_bytes) return over("slice sums read (bytes)", r_end * 4, ws_bytes);
+    }
+    return std::string();
+}
+
 bool q8_mfma_supported(const Q8GemvProblem& p)
 {
     if (p.batch < 3 || p.batch > 8 || p.n_in % 256 || p.n_in > 8192) return false;
@@ -413,6 +465,8 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
     const int nbw = slice_blocks(p.n_in, rows);
     t.ksplit = (int)(t.nb / nbw);
     if (t.ksplit > kMaxSlices) return hipErrorNotSupported;
+    const int64_t ws_bytes = q8_mfma_workspace_bytes(p.mode, p.n_in, rows, p.batch);
+    if (!q8_mfma_plan_check(p, ws_bytes).empty()) return hipErrorInvalidConfiguration;
     if (t.ksplit > 1) {
         if (!workspace) return hipErrorInvalidValue;
         t.part = static_cast<float*>(workspace);

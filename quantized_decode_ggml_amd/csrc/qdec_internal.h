@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <string>
 
 namespace qdec {
 
@@ -222,6 +223,10 @@ hipError_t launch_rmsnorm(const float* x, int64_t n, int64_t batch, const float*
 // used in stream order.  Flat rows: the sum of the QKV segments, else the
 // rows of the first matrix.
 int64_t q8_mfma_workspace_bytes(int mode, int64_t n_in, int64_t rows, int64_t batch);
+// Host-side extent check of the plan launch_q8_0_gemv_mfma would run with a
+// workspace of ws_bytes: "" when every access stays inside its buffer, else
+// a description of the overrun (the launcher refuses such a plan).
+std::string q8_mfma_plan_check(const Q8GemvProblem& p, int64_t ws_bytes);
 bool q8_mfma_supported(const Q8GemvProblem& p);
 hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, void* workspace,
                                  hipStream_t s);
@@ -253,6 +258,11 @@ hipError_t launch_q8_0_gemm(Q8View w, int64_t n_in, int64_t n_out, int64_t batch
 // f32_gemm_workspace_bytes(..., false) when there is one, as above.  Both
 // contract bf16(W) with bf16(x) in f32.
 int64_t f32_gemm_workspace_bytes(int64_t n_in, int64_t n_out, int64_t batch, bool bf16_copy);
+// Host-side extent checks of the batched-GEMM plans (DMA-fed kernel for Q8_0
+// weights or a bf16 copy, register-staged kernel otherwise) with a workspace
+// of ws_bytes (0: none); "" when every access stays inside its buffer.
+std::string q8_gemm_plan_check(int64_t n_in, int64_t n_out, int64_t batch, int64_t ws_bytes);
+std::string f32_gemm_plan_check(int64_t n_in, int64_t n_out, int64_t batch, bool bf16_copy, int64_t ws_bytes);
 hipError_t launch_f32_gemm(const float* w, const void* wbf16, int64_t n_in, int64_t n_out, int64_t batch,
                            const float* x, float* out, void* workspace, hipStream_t s);
 // dst[i] = bf16(src[i]) (round to nearest even), count % 4 == 0: the bf16 copy

@@ -101,3 +101,23 @@ def test_noalloc_scratch_covers_the_vocabulary(n_in, batch, k, fits):
     assert rc != qd.QDEC_OK          # no GPU here: a call that fits fails later, at the device
     assert ("static array" in qd.last_error()) == (not fits), qd.last_error()
     assert qd.launch_count() == before
+
+
+WIDTHS = [32, 64, 96, 256, 512, 768, 1024, 1280, 2048, 2560, 3072, 4096, 6144, 7936, 8192, 8224, 16384]
+ROWS = [1, 2, 15, 16, 17, 48, 77, 128, 130, 1000, 3072, 5120, 8192, 28672, 50000, 128256]
+BATCHES = [1, 2, 3, 4, 5, 6, 7, 8, 9, 100, 128, 129, 512, 513]
+
+
+def test_every_launch_plan_stays_in_its_buffers():
+    """The host-side extent checks (the launchers run them before every
+    launch) over a sweep of widths, rows and batches: every plan the library
+    would choose keeps each kernel's last access inside its buffers, with the
+    workspace each call would be given.  No device needed."""
+    before = qd.launch_count()
+    for n_in in WIDTHS:
+        for n_out in ROWS:
+            for batch in BATCHES:
+                rc = qd.lib.qdec_check_plans(n_in, n_out, batch)
+                assert rc == qd.QDEC_OK, (n_in, n_out, batch, qd.last_error())
+    assert qd.lib.qdec_check_plans(33, 16, 1) == qd.QDEC_EINVAL
+    assert qd.launch_count() == before
