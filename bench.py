@@ -362,6 +362,23 @@ def suite(args):
         timed(f"c2 q8_0_gemv_residual down 3072x8192 b{b}",
               [lambda w=w: qd.q8_0_gemv_residual(w, 8192, 3072, m2, r2, out=o2) for w in wdn],
               q8_bytes(3072, 8192) + b * 8192 * 4 + b * 3072 * 8)
+        # the whole FFN block as one chain: one upload of x from pinned host
+        # memory, SwiGLU, down with x as the residual, one readback (the
+        # block-level call of the pages); PCIe-inclusive, bytes = weights + x + out
+        hx = torch.from_numpy(synth.normal_f32(synth.seed(2, 5) + b, (b, 3072))).pin_memory()
+        ho = torch.empty((b, 3072), pin_memory=True)
+        xb, mb, ob = torch.empty((b, 3072), device=dev), torch.empty((b, 8192), device=dev), \
+            torch.empty((b, 3072), device=dev)
+
+        def ffn_chain(i, xb=xb, mb=mb, ob=ob, hx=hx, ho=ho):
+            xb.copy_(hx, non_blocking=True)
+            qd.q8_0_swiglu(wg[i % Lg], wu2[i % Lg], 3072, 8192, xb, out=mb)
+            qd.q8_0_gemv_residual(wdn[i % len(wdn)], 8192, 3072, mb, xb, out=ob)
+            ho.copy_(ob, non_blocking=True)
+
+        timed(f"c2 FFN block b{b}: x upload, SwiGLU, down+residual, readback (4 steps)",
+              [lambda i=i: ffn_chain(i) for i in range(max(Lg, len(wdn)))],
+              2 * q8_bytes(8192, 3072) + q8_bytes(3072, 8192) + b * 3072 * 8)
     del wg, wu2
     # chained pre-norm block at batch 1 (next-row f2): RMSNorm+QKV, O-proj+residual,
     # RMSNorm+SwiGLU, down+residual; 4 launches per block, blocks rotate
