@@ -114,6 +114,8 @@ __device__ inline void block_reduce_n(float (&v)[NG], float* red, bool is_max)
 // `group` (any size up to kMaxGroup), with a branch per head and step (at 24
 // query / 8 kv heads that form measured 18.6 us at 1024 positions, bound by
 // the serialised LDS round trips of its four waves).
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D, bool FINAL, int G, int CH>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_cache,
                                                          const float* __restrict__ v_cache, int64_t n_kv, int group_rt,
@@ -123,13 +125,22 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
     constexpr int TPP = 256 / CH, SEG = D / TPP;   // threads per position, d columns per thread (scores)
     constexpr int CPL = D / 64;                    // columns per lane in the weighted sum
     constexpr int GM = G > 0 ? G : kMaxGroup;     // unrolled head loops
+    constexpr int CPR = D / 4;                     // 16-byte chunks per K row
+    constexpr int RPI = 64 / CPR;                  // K rows per wave DMA instruction
+    constexpr int QD = CH / (4 * RPI);             // K DMA instructions per wave
+    constexpr int OWF = 4 * kMaxGroup * D;                   // the wave partials (floats)
+    constexpr int KL = CH * D > OWF + kMaxGroup * CH ? CH * D : OWF + kMaxGroup * CH;
     const int group = G > 0 ? G : group_rt;
     __shared__ __attribute__((aligned(16))) float qs[kMaxGroup * D];
-    __shared__ float ps[kMaxGroup][CH];
     __shared__ float red[4];
     __shared__ float redn[4 * kMaxGroup];
     __shared__ float mx[kMaxGroup], sm[kMaxGroup];
-    __shared__ float ow[4][kMaxGroup][D];
+    // the chunk's K rows (scores), then the weights p and the four waves'
+    // partial outputs (written only after every K read: the softmax barriers
+    // lie between)
+    __shared__ __attribute__((aligned(1024))) float kl[KL];
+    auto ow = reinterpret_cast<float (*)[kMaxGroup][D]>(kl);
+    auto ps = reinterpret_cast<float (*)[CH]>(kl + OWF);
     const int64_t chunk = blockIdx.x, kv = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t nchunks = gridDim.x;
@@ -142,7 +153,24 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
     const int64_t tbase = chunk * CH;
     const int tn = (int)(n_ctx - tbase < CH ? n_ctx - tbase : CH);
     // every load of the workgroup is issued before any arithmetic waits on one:
-    // this wave's V rows (used after the softmax), then the thread's K segment
+    // the chunk's K rows into LDS, whole rows per instruction (rows past n_ctx
+    // repeat the last; lane l of an instruction lands at 16-byte slot l % CPR
+    // of its row and carries the row's chunk (l % CPR) ^ (row % CPR), so that
+    // the per-position reads below hit every bank once), then this wave's V
+    // rows (used after the softmax)
+    {
+        const float* kbase = k_cache + kv * max_seq * D;
+#pragma unroll
+        for (int qi = 0; qi < QD; ++qi) {
+            const int row = (wave * QD + qi) * RPI + lane / CPR;
+            int64_t tk = tbase + row;
+            tk = tk < n_ctx ? tk : n_ctx - 1;
+            const int c = (lane % CPR) ^ (row % CPR);
+            __builtin_amdgcn_global_load_lds(kbase + tk * D + c * 4, (lds_void*)(kl + (wave * QD + qi) * 256), 16, 0,
+                                             0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     constexpr int VPW = CH / 4;                   // positions per wave in the weighted sum
     const float* vbase = v_cache + (kv * max_seq + tbase) * D + CPL * lane;
     float vr[VPW][CPL];
@@ -158,12 +186,18 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
             vr[i][0] = vbase[(int64_t)ts * D];
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's K rows have landed once at most its V loads remain; the
+    // barrier makes every wave's rows visible
+    static_assert(VPW < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VPW & 15) | ((VPW >> 4) << 14) | 0x70 | 0xF00);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     float4 kr[SEG / 4];
-    {
-        const int64_t tk = valid ? t : n_ctx - 1;
-        const float4* krow = reinterpret_cast<const float4*>(k_cache + (kv * max_seq + tk) * D + seg * SEG);
 #pragma unroll
-        for (int j4 = 0; j4 < SEG / 4; ++j4) kr[j4] = krow[j4];
+    for (int j4 = 0; j4 < SEG / 4; ++j4) {
+        const int c = seg * (SEG / 4) + j4;
+        kr[j4] = *reinterpret_cast<const float4*>(kl + pl * D + (c ^ (pl % CPR)) * 4);
     }
     float s[GM];
 #pragma unroll
