@@ -123,7 +123,6 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
                                                          float* __restrict__ part, float* __restrict__ out)
 {
     constexpr int TPP = 256 / CH, SEG = D / TPP;   // threads per position, d columns per thread (scores)
-    constexpr int CPL = D / 64;                    // columns per lane in the weighted sum
     constexpr int GM = G > 0 ? G : kMaxGroup;     // unrolled head loops
     constexpr int CPR = D / 4;                     // 16-byte chunks per K row
     constexpr int RPI = 64 / CPR;                  // K rows per wave DMA instruction
@@ -171,26 +170,26 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+    // V: wave w takes positions w + 4k; each load covers RPV of them, whole
+    // rows, 16 bytes (4 columns) a lane
     constexpr int VPW = CH / 4;                   // positions per wave in the weighted sum
-    const float* vbase = v_cache + (kv * max_seq + tbase) * D + CPL * lane;
-    float vr[VPW][CPL];
+    constexpr int LPR = D / 4;                    // lanes per V row
+    constexpr int RPV = 64 / LPR;                 // V rows per load
+    constexpr int VI = VPW / RPV;                 // V loads per lane
+    const int vrow = lane / LPR, vcol = 4 * (lane % LPR);
+    const float* vbase = v_cache + (kv * max_seq + tbase) * D + vcol;
+    float4 vr[VI];
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-        const int tt = wave + 4 * i;
+    for (int i = 0; i < VI; ++i) {
+        const int tt = wave + 4 * (RPV * i + vrow);
         const int ts = tt < tn ? tt : tn - 1;     // in bounds; weight 0 past tn
-        if constexpr (CPL == 2) {
-            const float2 v2 = *reinterpret_cast<const float2*>(vbase + (int64_t)ts * D);
-            vr[i][0] = v2.x;
-            vr[i][1] = v2.y;
-        } else {
-            vr[i][0] = vbase[(int64_t)ts * D];
-        }
+        vr[i] = *reinterpret_cast<const float4*>(vbase + (int64_t)ts * D);
     }
     __builtin_amdgcn_sched_barrier(0);
     // this wave's K rows have landed once at most its V loads remain; the
     // barrier makes every wave's rows visible
-    static_assert(VPW < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((VPW & 15) | ((VPW >> 4) << 14) | 0x70 | 0xF00);
+    static_assert(VI < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VI & 15) | ((VI >> 4) << 14) | 0x70 | 0xF00);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     float4 kr[SEG / 4];
@@ -263,28 +262,39 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
 
     // weighted sum of V over this wave's positions (rows already in registers;
     // positions past tn have weight 0)
-    float o[GM][CPL];
+    float o[GM][4];
 #pragma unroll
     for (int g = 0; g < GM; ++g)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) o[g][c] = 0.0f;
+        for (int c = 0; c < 4; ++c) o[g][c] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-        const int tt = wave + 4 * i;
+    for (int i = 0; i < VI; ++i) {
+        const int tt = wave + 4 * (RPV * i + vrow);
+        const float vv[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
 #pragma unroll
         for (int g = 0; g < GM; ++g) {
             if (G > 0 || g < group) {
                 const float p = tt < tn ? ps[g][tt] : 0.0f;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) o[g][c] = __builtin_fmaf(p, vr[i][c], o[g][c]);
+                for (int c = 0; c < 4; ++c) o[g][c] = __builtin_fmaf(p, vv[c], o[g][c]);
             }
         }
     }
+    // the RPV lane groups of the wave hold the same columns: add them
 #pragma unroll
     for (int g = 0; g < GM; ++g)
         if (G > 0 || g < group)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) ow[wave][g][CPL * lane + c] = o[g][c];
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int off = LPR; off < 64; off <<= 1) o[g][c] += __shfl_xor(o[g][c], off);
+    if (lane < LPR) {
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+            if (G > 0 || g < group)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ow[wave][g][vcol + c] = o[g][c];
+    }
     __syncthreads();
     for (int u = tid; u < group * D; u += 256) {
         const int g = u / D, j = u % D;
