@@ -45,13 +45,14 @@
  *     Inside HIP stream capture no copy can be made or waited for
  *     (QDEC_EINVAL): call qdec_prepare, which returns once the copy is
  *     complete, for every weight before capturing.
- *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in of
- *     1024..8192 in the supported steps) splits x, q8_0_gemv_topk keeps its
- *     candidate lists, and q8_0_gemm_batched (on its DMA-fed path:
- *     n_in % 64 == 0 and even n_out, K split over up to 8 slices when the
- *     output has few 128 x 128 tiles) rounds x to bf16 and keeps the slices'
- *     partial products (as do both batched GEMMs on their other K-split
- *     shapes), in a library-owned device buffer, one per
+ *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in a
+ *     multiple of 256 up to 8192) keeps the sums of its K slices where it
+ *     splits K over workgroups, q8_0_gemv_topk keeps its candidate lists,
+ *     attention keeps its chunk partials, and the batched GEMMs on their
+ *     DMA-fed path (n_in % 64 == 0, and even n_out for Q8_0; K split over up
+ *     to 8 slices when the output has few 128 x 128 tiles) round x to bf16
+ *     and keep the slices' partial products (as do both batched GEMMs on
+ *     their other K-split shapes), in a library-owned device buffer, one per
  *     (device, stream), made (or grown) on the first such call on that stream
  *     and freed by qdec_clear_cache.  Calls on one stream share it in
  *     stream order; calls on different streams never share one.  When a
@@ -106,8 +107,9 @@ typedef enum { QDEC_TYPE_F32 = 0, QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12, QDEC_
  * out[b][i] = sum_j deq(W)[i][j] * x[b][j] for 1 <= batch <= 8.
  * n_in % 32 == 0, n_in, n_out >= 1.  f32 accumulation.  Reproducibility: the
  * same inputs give the same bits on every call on a given path (with 3..8
- * batch rows and fewer than 8192 output rows K is split over workgroups,
- * whose sums a further small launch adds in a fixed order). */
+ * batch rows K is split over workgroups unless the grid is large enough
+ * without it, and a further small launch adds the slices' sums in a fixed
+ * order). */
 QDEC_API int q8_0_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
               const float* x, float* out, hipStream_t stream);
 

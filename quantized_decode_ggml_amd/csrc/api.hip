@@ -175,8 +175,10 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
 }
 
 // ------------------------------------------------------------ workspaces --
-// Scratch for the split activations of the matrix-core GEMV, one buffer per
-// (device, stream): calls on one stream are ordered, so they can share it;
+// Workspace (the 3..8-row GEMV's K-slice sums, top-k candidate lists,
+// attention chunk partials, the batched GEMMs' bf16 x and slice partials),
+// one buffer per (device, stream): calls on one stream are ordered, so they
+// can share it;
 // calls on different streams never do.  A buffer grows on demand outside
 // stream capture; a capturing stream whose buffer is missing or too small gets
 // none, and the caller then takes the VALU kernels.  A buffer that a larger

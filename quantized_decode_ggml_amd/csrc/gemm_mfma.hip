@@ -16,7 +16,7 @@
 // product is at most about 2*2^-9 relative.
 //
 // Two kernels:
-//  - gemm_q8_dma (Q8_0 weights, K % 64 == 0, even N, with a workspace): every
+//  - gemm_dma (Q8_0 weights, K % 64 == 0, even N, with a workspace): every
 //    operand streamed into LDS by DMA, eight waves per workgroup, B fragments
 //    dequantised in registers (described at the kernel).  With few output
 //    tiles K is split into slices whose partial products a small kernel sums
