@@ -85,6 +85,24 @@ def test_attention(qd, n_ctx, d, n_head, n_kv):
     assert (err <= tol).all(), f"worst err/tol {np.max(err / tol):.3g}"
 
 
+@pytest.mark.parametrize("n_ctx,d,n_head,n_kv", [(3000, 128, 32, 4), (2049, 64, 12, 2), (130, 64, 12, 2)])
+def test_attention_group_sizes(qd, n_ctx, d, n_head, n_kv):
+    """The specialised kernels for 8 and 6 query heads a kv head, on ragged
+    contexts either side of the 64/128-position chunk switch, with the cache
+    longer than the context."""
+    rng = np.random.default_rng(9900 + n_ctx + d + n_head)
+    max_seq = n_ctx + 77
+    kc = rng.standard_normal((n_kv, max_seq, d)).astype(np.float32)
+    vc = rng.standard_normal((n_kv, max_seq, d)).astype(np.float32)
+    q = (2.0 * rng.standard_normal((n_head, d))).astype(np.float32)
+    scale = 1.0 / np.sqrt(d)
+    got = host(qd.attention_decode(dev(q), dev(kc), dev(vc), n_ctx, scale))
+    ref, a_abs = oracle.attention(q, kc, vc, n_ctx, scale)
+    tol = attention_tol(q, kc, n_ctx, scale, n_head // n_kv, a_abs)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert (err <= tol).all(), f"worst err/tol {np.max(err / tol):.3g}"
+
+
 def test_attention_peaked_and_flat(qd):
     """One position far above the rest (weights ~ one-hot), and q = 0 (flat
     weights: the mean of V over n_ctx)."""
