@@ -86,6 +86,7 @@ int64_t copy_bytes(int type, int64_t n_in, int64_t n_out)
          : type == QDEC_TYPE_Q8_0 ? q8_plane_bytes(n_in, n_out)
          : type == kTypeQ8_0Tiled ? q8t_plane_bytes(n_in, n_out)
          : type == kTypeQ4KTiled ? q4kt_plane_bytes(n_in, n_out)
+         : type == kTypeQ6KTiled ? q6kt_plane_bytes(n_in, n_out)
          : type == QDEC_TYPE_Q6_K ? q6k_plane_bytes(n_in, n_out)
                                   : q4k_plane_bytes(n_in, n_out);
 }
@@ -97,6 +98,7 @@ hipError_t launch_copy_of(int type, const void* w, int64_t n_in, int64_t n_out, 
          : type == QDEC_TYPE_Q8_0 ? launch_repack_q8_0(raw, n_in, n_out, dst, s)
          : type == kTypeQ8_0Tiled ? launch_repack_q8_0_tiled(raw, n_in, n_out, dst, s)
          : type == kTypeQ4KTiled ? launch_repack_q4k_tiled(raw, n_in, n_out, dst, s)
+         : type == kTypeQ6KTiled ? launch_repack_q6k_tiled(raw, n_in, n_out, dst, s)
          : type == QDEC_TYPE_Q6_K ? launch_repack_q6k(raw, n_in, n_out, dst, s)
                                   : launch_repack_q4k(raw, n_in, n_out, dst, s);
 }
@@ -686,6 +688,12 @@ int q6k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const fl
     QDEC_TRY(check_ptr(fn, "out", out, 4));
     if (overlaps(out, batch * n_out * 4, x, batch * n_in * 4)) return fail(QDEC_EINVAL, "%s: out overlaps x", fn);
     const void* buf = nullptr;
+    if (q6k_mfma_supported(n_in, batch)) {
+        // one row on the matrix cores, from the fragment-tiled copy; inside a
+        // capture that copy may be missing, and the VALU kernel then runs
+        QDEC_TRY(repacked(w, kTypeQ6KTiled, n_in, n_out, stream, &buf, false, true));
+        if (buf) return finish(launch_q6k_gemv_mfma(q6kt_view(buf, n_in, n_out), n_in, n_out, x, out, stream), fn);
+    }
     QDEC_TRY(repacked(w, QDEC_TYPE_Q6_K, n_in, n_out, stream, &buf));
     return finish(launch_q6k_gemv(q6k_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
 }
@@ -745,11 +753,13 @@ int qdec_prepare(const void* w, int type, int64_t n_in, int64_t n_out, hipStream
     const void* buf = nullptr;
     QDEC_TRY(repacked(w, type, n_in, n_out, stream, &buf, true));
     // Q8_0 weights also get the fragment-tiled copy of the batched matrix-core
-    // GEMV, Q4_K weights that of the one-row matrix-core GEMV, so that graphs
-    // captured later can use them
+    // GEMV, Q4_K and Q6_K weights that of their one-row matrix-core GEMVs, so
+    // that graphs captured later can use them
     if (type == QDEC_TYPE_Q8_0) QDEC_TRY(repacked(w, kTypeQ8_0Tiled, n_in, n_out, stream, &buf, true));
     if (type == QDEC_TYPE_Q4_K && q4k_mfma_supported(n_in, 1))
         QDEC_TRY(repacked(w, kTypeQ4KTiled, n_in, n_out, stream, &buf, true));
+    if (type == QDEC_TYPE_Q6_K && q6k_mfma_supported(n_in, 1))
+        QDEC_TRY(repacked(w, kTypeQ6KTiled, n_in, n_out, stream, &buf, true));
     return QDEC_OK;
 }
 
@@ -783,6 +793,11 @@ int qdec_check_plans(int64_t n_in, int64_t n_out, int64_t batch)
             const std::string why = q8_mfma_plan_check(p, q8_mfma_workspace_bytes(mode, n_in, flat, batch));
             if (!why.empty()) return bad(why);
         }
+    }
+    // the one-row Q6_K matrix-core GEMV (widths that are multiples of 256)
+    if (n_in % 256 == 0 && q6k_mfma_supported(n_in, 1)) {
+        const std::string why = q6k_mfma_plan_check(n_in, n_out);
+        if (!why.empty()) return bad(why);
     }
     // the batched GEMMs, with and without a workspace (a capture on a stream
     // that has none), dense f32 with and without its bf16 copy
@@ -847,11 +862,12 @@ void qdec_clear_cache(void)
 
 int64_t qdec_cache_len(void)
 {
-    // one per (weight, public type, shape): the tiled copies Q8_0 and Q4_K
-    // weights also get for the matrix-core GEMVs are not counted separately
+    // one per (weight, public type, shape): the tiled copies Q8_0, Q4_K and
+    // Q6_K weights also get for the matrix-core GEMVs are not counted separately
     std::lock_guard<std::mutex> lock(g_mu);
     int64_t n = 0;
-    for (const auto& kv : g_cache) n += kv.first.type != kTypeQ8_0Tiled && kv.first.type != kTypeQ4KTiled;
+    for (const auto& kv : g_cache)
+        n += kv.first.type != kTypeQ8_0Tiled && kv.first.type != kTypeQ4KTiled && kv.first.type != kTypeQ6KTiled;
     return n;
 }
 

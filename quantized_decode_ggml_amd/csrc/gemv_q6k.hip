@@ -23,7 +23,13 @@
 // j + 64, ...; one batch row gives each wave one chunk column (n_in / 1024
 // waves per row group, one group per workgroup, 4 rows per wave); other
 // batches and widths use a bounds-checked loop over row groups of LPR lanes.
+// One batch row at widths 1024, 2048, 3072, 4096, 6144 and 8192 runs instead
+// on the integer matrix cores from a second, fragment-tiled copy (see the
+// matrix-core section below): x as a fixed-point number per scale group, the
+// weights as int8 4(q - 32), about a third of the VALU work per weight.
 #include "qdec_internal.h"
+
+#include <algorithm>
 
 namespace qdec {
 
@@ -277,6 +283,277 @@ __global__ __launch_bounds__(256) void dequant_q6k_kernel(Q6KView w, int64_t nch
     }
 }
 
+// Tiled repack (the matrix-core GEMV's copy): one thread per 12-byte cell,
+// i.e. per (row group G, chunk c, lane l): row 16G + l%16, scale group
+// 4(c%4) + l/16 of super-block c/4.  Threads of the first chunk of a
+// super-block also write their scale word, and lanes 0..15 of them the d
+// halfword.  Rows past n_out are written as zeros.
+__global__ __launch_bounds__(256) void repack_q6k_tiled_kernel(const uint8_t* __restrict__ raw, int64_t n_out,
+                                                               int64_t nsb, int64_t ncells,
+                                                               uint32_t* __restrict__ qt,
+                                                               uint32_t* __restrict__ sct,
+                                                               uint16_t* __restrict__ dt)
+{
+    const int64_t cell = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (cell >= ncells) return;
+    const int l = (int)(cell & 63);
+    const int64_t tile = cell >> 6;            // G * nch + c
+    const int64_t nch = nsb * 4;
+    const int64_t G = tile / nch;
+    const int64_t c = tile % nch;
+    const int64_t sb = c >> 2;
+    const int cs = (int)(c & 3), g = l >> 4;
+    const int64_t row = G * 16 + (l & 15);
+    uint32_t n0 = 0, n1 = 0, hw = 0, scw = 0;
+    uint16_t d = 0;
+    if (row < n_out) {
+        const uint8_t* blk = raw + (row * nsb + sb) * 210;
+        // weight p = 64 cs + 16 g + b of the super-block: half h = p / 128,
+        // quarter j = (p % 128) / 32, position p % 32 = 16 (g % 2) + b
+        const int h = cs >> 1, j = 2 * (cs & 1) + (g >> 1);
+        const uint8_t* ql = blk + 64 * h + 32 * (j & 1) + 16 * (g & 1);
+        const uint8_t* qh = blk + 128 + 32 * h + 16 * (g & 1);
+        for (int b = 0; b < 16; ++b) {
+            const uint32_t nib = (j < 2 ? ql[b] : (uint32_t)(ql[b] >> 4)) & 15u;
+            const uint32_t hi = ((uint32_t)(qh[b] >> (2 * j)) & 3u) ^ 2u;
+            const int i = b & 3, t = b >> 2;
+            if (t < 2) n0 |= nib << (8 * i + 4 * t);
+            else n1 |= nib << (8 * i + 4 * (t - 2));
+            hw |= hi << (8 * i + 2 * t);
+        }
+        if (cs == 0) {
+            const uint8_t* sc = blk + 192;
+            for (int k = 0; k < 4; ++k) scw |= (uint32_t)sc[4 * k + g] << (8 * k);
+            d = (uint16_t)(blk[208] | (blk[209] << 8));
+        }
+    }
+    qt[cell * 3 + 0] = n0;
+    qt[cell * 3 + 1] = n1;
+    qt[cell * 3 + 2] = hw;
+    if (cs == 0) {
+        const int64_t st = G * nsb + sb;
+        sct[st * 64 + l] = scw;
+        if (l < 16) dt[st * 16 + l] = d;
+    }
+}
+
+// ------------------------------------------------------ matrix cores --
+// One batch row on the integer matrix cores, from the tiled copy.  A 768-byte
+// tile is 16 rows x one 64-weight chunk (four 16-weight scale groups) and one
+// K = 64 step of v_mfma_i32_16x16x64_i8.  Lane l (row n = l % 16, k-group
+// g = l / 16) holds scale group g of row n: its 16 B operand bytes are that
+// group's weights, each rebuilt as the int8 value 4(q - 32) -- the nibble
+// shifted up two bits, the high bit pair (stored with its top bit flipped)
+// above it -- by three or four operations per four bytes.
+// x is a fixed-point number per scale group s of 16 values:
+// X_k = trunc(x_k * 2^(30 - e_s)), |x_k| < 2^e_s over the group, so |X_k| <
+// 2^30 and x_k = X_k 2^(e_s - 30) + eps_k, |eps_k| < 2^(e_s - 30).  X_k has
+// the signed base-256 digits a_0..a_3 (a_3 within -64..64).  The A operand's
+// row 4s + j holds digit j of group s on k-group s and zeros on the other
+// three, so the product's row 4s + j, column n, is D_j = sum_k 4(q_k - 32)
+// a_j,k over group s of row n: lane l receives in D[0..3] the four digit sums
+// of group l / 16 of row l % 16 (the group its own B bytes held), forms
+// u = (256 D3 + D2) 2^16 + (256 D1 + D0) and accumulates
+//     (d sc) * 2^(e_s - 32) * u,
+// d sc exact (11 x 8 significant bits), the power of two exact (the 2 of
+// e_s - 32 takes out the factor 4).  Both brackets are multiples of 4; they
+// convert exactly while below 2^26 in magnitude, which only an extreme group
+// (nearly every quant 0 with digits at the end of their range) can exceed;
+// the fma rounds once.  In LDS the A operand is kept as its non-zero part:
+// per chunk 16 cells of 16 bytes (group s, digit j), then one zero cell that
+// the lanes off the diagonal read.
+// A workgroup is RG 16-row groups, each with K split over KS waves of T
+// chunks (T % 4 == 0: a wave starts on a super-block).  Each thread loads its
+// quads of x and waits for them, then issues every weight load of its wave
+// (T tiles; per super-block the scale words and d); while those are in
+// flight the workgroup writes the A cells and per scale group e_s - 32.
+// Error per output, beyond the f32 rounding of the VALU kernel: at most
+// 2^(e_s - 30) <= 2^-29 max_s |x| per x value, times |d sc (q_k - 32)|.
+template <int KS, int T, int RG>
+__global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma(Q6KTView w, const float* __restrict__ x,
+                                                              int64_t n_in, int64_t n_out, float* __restrict__ out)
+{
+    static_assert(T % 4 == 0 && T >= 4 && T <= 16 && KS * RG <= 16, "T chunks per wave, KS * RG waves");
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const uint16_t global_u16;
+    constexpr int n = 64 * T * KS;     // n_in
+    constexpr int NCH = n / 64;
+    constexpr int NW = KS * RG;
+    constexpr int NT = 64 * NW;        // threads
+    constexpr int NQ = n / 4;          // quads of x
+    constexpr int QK = (NQ + NT - 1) / NT;
+    constexpr int CB = 272;            // LDS bytes a chunk: 16 A cells, one zero cell
+    static_assert(QK <= 4, "quads per thread");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[CB * NCH];
+    __shared__ __attribute__((aligned(16))) int xe[4][NCH];   // e_s - 32 of group s of chunk c
+    __shared__ int wbad[NW];
+    __shared__ float red[RG][KS][16];
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wv / KS, kw = wv % KS;
+    const int64_t groups = q6kt_groups(n_out);
+    const int64_t Gw = (int64_t)blockIdx.x * RG + rg;          // this wave's row group
+    const int64_t G = Gw < groups ? Gw : groups - 1;           // a spare wave reads the last one
+    const int64_t nsb = n_in >> 8;
+    const int c0 = kw * T;   // first chunk of this wave, a multiple of 4
+
+    // quads i = tid + k NT of x, live for whole waves (NQ % 64 == 0)
+    float4 xv[QK];
+#pragma unroll
+    for (int k = 0; k < QK; ++k)
+        xv[k] = 64 * wv + k * NT < NQ ? reinterpret_cast<const float4*>(x)[tid + k * NT]
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    // x first: every workgroup reads it, and behind the weight requests of
+    // the whole grid it would land late
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    // every weight load of this wave: T cells of 12 bytes, per super-block
+    // the scale word and d of the lane's row
+    Bits12 qv[T];
+    uint32_t scv[T / 4];
+    uint16_t dv[T / 4];
+    {
+        const int64_t cell0 = (G * NCH + c0) * 64 + lane;
+        const uint8_t* qb = w.q + cell0 * 12;
+        const global_u32* st = (const global_u32*)w.sc + (G * nsb + c0 / 4) * 64 + lane;
+        const global_u16* dt = (const global_u16*)w.d + (G * nsb + c0 / 4) * 16 + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            qv[t] = load12(qb, (int64_t)t * 768);
+            if (t % 4 == 0) {
+                scv[t / 4] = __builtin_nontemporal_load(st + (t / 4) * 64);
+                dv[t / 4] = __builtin_nontemporal_load(dt + (t / 4) * 16);
+            }
+        }
+    }
+    asm volatile("" ::: "memory");
+    // A cells and group exponents: quad i holds values 4i .. 4i + 3 of chunk
+    // c = i / 16, scale group s = (i / 4) % 4, at bytes 4 (i % 4) of its cells
+    int bad = 0;
+#pragma unroll
+    for (int k = 0; k < QK; ++k) {
+        if (64 * wv + k * NT >= NQ) break;
+        const int i = tid + k * NT;
+        const float v[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+        uint32_t amax = max(max(__builtin_bit_cast(uint32_t, v[0]) & 0x7fffffffu,
+                                __builtin_bit_cast(uint32_t, v[1]) & 0x7fffffffu),
+                            max(__builtin_bit_cast(uint32_t, v[2]) & 0x7fffffffu,
+                                __builtin_bit_cast(uint32_t, v[3]) & 0x7fffffffu));
+        // over the group's 4 quads (4 consecutive lanes): lane ^ 1, lane ^ 2
+        amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
+        amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
+        bad |= amax >= 0x7f800000u;
+        // amax = m 2^e with 0.5 <= m < 1, so every |x| < 2^e (e = 0 for zeros)
+        const int e_s = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
+        // X = trunc(x 2^(30 - e)), |X| < 2^30; its signed base-256 digits are
+        // the bytes of X + 0x80808080, each less 0x80
+        uint32_t y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = (uint32_t)(int)__builtin_amdgcn_ldexpf(v[e], 30 - e_s) + 0x80808080u;
+        // word j = digit j of the 4 values
+        uint32_t wd[4];
+        {
+            const uint32_t t01l = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
+            const uint32_t t01h = __builtin_amdgcn_perm(y[1], y[0], 0x07030602u);
+            const uint32_t t23l = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
+            const uint32_t t23h = __builtin_amdgcn_perm(y[3], y[2], 0x07030602u);
+            wd[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u) ^ 0x80808080u;
+            wd[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u) ^ 0x80808080u;
+            wd[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u) ^ 0x80808080u;
+            wd[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u) ^ 0x80808080u;
+        }
+        const int c = i >> 4, s = (i >> 2) & 3, qq = i & 3;
+        uint8_t* cell = lds + CB * c + 64 * s + 4 * qq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(cell + 16 * j) = wd[j];
+        if (qq == 0) xe[s][c] = e_s - 32;
+        if ((i & 15) == 0) *reinterpret_cast<uint4*>(lds + CB * c + 256) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // a non-finite x makes every output NaN
+    const uint64_t badm = __builtin_amdgcn_ballot_w64(bad != 0);
+    if (lane == 0) wbad[wv] = badm != 0;
+    __syncthreads();
+    const bool any_bad = __builtin_amdgcn_ballot_w64(lane < NW && wbad[lane < NW ? lane : 0] != 0) != 0;
+
+    // A operand of lane (row m = lane % 16, k-group g = lane / 16): cell m of
+    // the chunk on the diagonal (m / 4 == g), the zero cell elsewhere; the D
+    // side and the B bytes of the lane are group g of row lane % 16
+    const int m = lane & 15, g = lane >> 4;
+    const int aoff = CB * c0 + ((m >> 2) == g ? 16 * m : 256);
+    int eb[T];
+#pragma unroll
+    for (int q = 0; q < T / 4; ++q) {
+        const int4 e4 = *reinterpret_cast<const int4*>(&xe[g][c0 + 4 * q]);
+        eb[4 * q] = e4.x;
+        eb[4 * q + 1] = e4.y;
+        eb[4 * q + 2] = e4.z;
+        eb[4 * q + 3] = e4.w;
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const i32x4 A = *reinterpret_cast<const i32x4*>(lds + aoff + CB * t);
+        const uint32_t n0 = qv[t].a, n1 = qv[t].b, hw = qv[t].c;
+        const i32x4 B = {(int)(((n0 << 2) & 0x3C3C3C3Cu) | ((hw << 6) & 0xC0C0C0C0u)),
+                         (int)(((n0 >> 2) & 0x3C3C3C3Cu) | ((hw << 4) & 0xC0C0C0C0u)),
+                         (int)(((n1 << 2) & 0x3C3C3C3Cu) | ((hw << 2) & 0xC0C0C0C0u)),
+                         (int)(((n1 >> 2) & 0x3C3C3C3Cu) | (hw & 0xC0C0C0C0u))};
+        const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+        const float u = __builtin_fmaf((float)(D[3] * 256 + D[2]), 65536.0f, (float)(D[1] * 256 + D[0]));
+        const float d = fp16_bits_to_f32(dv[t / 4]);
+        const float sc = (float)(int8_t)((scv[t / 4] >> (8 * (t % 4))) & 0xffu);
+        acc = __builtin_fmaf(d * sc, __builtin_amdgcn_ldexpf(u, eb[t]), acc);
+    }
+    // row r: its four groups in lanes r + 16 g, then the KS waves of its
+    // row group in order
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if constexpr (KS > 1) {
+        if (lane < 16) red[rg][kw][lane] = acc;
+        __syncthreads();
+        if (kw != 0) return;
+        if (lane < 16) {
+            float s2 = red[rg][0][lane];
+#pragma unroll
+            for (int k = 1; k < KS; ++k) s2 += red[rg][k][lane];
+            acc = s2;
+        }
+    }
+    if (any_bad) acc = __builtin_nanf("");
+    const int64_t row = Gw * 16 + lane;
+    if (lane < 16 && Gw < groups && row < n_out) out[row] = acc;
+}
+
+// K split: n_in = 64 KS T, T = 8, 12 or 16 chunks a wave: 1024 on 2 waves,
+// 2048 .. 4096 on 4, 6144 and 8192 on 8.
+bool q6k_mfma_shape(int64_t n_in, int* ks, int* t)
+{
+    switch (n_in) {
+        case 1024: *ks = 2; *t = 8; return true;
+        case 2048: *ks = 4; *t = 8; return true;
+        case 3072: *ks = 4; *t = 12; return true;
+        case 4096: *ks = 4; *t = 16; return true;
+        case 6144: *ks = 8; *t = 12; return true;
+        case 8192: *ks = 8; *t = 16; return true;
+        default: return false;
+    }
+}
+
+// Row groups a workgroup: two from 512 groups on (sharing the x operands),
+// within 16 waves a workgroup.
+int q6k_mfma_rg(int64_t groups, int ks) { return groups >= 512 && 2 * ks <= 16 ? 2 : 1; }
+
+using KernelFnT6 = void (*)(Q6KTView, const float*, int64_t, int64_t, float*);
+
+template <int KS, int T>
+KernelFnT6 q6k_mfma_pick(int rg)
+{
+    return rg == 2 ? q6k_gemv_mfma<KS, T, 2> : q6k_gemv_mfma<KS, T, 1>;
+}
+
 using KernelFn = void (*)(Q6KArgs);
 
 template <int R>
@@ -357,6 +634,65 @@ hipError_t launch_q6k_gemv(Q6KView w, int64_t n_in, int64_t n_out, int64_t batch
         threads = 256;
     }
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+    count_launch();
+    return hipGetLastError();
+}
+
+hipError_t launch_repack_q6k_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s)
+{
+    const Q6KTView v = q6kt_view(dst, n_in, n_out);
+    const int64_t nsb = n_in / 256, ncells = q6kt_groups(n_out) * (n_in / 64) * 64;
+    hipLaunchKernelGGL(repack_q6k_tiled_kernel, dim3(grid_for(ncells, 256)), dim3(256), 0, s, raw, n_out, nsb,
+                       ncells, reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(v.q)),
+                       const_cast<uint32_t*>(v.sc), const_cast<uint16_t*>(v.d));
+    count_launch();
+    return hipGetLastError();
+}
+
+bool q6k_mfma_supported(int64_t n_in, int64_t batch)
+{
+    int ks = 0, t = 0;
+    return batch == 1 && q6k_mfma_shape(n_in, &ks, &t);
+}
+
+std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out)
+{
+    int ks = 0, t = 0;
+    if (!q6k_mfma_shape(n_in, &ks, &t)) return "q6k matrix-core GEMV: unsupported width " + std::to_string(n_in);
+    if (64LL * ks * t != n_in) return "q6k matrix-core GEMV: K split does not cover the row";
+    const int64_t groups = q6kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
+    const int rg = q6k_mfma_rg(groups, ks);
+    const int64_t grid = (groups + rg - 1) / rg;
+    if (grid <= 0 || grid > 0x7fffffffLL) return "q6k matrix-core GEMV: grid out of range";
+    // the last wave reads row group min(grid rg - 1, groups - 1), chunks up to
+    // (ks - 1) t + t - 1 = nch - 1, super-blocks up to nsb - 1
+    const int64_t g_last = std::min<int64_t>(grid * rg - 1, groups - 1);
+    const int64_t q_end = ((g_last * nch + (int64_t)(ks - 1) * t + t - 1) * 64 + 63) * 12 + 12;
+    const int64_t sc_end = ((g_last * nsb + nsb - 1) * 64 + 63) * 4 + 4;
+    const int64_t d_end = ((g_last * nsb + nsb - 1) * 16 + 15) * 2 + 2;
+    const int64_t g = groups;
+    if (q_end > g * nch * 768 || sc_end > g * nsb * 256 || d_end > g * nsb * 32)
+        return "q6k matrix-core GEMV: a weight read runs past the tiled copy";
+    // x: quads tid + k NT below n / 4; out: rows below n_out (checked in the kernel)
+    const int64_t nt = 64LL * ks * rg, nq = n_in / 4;
+    if (nq % 64 != 0 || (nq + nt - 1) / nt > 4) return "q6k matrix-core GEMV: x quads do not fit the threads";
+    return "";
+}
+
+hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+                                hipStream_t s)
+{
+    int ks = 0, t = 0;
+    if (!q6k_mfma_shape(n_in, &ks, &t) || !q6k_mfma_plan_check(n_in, n_out).empty())
+        return hipErrorInvalidConfiguration;
+    const int64_t groups = q6kt_groups(n_out);
+    const int rg = q6k_mfma_rg(groups, ks);
+    KernelFnT6 fn = ks == 2 ? q6k_mfma_pick<2, 8>(rg)
+                  : ks == 4 ? (t == 8 ? q6k_mfma_pick<4, 8>(rg) : t == 12 ? q6k_mfma_pick<4, 12>(rg)
+                                                                          : q6k_mfma_pick<4, 16>(rg))
+                            : (t == 12 ? q6k_mfma_pick<8, 12>(rg) : q6k_mfma_pick<8, 16>(rg));
+    hipLaunchKernelGGL(fn, dim3((unsigned)((groups + rg - 1) / rg)), dim3(64 * ks * rg), 0, s, w, x, n_in, n_out,
+                       out);
     count_launch();
     return hipGetLastError();
 }

@@ -153,6 +153,46 @@ inline Q4KTView q4kt_view(const void* base, int64_t n_in, int64_t n_out)
                     reinterpret_cast<const uint32_t*>(p + off_dm)};
 }
 
+// Fragment-tiled Q6_K matrix (the one-row matrix-core GEMV's copy): rows in
+// groups of 16 (the last padded with zero rows), 64-weight chunks c (chunk c
+// = weights 64(c%4) .. +63 of super-block c/4: four 16-weight scale groups).
+// For group G:
+//   q  : 768-byte tile (G*nch + c), lane l's 12 bytes at 12l hold the 16
+//        weights w_b = 64(c%4) + 16(l/16) + b (b = 0..15) of row 16G + l%16
+//        as three words N0, N1, H: byte i of N0 is nib(w_i) | nib(w_4+i) << 4,
+//        of N1 nib(w_8+i) | nib(w_12+i) << 4, and byte i of H carries
+//        hi(w_4t+i) ^ 2 in bits 2t, 2t+1 (t = 0..3; nib and hi the low four
+//        and high two bits of the 6-bit quant);
+//   sc : 256-byte tile (G*nsb + sb), lane l's word at 4l: byte k is the
+//        scale of group 4k + l/16 of row 16G + l%16 (chunk 4sb + k);
+//   d  : 32-byte tile (G*nsb + sb), halfword r = d of row 16G + r (fp16 bits).
+// 210 bytes per 256 weights, as the GGML block.
+constexpr int kTypeQ6KTiled = 0x10E;
+
+struct Q6KTView {
+    const uint8_t* q;
+    const uint32_t* sc;
+    const uint16_t* d;
+};
+
+__host__ __device__ inline int64_t q6kt_groups(int64_t n_out) { return (n_out + 15) / 16; }
+
+inline int64_t q6kt_plane_bytes(int64_t n_in, int64_t n_out)
+{
+    const int64_t g = q6kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
+    return align_up(g * nch * 768, kAlign) + align_up(g * nsb * 256, kAlign) + align_up(g * nsb * 32, kAlign);
+}
+
+inline Q6KTView q6kt_view(const void* base, int64_t n_in, int64_t n_out)
+{
+    const char* p = static_cast<const char*>(base);
+    const int64_t g = q6kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
+    const int64_t off_sc = align_up(g * nch * 768, kAlign);
+    const int64_t off_d = off_sc + align_up(g * nsb * 256, kAlign);
+    return Q6KTView{reinterpret_cast<const uint8_t*>(p), reinterpret_cast<const uint32_t*>(p + off_sc),
+                    reinterpret_cast<const uint16_t*>(p + off_d)};
+}
+
 inline int64_t q4k_plane_bytes(int64_t n_in, int64_t n_out)
 {
     const int64_t nsb = n_out * (n_in / 256);
@@ -181,6 +221,7 @@ hipError_t launch_repack_q8_0_tiled(const uint8_t* raw, int64_t n_in, int64_t n_
                                     hipStream_t s);
 hipError_t launch_repack_q6k(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s);
 hipError_t launch_repack_q4k_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s);
+hipError_t launch_repack_q6k_tiled(const uint8_t* raw, int64_t n_in, int64_t n_out, void* dst, hipStream_t s);
 hipError_t launch_dequant_q6k(Q6KView w, int64_t n_in, int64_t n_out, float* out, hipStream_t s);
 hipError_t launch_q6k_gemv(Q6KView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
                            hipStream_t s);
@@ -238,6 +279,13 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
 // takes the shape.
 bool q4k_mfma_supported(int64_t n_in, int64_t batch);
 hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+                                hipStream_t s);
+// The same for Q6_K (n_in one of 1024, 2048, 3072, 4096, 6144, 8192), with a
+// host-side extent check of its plan ("" when every access stays inside the
+// tiled copy, x and out; the launcher refuses any other plan).
+bool q6k_mfma_supported(int64_t n_in, int64_t batch);
+std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out);
+hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
                                 hipStream_t s);
 
 // Batched GEMM over a Q8_0 copy.  With a workspace of q8_gemm_workspace_bytes,

@@ -1,9 +1,10 @@
 """GPU parity of the Q6_K path: the dequantisation export bit for bit against
 the oracle (every weight is exact in f32), and the GEMV to the f32 bound
 |gpu - oracle| <= 1e-5 * S + 1e-6, S = sum_j |w_ij x_bj| from the oracle, on
-the one-row fast shapes (widths 1024..8192 in steps of 1024 on the listed
-set), the general path (other widths, several batch rows), ragged row counts
-and the 128256 x 3072 output-projection shape.  Layout reading: the public
+the one-row matrix-core shapes (widths 1024, 2048, 3072, 4096, 6144, 8192),
+the VALU paths (other widths, several batch rows, a graph captured before the
+tiled copy exists), ragged row counts and the 128256 x 3072
+output-projection shape.  Layout reading: the public
 GGML Q6_K block (parity against real GGML files unpinned)."""
 import numpy as np
 import pytest
@@ -97,3 +98,97 @@ def test_output_projection_shape(qd):
     out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
     ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
     check_f32(out, ref, S, "q6k 128256x3072")
+
+
+# One batch row runs on the integer matrix cores for n_in = 1024, 2048, 3072,
+# 4096, 6144 and 8192: x is taken there as a 30-bit fixed-point number per 16
+# values (one scale group), so inputs whose magnitudes differ widely within a
+# group are its hard cases.
+def _x_kind(kind, seed, n_in):
+    x = synth.normal_f32(seed, (1, n_in))
+    if kind == "outliers":      # one value 1e4 times larger in every 16
+        x[0, 5::16] *= 1e4
+    elif kind == "spread":      # magnitudes over 2^-40 .. 2^40 within each group
+        x *= np.exp2(np.tile(np.linspace(-40, 40, 16), n_in // 16)).astype(np.float32)
+    elif kind == "zeros":       # whole zero groups and powers of two
+        x[0, :256] = 0
+        x[0, 256:512] = np.exp2(np.arange(256) % 16 - 8.0) * np.where(np.arange(256) % 3, 1, -1)
+    elif kind == "tiny":
+        x *= np.float32(1e-30)
+    elif kind == "huge":
+        x *= np.float32(1e30)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("n_in", [1024, 2048, 3072, 4096, 6144, 8192])
+@pytest.mark.parametrize("kind", ["normal", "outliers", "spread", "zeros", "tiny", "huge"])
+def test_one_row_matrix_core_inputs(qd, n_in, kind):
+    n_out = 37   # ragged: the last 16-row group is partly padding
+    raw = synth.q6k_weights(9650 + n_in, n_out, n_in)
+    x = _x_kind(kind, 9651 + n_in, n_in)
+    out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q6k one row {kind} {n_out}x{n_in}")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(8197, 2048), (8192, 1024), (1000, 6144), (20, 8192), (16, 3072)])
+def test_one_row_matrix_core_grids(qd, n_out, n_in):
+    """Two row groups a workgroup from 512 groups on, with a spare last group
+    (8197 rows: 513 groups), and single-group grids."""
+    raw = synth.q6k_weights(9660 + n_out, n_out, n_in)
+    x = synth.normal_f32(9661 + n_in, (1, n_in))
+    out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q6k one row {n_out}x{n_in}")
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_one_row_non_finite_x_propagates(qd, bad):
+    n_out, n_in = 40, 3072
+    raw = synth.q6k_weights(9670, n_out, n_in)
+    x = synth.normal_f32(9671, (1, n_in))
+    x[0, 700] = bad
+    out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
+    assert np.all(np.isnan(out)), "a non-finite x must make every output NaN"
+
+
+def test_one_row_deterministic(qd):
+    """Fixed summation order: repeated calls give the same bits."""
+    n_out, n_in = 8192, 3072
+    raw = dev(synth.q6k_weights(9680, n_out, n_in))
+    x = dev(synth.normal_f32(9681, (1, n_in)))
+    first = host(qd.q6k_gemv(raw, n_in, n_out, x))
+    for _ in range(3):
+        again = host(qd.q6k_gemv(raw, n_in, n_out, x))
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+def test_capture_before_the_tiled_copy_uses_the_valu_kernel(qd):
+    """Inside a graph capture no copy can be made: with only the row-major
+    copy present (a batch-2 call made it), a one-row call captured before any
+    one-row call runs the VALU kernel, and the replays agree with the oracle."""
+    n_out, n_in = 300, 3072
+    raw = synth.q6k_weights(9690, n_out, n_in)
+    w = dev(raw)
+    x2 = dev(synth.normal_f32(9691, (2, n_in)))
+    qd.q6k_gemv(w, n_in, n_out, x2)          # makes the row-major copy only
+    torch.cuda.synchronize()
+    qd.q6k_gemv(w, n_in, n_out, x2)          # finds that copy complete
+    torch.cuda.synchronize()
+    x = synth.normal_f32(9692, (1, n_in))
+    xd = dev(x)
+    out = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            qd.q6k_gemv(w, n_in, n_out, xd, out=out)
+    ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        check_f32(out.cpu().numpy(), ref, S, "q6k captured one row")
+    # outside a capture the tiled copy is made, and the result agrees too
+    direct = host(qd.q6k_gemv(w, n_in, n_out, xd))
+    check_f32(direct, ref, S, "q6k one row after the capture")
