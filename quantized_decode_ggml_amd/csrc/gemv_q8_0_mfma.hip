@@ -1,7 +1,10 @@
 // Q8_0 GEMV for 3..8 batch rows on the matrix cores (gfx950 MFMA), plain,
 // residual, fused QKV and fused SwiGLU.  Same results as the VALU kernels to
 // the f32 tolerance; used when the batch makes those VALU-bound (each weight
-// then costs one multiply-add per batch row on 16-lane SIMDs).
+// then costs one multiply-add per batch row on 16-lane SIMDs).  Two kernels:
+// at widths 1024, 2048, 3072 and 4096 an integer matrix-core kernel that
+// keeps whole rows in one workgroup (see "integer matrix cores" below); at
+// the other widths the bf16 kernel described here.
 //
 // What is computed is unchanged (rustdoc "Module cuda_lane", Functions
 // section): out[b][i] = sum_j (d*q)[i][j] x[b][j] with the epilogues of the
@@ -110,6 +113,28 @@ struct TileArgs {
     float* part;  // ksplit > 1: per (set, slice) the slice's sums, kWaves x NM x batch x 16 floats
 };
 
+// Tile and scale pointers of matrix m of flat 16-row group G (clamped to the
+// last group by the caller), at block blk0, for lane `lane`.
+template <int MODE>
+__device__ inline void group_tiles(const TileArgs& t, int64_t G, int m, int64_t blk0, int lane, const int8_t*& tq,
+                                   const uint16_t*& td)
+{
+    const int64_t tile_stride = t.nb * 512, dtile_stride = t.nb * 16;
+    int64_t oq, od, local;
+    if constexpr (MODE == kSwiGLU) {
+        oq = m ? t.tq1 : 0;
+        od = m ? t.td1 : 0;
+        local = G;
+    } else {
+        const int64_t s1 = G >= t.gend0, s2 = G >= t.gend1;   // 0 or 1, uniform
+        oq = (s1 - s2) * t.tq1 + s2 * t.tq2;
+        od = (s1 - s2) * t.td1 + s2 * t.td2;
+        local = G - s1 * t.gend0 - s2 * (t.gend1 - t.gend0);
+    }
+    tq = t.q0 + oq + local * tile_stride + blk0 * 512 + 8 * lane;
+    td = t.d0 + od + local * dtile_stride + blk0 * 16 + (lane & 15);
+}
+
 // The stacked A rows: virtual row v = p * batch + b holds part p of x[b]
 // (3 * batch rows); fragment f covers rows 16f .. 16f + 15, and lane l of a
 // fragment holds row 16f + l % 16 at k = 8 (l / 16) .. + 7 of its block.
@@ -157,23 +182,8 @@ __global__ __launch_bounds__(kWaves * 64) void q8_0_gemv_mfma(Q8GemvArgs a, Tile
     {
         int64_t G = set * kWaves + w;
         G = G < t.groups ? G : t.groups - 1;                  // loads stay in bounds
-        const int64_t tile_stride = t.nb * 512, dtile_stride = t.nb * 16;
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            int64_t oq, od, local;
-            if constexpr (MODE == kSwiGLU) {
-                oq = m ? t.tq1 : 0;
-                od = m ? t.td1 : 0;
-                local = G;
-            } else {
-                const int64_t s1 = G >= t.gend0, s2 = G >= t.gend1;   // 0 or 1, uniform
-                oq = (s1 - s2) * t.tq1 + s2 * t.tq2;
-                od = (s1 - s2) * t.td1 + s2 * t.td2;
-                local = G - s1 * t.gend0 - s2 * (t.gend1 - t.gend0);
-            }
-            tq[m] = t.q0 + oq + local * tile_stride + blk0 * 512 + 8 * lane;
-            td[m] = t.d0 + od + local * dtile_stride + blk0 * 16 + (lane & 15);
-        }
+        for (int m = 0; m < NM; ++m) group_tiles<MODE>(t, G, m, blk0, lane, tq[m], td[m]);
     }
     u32x2 wq[RS][NM];
     uint16_t wd[RS][NM];
@@ -313,6 +323,214 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(Q8GemvArgs a, const flo
     store_row<MODE>(a, row, b, s[0], s[NM - 1]);
 }
 
+// ------------------------------------------- integer matrix cores --
+// The same products for widths up to 4096 with the whole K of a row inside
+// one workgroup (one launch, no slice sums), on v_mfma_i32_16x16x32_i8.
+// x enters as a 30-bit fixed-point number per (batch row, Q8_0 block):
+// X = trunc(x * 2^(30 - e)), |x| < 2^e over the block's 32 values, so
+// x = X 2^(e - 30) + eps, |eps| < 2^(e - 30) <= 2^-29 max |x| of the block
+// (zero for every value within 2^6 of the block's largest).  X is written as
+// four signed base-256 digits (the bytes of X + 0x80808080, each less 0x80).
+// A fragment of the A operand stacks 4 batch rows x 4 digits as its 16 rows,
+// row 4 (b % 4) + j; the B operand is the tile's 8 int8 weights of the lane
+// as they stand.  One MFMA per block and fragment gives in exact int32
+// D_j = sum_k q_k a_j,k for batch row b and weight row n in lane
+// n + 16 (b % 4), elements j = 0..3; the lane forms
+// u = (256 D3 + D2) 2^16 + (256 D1 + D0) (each bracket below 2^27, exact in
+// f32 up to 2^24 and rounded once above; the fma rounds once) and
+// accumulates d * (u 2^(e - 30)), the power of two exact.  Against the bf16
+// split: no int8 -> bf16 conversion (17 instructions a block and matrix) and
+// 4 bytes of A operand per x value instead of 6, so a workgroup holds the A
+// operands of a whole row in LDS (batch x n_in x 4 bytes: 96 KB at 8 x 3072)
+// and no K slice leaves the workgroup.
+// A workgroup is RG 16-row groups (x 2 matrices for SwiGLU), each with its K
+// over KS waves of T blocks.  Every thread loads its x items and waits for
+// them (behind the grid's weight requests they would land late), then every
+// weight load of its wave is issued, and while those fly the workgroup
+// writes the A fragments and the exponents.  The KS wave sums of an output
+// are added in wave order through LDS; then the epilogue.  A non-finite x
+// makes every output of its batch row NaN.
+// Rounding: per block at most 2 in u and 1 in the accumulation, KS - 1 for
+// the wave sums, 1 for the residual; with T <= 16 below 60 units of 2^-24 of
+// sum_j |w x|, plus the truncation of x above.
+template <int MODE, int KS, int T, int NV, int RG>
+__global__ __launch_bounds__(64 * KS * RG) void q8_0_gemv_i8(Q8GemvArgs a, TileArgs t)
+{
+    static_assert(KS * RG <= 16 && T % 4 == 0 && NV >= 1 && NV <= 2, "KS * RG waves, T blocks a wave");
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NM = (MODE == kSwiGLU) ? 2 : 1;
+    constexpr int NB = KS * T;                          // Q8_0 blocks of a row
+    constexpr int NW = KS * RG;
+    constexpr int NT = 64 * NW;
+    constexpr int XB = NB * NV * 512;                   // A fragments
+    constexpr int RB = NW * NM * NV * 64 * 4;           // wave sums, after the products
+    constexpr int LB = XB > RB ? XB : RB;
+    constexpr int IPT = (4 * NV * NB * 4 + NT - 1) / NT;   // x items (8 values) a thread
+    __shared__ __attribute__((aligned(16))) char lds[LB];
+    __shared__ __attribute__((aligned(16))) int xe[4 * NV][NB];   // e - 30 per (batch row, block)
+    __shared__ uint32_t wbad[NW];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = w / KS, kw = w % KS;
+    const int64_t Gw = (int64_t)blockIdx.x * RG + rg;
+    const int64_t G = Gw < t.groups ? Gw : t.groups - 1;     // a spare wave reads the last group
+    const int64_t blk0 = (int64_t)kw * T;
+
+    // x item it = (b, blk, g), g fastest: values 32 blk + 8 g .. +7 of batch row b
+    const int items = a.batch * NB * 4;
+    float4 xv[IPT][2];
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+        const int it = (int)threadIdx.x + j * NT;
+        if (it < items) {
+            const float4* src =
+                reinterpret_cast<const float4*>(a.x + (int64_t)(it / (NB * 4)) * a.n_in) + 2 * (it % (NB * 4));
+            xv[j][0] = src[0];
+            xv[j][1] = src[1];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    // every weight load of this wave
+    const int8_t* tq[NM];
+    const uint16_t* td[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) group_tiles<MODE>(t, G, m, blk0, lane, tq[m], td[m]);
+    u32x2 wq[T][NM];
+    uint16_t wd[T][NM];
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            wq[i][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tq[m] + i * 512));
+            wd[i][m] = __builtin_nontemporal_load(td[m] + i * 16);
+        }
+    asm volatile("" ::: "memory");
+
+    // A fragments: lane (m, g) of fragment (blk, f) reads the 8 bytes at
+    // ((blk NV + f) 64 + 16 g + (m ^ (blk % 16))) * 8 -- digit m % 4 of
+    // batch row 4 f + m / 4 at k = 8 g .. 8 g + 7 of block blk.  The XOR is a
+    // permutation inside each 16-lane group (the reads stay conflict-free);
+    // it spreads the writes, where the lanes of a wave hold 16 blocks x 4
+    // k-groups of one digit row, over all LDS banks (unswizzled they hit two).
+    u32x2* xf = reinterpret_cast<u32x2*>(lds);
+    uint32_t badm = 0;   // bit b: a non-finite x in batch row b
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+        const int it = (int)threadIdx.x + j * NT;
+        if (it < items) {   // the 4 lanes of a block agree
+            const int b = it / (NB * 4), blk = (it >> 2) % NB, g = it & 3;
+            const float v[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                                xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+            uint32_t amax = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = max(amax, __builtin_bit_cast(uint32_t, v[e]) & 0x7fffffffu);
+            // over the block's 4 items (4 consecutive lanes): lane ^ 1, lane ^ 2
+            amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
+            amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
+            if (amax >= 0x7f800000u) badm |= 1u << b;
+            // amax = m 2^e with 0.5 <= m < 1, so every |x| < 2^e (e = 0 for zeros)
+            const int ex = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
+            uint32_t y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (uint32_t)(int)__builtin_amdgcn_ldexpf(v[e], 30 - ex) + 0x80808080u;
+            // word dj of each half: digit dj of its 4 values
+            uint32_t dg[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t t01l = __builtin_amdgcn_perm(y[4 * h + 1], y[4 * h], 0x05010400u);
+                const uint32_t t01h = __builtin_amdgcn_perm(y[4 * h + 1], y[4 * h], 0x07030602u);
+                const uint32_t t23l = __builtin_amdgcn_perm(y[4 * h + 3], y[4 * h + 2], 0x05010400u);
+                const uint32_t t23h = __builtin_amdgcn_perm(y[4 * h + 3], y[4 * h + 2], 0x07030602u);
+                dg[h][0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u) ^ 0x80808080u;
+                dg[h][1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u) ^ 0x80808080u;
+                dg[h][2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u) ^ 0x80808080u;
+                dg[h][3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u) ^ 0x80808080u;
+            }
+            u32x2* frag = xf + (blk * NV + (b >> 2)) * 64 + 16 * g;
+#pragma unroll
+            for (int dj = 0; dj < 4; ++dj) frag[(4 * (b & 3) + dj) ^ (blk & 15)] = u32x2{dg[0][dj], dg[1][dj]};
+            if (g == 0) xe[b][blk] = ex - 30;
+        }
+    }
+    uint32_t wm = 0;
+#pragma unroll
+    for (int b = 0; b < 4 * NV; ++b)
+        if (__builtin_amdgcn_ballot_w64(((badm >> b) & 1u) != 0) != 0) wm |= 1u << b;
+    if (lane == 0) wbad[w] = wm;
+    __syncthreads();   // LDS only: the weight loads stay in flight
+    uint32_t bad = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) bad |= wbad[k];
+
+    // lane (n = lane % 16, b' = lane / 16) of fragment f: batch row 4 f + b'
+    int eb[NV][T];
+#pragma unroll
+    for (int f = 0; f < NV; ++f)
+#pragma unroll
+        for (int q = 0; q < T / 4; ++q) {
+            const int4 e4 = *reinterpret_cast<const int4*>(&xe[4 * f + (lane >> 4)][blk0 + 4 * q]);
+            eb[f][4 * q] = e4.x;
+            eb[f][4 * q + 1] = e4.y;
+            eb[f][4 * q + 2] = e4.z;
+            eb[f][4 * q + 3] = e4.w;
+        }
+    float acc[NM][NV];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int f = 0; f < NV; ++f) acc[m][f] = 0.0f;
+    const u32x2* xw = xf + blk0 * NV * 64;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+        const int sl = lane ^ (int)((blk0 + i) & 15);
+        u32x2 A[NV];
+#pragma unroll
+        for (int f = 0; f < NV; ++f) A[f] = xw[(i * NV + f) * 64 + sl];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const float dsc = fp16_bits_to_f32(wd[i][m]);
+#pragma unroll
+            for (int f = 0; f < NV; ++f) {
+                const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, A[f]),
+                                                                      __builtin_bit_cast(long, wq[i][m]),
+                                                                      i32x4{0, 0, 0, 0}, 0, 0, 0);
+                const float u =
+                    __builtin_fmaf((float)(D[3] * 256 + D[2]), 65536.0f, (float)(D[1] * 256 + D[0]));
+                acc[m][f] = __builtin_fmaf(dsc, __builtin_amdgcn_ldexpf(u, eb[f][i]), acc[m][f]);
+            }
+        }
+    }
+
+    // the KS wave sums of each output in wave order, then the epilogue
+    __syncthreads();   // every wave is done with the A fragments
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int f = 0; f < NV; ++f) red[((w * NM + m) * NV + f) * 64 + lane] = acc[m][f];
+    __syncthreads();
+    if (kw != 0) return;
+    const int64_t row = Gw * 16 + (lane & 15);
+#pragma unroll
+    for (int f = 0; f < NV; ++f) {
+        float sm[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            sm[m] = red[(((rg * KS) * NM + m) * NV + f) * 64 + lane];
+#pragma unroll
+            for (int k = 1; k < KS; ++k) sm[m] += red[((((rg * KS + k) * NM) + m) * NV + f) * 64 + lane];
+        }
+        const int b = 4 * f + (lane >> 4);
+        if (b < a.batch && Gw < t.groups && row < a.total_rows) {
+            const float nan = __builtin_nanf("");
+            const bool nb_ = (bad >> b) & 1u;
+            store_row<MODE>(a, row, b, nb_ ? nan : sm[0], nb_ ? nan : sm[NM - 1]);
+        }
+    }
+}
+
 using MfmaFn = void (*)(Q8GemvArgs, TileArgs);
 
 // x fragments per block: the 3 * batch stacked part rows in groups of 16
@@ -334,6 +552,42 @@ template <int MODE>
 MfmaFn pick_mfma(int nbw, int nv)
 {
     return nv == 1 ? pick_nbw<MODE, 1>(nbw) : pick_nbw<MODE, 2>(nbw);
+}
+
+// K split of the integer path: n_in = 32 KS T, T = 16 blocks a wave; two
+// row groups a workgroup from 512 groups on, up to 12 waves (16 waves of
+// SwiGLU would spill registers).
+bool i8_shape(int64_t n_in, int* ks, int* t)
+{
+    *t = 16;
+    switch (n_in) {
+        case 1024: *ks = 2; return true;
+        case 2048: *ks = 4; return true;
+        case 3072: *ks = 6; return true;
+        case 4096: *ks = 8; return true;
+        default: return false;
+    }
+}
+
+int i8_rg(int64_t groups, int ks) { return groups >= 512 && ks <= 6 ? 2 : 1; }
+
+template <int MODE, int KS, int T>
+MfmaFn pick_i8_rg(int nv, int rg)
+{
+    if (nv == 1) return rg == 2 ? q8_0_gemv_i8<MODE, KS, T, 1, 2> : q8_0_gemv_i8<MODE, KS, T, 1, 1>;
+    return rg == 2 ? q8_0_gemv_i8<MODE, KS, T, 2, 2> : q8_0_gemv_i8<MODE, KS, T, 2, 1>;
+}
+
+template <int MODE>
+MfmaFn pick_i8(int ks, int nv, int rg)
+{
+    switch (ks) {
+        case 2: return pick_i8_rg<MODE, 2, 16>(nv, rg);
+        case 4: return pick_i8_rg<MODE, 4, 16>(nv, rg);
+        case 6: return pick_i8_rg<MODE, 6, 16>(nv, rg);
+        case 8: return nv == 1 ? q8_0_gemv_i8<MODE, 8, 16, 1, 1> : q8_0_gemv_i8<MODE, 8, 16, 2, 1>;
+        default: return nullptr;
+    }
 }
 
 // Flat 16-row groups of a problem: the segments (all but the last a multiple
@@ -382,6 +636,24 @@ std::string q8_mfma_plan_check(const Q8GemvProblem& p, int64_t ws_bytes)
         return std::string(why);
     };
     const int64_t nb = p.n_in / 32, rows = flat_rows(p);
+    int iks = 0, it = 0;
+    if (i8_shape(p.n_in, &iks, &it)) {
+        // integer path: one workgroup per RG row groups, whole rows
+        if ((int64_t)iks * it != nb) return over("waves x blocks", (int64_t)iks * it, nb);
+        if (p.batch > 8) return over("batch rows", p.batch, 8);
+        // x: item (b, blk, g) reads floats b n_in + 32 blk + 8 g .. +7
+        const int64_t x_end = (p.batch - 1) * p.n_in + (nb - 1) * 32 + 3 * 8 + 8;
+        if (x_end > p.batch * p.n_in) return over("x", x_end, p.batch * p.n_in);
+        for (int k = 0; k < (p.mode == kSwiGLU ? 2 : p.nseg); ++k) {
+            const int64_t segrows = p.mode == kSwiGLU ? p.rows[0] : p.rows[k];
+            const int64_t g = q8t_groups(segrows), tiles = g * nb;
+            const int64_t q_end = ((g - 1) * nb + nb - 1) * 512 + 8 * 63 + 8;
+            const int64_t d_end = (((g - 1) * nb + nb - 1) * 16 + 15 + 1) * 2;
+            if (q_end > tiles * 512) return over("weight tiles", q_end, tiles * 512);
+            if (d_end > tiles * 32) return over("tile scales", d_end, tiles * 32);
+        }
+        return std::string();
+    }
     const int nbw = slice_blocks(p.n_in, rows);
     const int64_t ksplit = nb / nbw;
     if (nbw != 8 && nbw != 16 && nbw != 24 && nbw != 32) return over("slice blocks", nbw, 32);
@@ -430,6 +702,8 @@ bool q8_mfma_supported(const Q8GemvProblem& p)
 // kWaves x NM x batch x 16 floats.
 int64_t q8_mfma_workspace_bytes(int mode, int64_t n_in, int64_t rows, int64_t batch)
 {
+    int iks = 0, it = 0;
+    if (i8_shape(n_in, &iks, &it)) return 0;   // the integer path keeps whole rows
     const int64_t ksplit = (n_in / 32) / slice_blocks(n_in, rows);
     if (ksplit <= 1) return 0;
     const int64_t sets = (q8t_groups(rows) + kWaves - 1) / kWaves;
@@ -460,6 +734,23 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
     } else {
         t.groups = q8t_groups(p.rows[0]);
         t.gend0 = t.gend1 = t.groups;
+    }
+    int iks = 0, it = 0;
+    if (i8_shape(p.n_in, &iks, &it)) {
+        if (!q8_mfma_plan_check(p, 0).empty()) return hipErrorInvalidConfiguration;
+        const int rg = i8_rg(t.groups, iks), nv = (int)((p.batch + 3) / 4);
+        t.ksplit = 1;
+        MfmaFn fn = nullptr;
+        switch (p.mode) {
+            case kPlain: fn = pick_i8<kPlain>(iks, nv, rg); break;
+            case kResidual: fn = pick_i8<kResidual>(iks, nv, rg); break;
+            case kQKV: fn = pick_i8<kQKV>(iks, nv, rg); break;
+            default: fn = pick_i8<kSwiGLU>(iks, nv, rg); break;
+        }
+        if (!fn) return hipErrorNotSupported;
+        hipLaunchKernelGGL(fn, dim3((unsigned)((t.groups + rg - 1) / rg)), dim3(64 * iks * rg), 0, s, a, t);
+        count_launch();
+        return hipGetLastError();
     }
     const int64_t rows = flat_rows(p);
     const int nbw = slice_blocks(p.n_in, rows);

@@ -1,8 +1,10 @@
-"""GPU parity of the matrix-core Q8_0 GEMV path (3..8 batch rows): which path
+"""GPU parity of the matrix-core Q8_0 GEMV paths (3..8 batch rows): which path
 runs, every supported width, ragged rows and segments, activations over a wide
-dynamic range (the exact three-part bf16 split of x), bitwise reproducibility
-of the K split over workgroups, graph capture with and without a prepared
-workspace, and a refused workspace allocation.
+dynamic range (the exact three-part bf16 split of x; the per-block fixed-point
+x of the integer path at widths 1024..4096), bitwise reproducibility of the K
+split over workgroups and of the one-launch integer path, non-finite x, graph
+capture with and without a prepared workspace, and a refused workspace
+allocation.
 
 Bar: the f32 bound, |gpu - oracle| <= 1e-5 * S + 1e-6 with S = sum_j |w x|
 from the oracle (SwiGLU: the propagated bound of helpers.swiglu_tol).
@@ -54,15 +56,17 @@ def launches(qd, fn):
     return r, qd.launch_count() - before
 
 
-@pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 2), (3072, 4, 2),
-                                               (3072, 8, 2), (8192, 5, 2), (2048, 8, 2), (1024, 8, 2),
-                                               (512, 4, 2), (2560, 8, 2), (256, 6, 1), (2080, 8, 1),
-                                               (9216, 4, 1)])
+@pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 1), (3072, 4, 1),
+                                               (3072, 8, 1), (8192, 5, 2), (2048, 8, 1), (1024, 8, 1),
+                                               (4096, 6, 1), (512, 4, 2), (2560, 8, 2), (6144, 3, 2),
+                                               (256, 6, 1), (2080, 8, 1), (9216, 4, 1)])
 def test_path_selection(qd, n_in, batch, expect):
-    """3..8 rows at a supported width (n_in % 256 == 0, up to 8192): the
-    matrix-core kernel, plus the ordered sum of its K slices where K is split
-    over workgroups (2 launches; 48 rows always split K from 512 columns,
-    256 columns is one slice); otherwise the VALU kernel (1 launch)."""
+    """3..8 rows at 1024, 2048, 3072 or 4096 columns: the integer matrix-core
+    kernel, whole rows in one workgroup (1 launch).  Other supported widths
+    (n_in % 256 == 0, up to 8192): the bf16 matrix-core kernel, plus the
+    ordered sum of its K slices where K is split over workgroups (2 launches;
+    48 rows always split K from 512 columns, 256 columns is one slice);
+    otherwise the VALU kernel (1 launch)."""
     n_out = 48
     raw = q8_weights(9000 + n_in, n_out, n_in)
     x = synth.normal_f32(9001 + batch, (batch, n_in))
@@ -141,11 +145,11 @@ def test_residual_in_place(qd, batch):
 @pytest.mark.parametrize("n_out", [8192, 1024])
 def test_graph_capture_with_workspace(qd, n_out):
     """Warm-up on the capture stream makes its workspace; the captured graph
-    then uses the matrix-core path (2 launches recorded: the kernel and the
-    ordered sum of its K slices) and every replay, with eager work in
+    then uses the bf16 matrix-core path (2 launches recorded: the kernel and
+    the ordered sum of its K slices) and every replay, with eager work in
     between, matches the eager result bit for bit."""
     bitwise = True
-    n_in, batch = 3072, 4
+    n_in, batch = 8192, 4
     raw = q8_weights(9600, n_out, n_in)
     x = synth.normal_f32(9601, (batch, n_in))
     w, xd = dev(raw), dev(x)
@@ -174,7 +178,7 @@ def test_graph_capture_with_workspace(qd, n_out):
     del g
 
 
-@pytest.mark.parametrize("n_out,n_in,mode", [(3072, 8192, "residual"), (1024, 2048, "plain"), (77, 3072, "plain")])
+@pytest.mark.parametrize("n_out,n_in,mode", [(3072, 8192, "residual"), (1024, 6144, "plain"), (77, 2560, "plain")])
 @pytest.mark.parametrize("batch", [3, 5, 8])
 def test_k_split_bitwise_reproducible(qd, n_out, n_in, mode, batch):
     """K split over workgroups, the slices added in slice order by a second
@@ -203,9 +207,10 @@ def test_k_split_bitwise_reproducible(qd, n_out, n_in, mode, batch):
 
 
 def test_graph_capture_without_workspace_falls_back(qd):
-    """A capturing stream with no workspace cannot allocate one: the call takes
-    the VALU kernel (1 launch recorded) and stays within the bound."""
-    n_out, n_in, batch = 512, 3072, 8
+    """A capturing stream with no workspace cannot allocate one: a call that
+    would split K takes the VALU kernel (1 launch recorded) and stays within
+    the bound."""
+    n_out, n_in, batch = 512, 8192, 8
     raw = q8_weights(9700, n_out, n_in)
     x = synth.normal_f32(9701, (batch, n_in))
     w, xd = dev(raw), dev(x)
@@ -227,12 +232,14 @@ def test_graph_capture_without_workspace_falls_back(qd):
 
 
 @pytest.mark.parametrize("mode", ["plain", "residual", "qkv", "swiglu"])
-def test_one_slice_per_row_needs_no_workspace(qd, mode):
-    """28672 rows x 1024 columns fill the chip with one K slice per row: the
+@pytest.mark.parametrize("n_in", [512, 1024])
+def test_one_slice_per_row_needs_no_workspace(qd, mode, n_in):
+    """28672 rows x 512 columns fill the chip with one K slice per row of the
+    bf16 kernel, and at 1024 columns the integer kernel keeps whole rows: the
     workgroups store the rows themselves (1 launch), so a capture on a stream
-    that has no workspace still takes the matrix-core kernel; replays match
-    the eager result bit for bit and the oracle to the f32 bound."""
-    n_in, batch = 1024, 5
+    that has no workspace still takes a matrix-core kernel; replays match the
+    eager result bit for bit and the oracle to the f32 bound."""
+    batch = 5
     n_out = 28672 if mode != "qkv" else 14336
     raws = [q8_weights(9720 + k, n_out, n_in) for k in range(3 if mode == "qkv" else 2 if mode == "swiglu" else 1)]
     x = synth.normal_f32(9725, (batch, n_in))
@@ -309,7 +316,7 @@ def test_capture_with_pending_repack_is_rejected(qd):
 
 
 def test_workspace_allocation_refused(qd, monkeypatch):
-    n_out, n_in, batch = 64, 3072, 4
+    n_out, n_in, batch = 64, 8192, 4
     w = dev(q8_weights(9800, n_out, n_in))
     x = dev(synth.normal_f32(9801, (batch, n_in)))
     qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)       # the repack itself is allowed
@@ -318,3 +325,95 @@ def test_workspace_allocation_refused(qd, monkeypatch):
     with pytest.raises(qd.QdecError) as ei:
         qd.q8_0_gemv(w, n_in, n_out, x)
     assert ei.value.status == qd.QDEC_ENOMEM
+
+
+# The integer path (widths 1024 .. 4096) takes x as a 30-bit fixed-point number
+# per (batch row, 32-value block), so inputs whose magnitudes differ widely
+# inside a block are its hard cases.
+def _x_kind(kind, seed, batch, n_in):
+    x = synth.normal_f32(seed, (batch, n_in))
+    if kind == "outliers":      # one value 1e4 times larger in every block
+        x[:, 17::32] *= 1e4
+    elif kind == "spread":      # magnitudes over 2^-40 .. 2^40 inside each block
+        x *= np.exp2(np.tile(np.linspace(-40, 40, 32), n_in // 32)).astype(np.float32)
+    elif kind == "zeros":       # whole zero blocks, zero rows and powers of two
+        x[:, :64] = 0
+        x[0, :] = 0
+        x[:, 64:128] = np.exp2(np.arange(64) % 16 - 8.0) * np.where(np.arange(64) % 3, 1, -1)
+    elif kind == "tiny":
+        x *= np.float32(1e-30)
+    elif kind == "huge":
+        x *= np.float32(1e30)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("n_in", [1024, 2048, 3072, 4096])
+@pytest.mark.parametrize("kind", ["normal", "outliers", "spread", "zeros", "tiny", "huge"])
+@pytest.mark.parametrize("batch", [3, 5, 8])
+def test_integer_path_inputs(qd, n_in, kind, batch):
+    n_out = 37   # ragged: the last 16-row group is partly padding
+    raw = q8_weights(9900 + n_in, n_out, n_in)
+    x = _x_kind(kind, 9901 + n_in + batch, batch, n_in)
+    out = host(qd.q8_0_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"integer path {kind} {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(8197, 2048), (8192, 3072), (1000, 4096), (16, 1024), (5120, 3072)])
+@pytest.mark.parametrize("batch", [4, 7])
+def test_integer_path_grids(qd, n_out, n_in, batch):
+    """Two row groups a workgroup from 512 groups on, with a spare last group
+    (8197 rows: 513 groups), and single-group grids; five calls give the same
+    bits."""
+    raw = q8_weights(9950 + n_out, n_out, n_in)
+    x = synth.normal_f32(9951 + n_in, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    runs = []
+    for _ in range(5):
+        out, n = launches(qd, lambda: qd.q8_0_gemv(w, n_in, n_out, xd))
+        assert n == 1
+        runs.append(host(out))
+    for k in range(1, 5):
+        assert np.array_equal(runs[k].view(np.uint32), runs[0].view(np.uint32)), f"call {k} differs"
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    check_f32(runs[0], ref, S, f"integer path {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("n_in", [1024, 3072])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_integer_path_non_finite_row(qd, n_in, bad):
+    """A non-finite x makes every output of its batch row NaN; the other
+    rows are unaffected."""
+    n_out, batch = 40, 6
+    raw = q8_weights(9960, n_out, n_in)
+    x = synth.normal_f32(9961, (batch, n_in))
+    x[2, 700] = bad
+    out = host(qd.q8_0_gemv(dev(raw), n_in, n_out, dev(x)))
+    assert np.all(np.isnan(out[2])), "a non-finite x must reach every output of its row"
+    keep = [b for b in range(batch) if b != 2]
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x[keep])
+    check_f32(out[keep], ref, S, "rows without a non-finite x")
+
+
+@pytest.mark.parametrize("n_in", [1024, 3072, 4096])
+@pytest.mark.parametrize("batch", [3, 8])
+def test_integer_path_residual_and_qkv(qd, n_in, batch):
+    n_out = 96
+    raw = q8_weights(9970 + n_in, n_out, n_in)
+    x = synth.normal_f32(9971 + batch, (batch, n_in))
+    r = synth.normal_f32(9972 + batch, (batch, n_out))
+    out = host(qd.q8_0_gemv_residual(dev(raw), n_in, n_out, dev(x), dev(r)))
+    ref, S = oracle.q8_0_gemv_residual(raw, n_in, n_out, x, r)
+    check_f32(out, ref, S, f"integer residual {n_in} b{batch}")
+    n_q, n_kv = 64, 16
+    wq, wk, wv = (q8_weights(9980 + k, n, n_in) for k, n in enumerate((n_q, n_kv, n_kv)))
+    dq, dk, dv, xd = dev(wq), dev(wk), dev(wv), dev(x)
+    for t, rows in ((dq, n_q), (dk, n_kv), (dv, n_kv)):
+        qd.prepare(t, qd.TYPE_Q8_0, n_in, rows)            # repacks are not counted below
+    (q, k, v), n = launches(qd, lambda: qd.q8_0_qkv(dq, dk, dv, n_in, n_q, n_kv, xd))
+    assert n == 1
+    (rq, rk, rv), (sq, sk, sv) = oracle.q8_0_qkv(wq, wk, wv, n_in, n_q, n_kv, x)
+    check_f32(host(q), rq, sq, "q")
+    check_f32(host(k), rk, sk, "k")
+    check_f32(host(v), rv, sv, "v")
