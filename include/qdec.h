@@ -48,7 +48,8 @@
  *   - Workspace: the matrix-core GEMV for 3..8 batch rows (Q8_0, n_in a
  *     multiple of 256 up to 8192) keeps the sums of its K slices where it
  *     splits K over workgroups (never at n_in 1024, 2048, 3072 or 4096,
- *     whose rows stay in one workgroup), q8_0_gemv_topk keeps its candidate lists,
+ *     nor at 6144 or 8192 with up to 4 rows outside SwiGLU, whose rows stay
+ *     in one workgroup), q8_0_gemv_topk keeps its candidate lists,
  *     attention keeps its chunk partials, and the batched GEMMs on their
  *     DMA-fed path (n_in % 64 == 0, and even n_out for Q8_0; K split over up
  *     to 8 slices when the output has few 128 x 128 tiles) round x to bf16
@@ -108,13 +109,14 @@ typedef enum { QDEC_TYPE_F32 = 0, QDEC_TYPE_Q8_0 = 8, QDEC_TYPE_Q4_K = 12, QDEC_
  * out[b][i] = sum_j deq(W)[i][j] * x[b][j] for 1 <= batch <= 8.
  * n_in % 32 == 0, n_in, n_out >= 1.  f32 accumulation.  Reproducibility: the
  * same inputs give the same bits on every call on a given path (with 3..8
- * batch rows at n_in 1024, 2048, 3072 or 4096 each row stays in one
- * workgroup; at other widths K is split over workgroups unless the grid is
- * large enough without it, and a further small launch adds the slices' sums
- * in a fixed order).  With 3..8 rows at those four widths x enters the matrix
- * cores as a 30-bit fixed-point number per 32-value block (error at most
- * 2^-29 of the block's largest |x| per value, beyond f32 rounding) and a
- * non-finite x makes every output of its batch row NaN. */
+ * batch rows at n_in 1024, 2048, 3072 or 4096, and 3..4 rows at 6144 or
+ * 8192, each row stays in one workgroup; otherwise K is split over
+ * workgroups unless the grid is large enough without it, and a further small
+ * launch adds the slices' sums in a fixed order).  On the one-workgroup
+ * shapes x enters the matrix cores as a 30-bit fixed-point number per
+ * 32-value block (error at most 2^-29 of the block's largest |x| per value,
+ * beyond f32 rounding) and a non-finite x makes every output of its batch
+ * row NaN. */
 QDEC_API int q8_0_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
               const float* x, float* out, hipStream_t stream);
 

@@ -556,8 +556,10 @@ MfmaFn pick_mfma(int nbw, int nv)
 
 // K split of the integer path: n_in = 32 KS T, T = 16 blocks a wave; two
 // row groups a workgroup from 512 groups on, up to 12 waves (16 waves of
-// SwiGLU would spill registers).
-bool i8_shape(int64_t n_in, int* ks, int* t)
+// SwiGLU would spill registers).  6144 and 8192 columns fit LDS (12 and 16
+// waves, 96 and 128 KB of A operands) with one fragment, up to 4 batch rows,
+// and one matrix.
+bool i8_shape(int64_t n_in, int64_t batch, int mode, int* ks, int* t)
 {
     *t = 16;
     switch (n_in) {
@@ -565,6 +567,8 @@ bool i8_shape(int64_t n_in, int* ks, int* t)
         case 2048: *ks = 4; return true;
         case 3072: *ks = 6; return true;
         case 4096: *ks = 8; return true;
+        case 6144: *ks = 12; return batch <= 4 && mode != kSwiGLU;
+        case 8192: *ks = 16; return batch <= 4 && mode != kSwiGLU;
         default: return false;
     }
 }
@@ -586,6 +590,12 @@ MfmaFn pick_i8(int ks, int nv, int rg)
         case 4: return pick_i8_rg<MODE, 4, 16>(nv, rg);
         case 6: return pick_i8_rg<MODE, 6, 16>(nv, rg);
         case 8: return nv == 1 ? q8_0_gemv_i8<MODE, 8, 16, 1, 1> : q8_0_gemv_i8<MODE, 8, 16, 2, 1>;
+        case 12:
+            if constexpr (MODE != kSwiGLU) return nv == 1 ? q8_0_gemv_i8<MODE, 12, 16, 1, 1> : nullptr;
+            return nullptr;
+        case 16:
+            if constexpr (MODE != kSwiGLU) return nv == 1 ? q8_0_gemv_i8<MODE, 16, 16, 1, 1> : nullptr;
+            return nullptr;
         default: return nullptr;
     }
 }
@@ -637,7 +647,7 @@ std::string q8_mfma_plan_check(const Q8GemvProblem& p, int64_t ws_bytes)
     };
     const int64_t nb = p.n_in / 32, rows = flat_rows(p);
     int iks = 0, it = 0;
-    if (i8_shape(p.n_in, &iks, &it)) {
+    if (i8_shape(p.n_in, p.batch, p.mode, &iks, &it)) {
         // integer path: one workgroup per RG row groups, whole rows
         if ((int64_t)iks * it != nb) return over("waves x blocks", (int64_t)iks * it, nb);
         if (p.batch > 8) return over("batch rows", p.batch, 8);
@@ -703,7 +713,7 @@ bool q8_mfma_supported(const Q8GemvProblem& p)
 int64_t q8_mfma_workspace_bytes(int mode, int64_t n_in, int64_t rows, int64_t batch)
 {
     int iks = 0, it = 0;
-    if (i8_shape(n_in, &iks, &it)) return 0;   // the integer path keeps whole rows
+    if (i8_shape(n_in, batch, mode, &iks, &it)) return 0;   // the integer path keeps whole rows
     const int64_t ksplit = (n_in / 32) / slice_blocks(n_in, rows);
     if (ksplit <= 1) return 0;
     const int64_t sets = (q8t_groups(rows) + kWaves - 1) / kWaves;
@@ -736,7 +746,7 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
         t.gend0 = t.gend1 = t.groups;
     }
     int iks = 0, it = 0;
-    if (i8_shape(p.n_in, &iks, &it)) {
+    if (i8_shape(p.n_in, p.batch, p.mode, &iks, &it)) {
         if (!q8_mfma_plan_check(p, 0).empty()) return hipErrorInvalidConfiguration;
         const int rg = i8_rg(t.groups, iks), nv = (int)((p.batch + 3) / 4);
         t.ksplit = 1;

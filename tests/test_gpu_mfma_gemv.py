@@ -58,11 +58,13 @@ def launches(qd, fn):
 
 @pytest.mark.parametrize("n_in,batch,expect", [(3072, 1, 1), (3072, 2, 1), (3072, 3, 1), (3072, 4, 1),
                                                (3072, 8, 1), (8192, 5, 2), (2048, 8, 1), (1024, 8, 1),
-                                               (4096, 6, 1), (512, 4, 2), (2560, 8, 2), (6144, 3, 2),
+                                               (4096, 6, 1), (512, 4, 2), (2560, 8, 2), (6144, 3, 1),
+                                               (8192, 4, 1), (6144, 5, 2),
                                                (256, 6, 1), (2080, 8, 1), (9216, 4, 1)])
 def test_path_selection(qd, n_in, batch, expect):
-    """3..8 rows at 1024, 2048, 3072 or 4096 columns: the integer matrix-core
-    kernel, whole rows in one workgroup (1 launch).  Other supported widths
+    """3..8 rows at 1024, 2048, 3072 or 4096 columns, and 3..4 rows at 6144 or
+    8192: the integer matrix-core kernel, whole rows in one workgroup (1
+    launch).  Other supported widths
     (n_in % 256 == 0, up to 8192): the bf16 matrix-core kernel, plus the
     ordered sum of its K slices where K is split over workgroups (2 launches;
     48 rows always split K from 512 columns, 256 columns is one slice);
@@ -149,7 +151,7 @@ def test_graph_capture_with_workspace(qd, n_out):
     the ordered sum of its K slices) and every replay, with eager work in
     between, matches the eager result bit for bit."""
     bitwise = True
-    n_in, batch = 8192, 4
+    n_in, batch = 8192, 6
     raw = q8_weights(9600, n_out, n_in)
     x = synth.normal_f32(9601, (batch, n_in))
     w, xd = dev(raw), dev(x)
@@ -179,7 +181,7 @@ def test_graph_capture_with_workspace(qd, n_out):
 
 
 @pytest.mark.parametrize("n_out,n_in,mode", [(3072, 8192, "residual"), (1024, 6144, "plain"), (77, 2560, "plain")])
-@pytest.mark.parametrize("batch", [3, 5, 8])
+@pytest.mark.parametrize("batch", [5, 8])
 def test_k_split_bitwise_reproducible(qd, n_out, n_in, mode, batch):
     """K split over workgroups, the slices added in slice order by a second
     launch.  Five calls give the same bits, and they match the oracle to the
@@ -316,7 +318,7 @@ def test_capture_with_pending_repack_is_rejected(qd):
 
 
 def test_workspace_allocation_refused(qd, monkeypatch):
-    n_out, n_in, batch = 64, 8192, 4
+    n_out, n_in, batch = 64, 8192, 6
     w = dev(q8_weights(9800, n_out, n_in))
     x = dev(synth.normal_f32(9801, (batch, n_in)))
     qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)       # the repack itself is allowed
@@ -347,10 +349,12 @@ def _x_kind(kind, seed, batch, n_in):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("n_in", [1024, 2048, 3072, 4096])
+@pytest.mark.parametrize("n_in", [1024, 2048, 3072, 4096, 6144, 8192])
 @pytest.mark.parametrize("kind", ["normal", "outliers", "spread", "zeros", "tiny", "huge"])
-@pytest.mark.parametrize("batch", [3, 5, 8])
+@pytest.mark.parametrize("batch", [3, 4, 5, 8])
 def test_integer_path_inputs(qd, n_in, kind, batch):
+    if n_in >= 6144 and batch > 4:
+        pytest.skip("5..8 rows at 6144 and 8192 columns take the bf16 kernel")
     n_out = 37   # ragged: the last 16-row group is partly padding
     raw = q8_weights(9900 + n_in, n_out, n_in)
     x = _x_kind(kind, 9901 + n_in + batch, batch, n_in)
@@ -359,8 +363,9 @@ def test_integer_path_inputs(qd, n_in, kind, batch):
     check_f32(out, ref, S, f"integer path {kind} {n_out}x{n_in} b{batch}")
 
 
-@pytest.mark.parametrize("n_out,n_in", [(8197, 2048), (8192, 3072), (1000, 4096), (16, 1024), (5120, 3072)])
-@pytest.mark.parametrize("batch", [4, 7])
+@pytest.mark.parametrize("n_out,n_in,batch", [(8197, 2048, 4), (8197, 2048, 7), (8192, 3072, 4), (8192, 3072, 7),
+                                               (1000, 4096, 7), (16, 1024, 4), (5120, 3072, 7), (3072, 8192, 4),
+                                               (3072, 8192, 3), (1000, 6144, 4)])
 def test_integer_path_grids(qd, n_out, n_in, batch):
     """Two row groups a workgroup from 512 groups on, with a spare last group
     (8197 rows: 513 groups), and single-group grids; five calls give the same
@@ -396,8 +401,7 @@ def test_integer_path_non_finite_row(qd, n_in, bad):
     check_f32(out[keep], ref, S, "rows without a non-finite x")
 
 
-@pytest.mark.parametrize("n_in", [1024, 3072, 4096])
-@pytest.mark.parametrize("batch", [3, 8])
+@pytest.mark.parametrize("n_in,batch", [(1024, 3), (1024, 8), (3072, 3), (3072, 8), (4096, 8), (8192, 4)])
 def test_integer_path_residual_and_qkv(qd, n_in, batch):
     n_out = 96
     raw = q8_weights(9970 + n_in, n_out, n_in)

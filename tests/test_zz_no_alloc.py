@@ -33,12 +33,14 @@ def _noalloc(qd, w, n_in, n_out, x, k, logits, idx, val, stream):
                                          _ptr(val), ctypes.c_void_p(stream.cuda_stream))
 
 
-# (n_out, n_in, batch, k, seed); 3..8 rows take the matrix-core projection,
-# whose K slices' sums live in the scratch (added in a fixed order, so the
-# logits are reproducible bit for bit); more than 4096 logits use the
-# candidate lists in the scratch
+# (n_out, n_in, batch, k, seed); 3..8 rows take a matrix-core projection: at
+# 1024..4096 columns whole rows stay in one workgroup, at 2560 columns (and
+# 6144, 8192 from 5 rows) the K slices' sums live in the scratch (added in a
+# fixed order, so the logits are reproducible bit for bit); more than 4096
+# logits use the candidate lists in the scratch
 @pytest.mark.parametrize("cases", [[(50000, 3072, 4, 40, 91), (3000, 1024, 2, 7, 92)],
-                                   [(40000, 3072, 8, 256, 93), (9000, 2048, 3, 1, 94)]])
+                                   [(40000, 3072, 8, 256, 93), (9000, 2048, 3, 1, 94)],
+                                   [(6000, 2560, 6, 40, 95), (5000, 2560, 3, 3, 96)]])
 def test_noalloc_matches_allocating_entry_point(qd, cases):
     stream = torch.cuda.current_stream()
     for n_out, n_in, batch, k, seed in cases:
