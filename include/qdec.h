@@ -71,6 +71,11 @@
  *     the last failure on the calling thread.
  *   - Thread safety: calls may come from several host threads; the repack
  *     cache is guarded by a mutex.
+ *   - Environment (debugging only): QDEC_LOG=1 writes one stderr line per
+ *     library allocation or release ("qdec|repack|...", "qdec|workspace|...",
+ *     "qdec|release|...", "qdec|clear_cache|...": device, pointer, type,
+ *     shape, bytes); QDEC_FAIL_ALLOC=1 makes every repack or workspace
+ *     allocation fail with QDEC_ENOMEM.
  */
 #ifndef QDEC_H
 #define QDEC_H

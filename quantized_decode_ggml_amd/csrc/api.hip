@@ -73,6 +73,31 @@ bool fail_alloc_hook()
     return v && v[0] == '1';
 }
 
+// QDEC_LOG=1: one stderr line per library allocation or release (a repacked
+// copy made or freed, a workspace made or grown), keys separated by '|'.
+bool log_on()
+{
+    static const bool on = [] {
+        const char* v = std::getenv("QDEC_LOG");
+        return v && v[0] == '1';
+    }();
+    return on;
+}
+
+const char* type_name(int type)
+{
+    switch (type) {
+        case QDEC_TYPE_F32: return "f32_bf16_copy";
+        case QDEC_TYPE_Q8_0: return "q8_0";
+        case QDEC_TYPE_Q4_K: return "q4_k";
+        case QDEC_TYPE_Q6_K: return "q6_k";
+        case kTypeQ8_0Tiled: return "q8_0_tiled";
+        case kTypeQ4KTiled: return "q4_k_tiled";
+        case kTypeQ6KTiled: return "q6_k_tiled";
+        default: return "unknown";
+    }
+}
+
 void destroy(Entry& e)
 {
     if (e.ready) (void)hipEventDestroy(e.ready);
@@ -152,6 +177,9 @@ int repacked(const void* w, int type, int64_t n_in, int64_t n_out, hipStream_t s
         }
         ent.made_on = s;
         it = g_cache.emplace(key, ent).first;
+        if (log_on())
+            std::fprintf(stderr, "qdec|repack|dev=%d|w=%p|type=%s|n_in=%lld|n_out=%lld|bytes=%lld\n", dev, w,
+                         type_name(type), (long long)n_in, (long long)n_out, (long long)ent.bytes);
     }
     Entry& ent = it->second;
     if (!ent.done) {
@@ -222,6 +250,9 @@ int stream_workspace(hipStream_t s, int64_t bytes, void** out)
     }
     ent.bytes = bytes;
     *out = ent.buf;
+    if (log_on())
+        std::fprintf(stderr, "qdec|workspace|dev=%d|stream=%p|bytes=%lld|retired=%zu\n", dev, (void*)s,
+                     (long long)bytes, g_ws_retired.size());
     return QDEC_OK;
 }
 
@@ -824,6 +855,9 @@ int qdec_release(const void* w)
     for (auto it = g_cache.begin(); it != g_cache.end();) {
         if (it->first.dev == dev && it->first.ptr == reinterpret_cast<uintptr_t>(w)) {
             (void)hipDeviceSynchronize();
+            if (log_on())
+                std::fprintf(stderr, "qdec|release|dev=%d|w=%p|type=%s|bytes=%lld\n", dev, w,
+                             type_name(it->first.type), (long long)it->second.bytes);
             destroy(it->second);
             it = g_cache.erase(it);
             ++n;
@@ -837,6 +871,9 @@ int qdec_release(const void* w)
 void qdec_clear_cache(void)
 {
     std::lock_guard<std::mutex> lock(g_mu);
+    if (log_on())
+        std::fprintf(stderr, "qdec|clear_cache|copies=%zu|workspaces=%zu|retired=%zu\n", g_cache.size(), g_ws.size(),
+                     g_ws_retired.size());
     int cur = 0;
     const bool have_dev = hipGetDevice(&cur) == hipSuccess;
     for (auto& kv : g_cache) {

@@ -525,3 +525,31 @@ def test_graph_replay_after_workspace_growth(qd):
     assert np.all(np.abs(got - rb) <= BF16_REL * Sb)
     del g
 
+
+
+def test_qdec_log_lines(tmp_path):
+    """QDEC_LOG=1: a child process that prepares a weight, runs a batched GEMV
+    (repacks and a workspace), releases the weight and clears the cache writes
+    one '|'-keyed stderr line for each of those events."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import torch, numpy as np, quantized_decode_ggml_amd as qd, synth\n"
+        "raw = synth.q8_0_weights(5, 64, 8192)[0]\n"
+        "w = torch.from_numpy(raw).cuda()\n"
+        "qd.prepare(w, qd.TYPE_Q8_0, 8192, 64)\n"
+        "x = torch.from_numpy(synth.normal_f32(6, (6, 8192))).cuda()\n"
+        "qd.q8_0_gemv(w, 8192, 64, x); torch.cuda.synchronize()\n"
+        "qd.release(w); qd.clear_cache()\n")
+    env = dict(os.environ, QDEC_LOG="1", PYTHONPATH=os.pathsep.join([root, os.path.join(root, "tests")]))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env, cwd=root)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("qdec|")]
+    kinds = [ln.split("|")[1] for ln in lines]
+    assert kinds.count("repack") == 2, lines          # row-major and tiled Q8_0 copies
+    assert "type=q8_0|n_in=8192|n_out=64" in "".join(lines)
+    assert "type=q8_0_tiled" in "".join(lines)
+    assert kinds.count("workspace") == 1, lines       # the K slices' sums of the 6-row product
+    assert kinds.count("release") == 2 and kinds[-1] == "clear_cache", lines
