@@ -313,8 +313,9 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
 }
 
 // Merge of the chunk partials of one query head (log-sum-exp): the chunk
-// maxima and weights are read in parallel (one chunk per thread, strided) and
-// kept in LDS, then each thread sums its column over the chunks.  (A variant
+// maxima and sums are read in parallel (one chunk per thread, strided), each
+// chunk's weight exp(m_c - m) and weighted sum l_c exp(m_c - m) kept in LDS,
+// then each thread sums its column over the chunks.  (A variant
 // with 256 threads splitting the chunks four ways and an exp per chunk and
 // thread measured slower, and so did a one-pass merge with a running maximum
 // (two exponentials per chunk in one dependent chain per thread: 26 -> 42 us
@@ -323,7 +324,8 @@ template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int64_t nchunks, int group,
                                                          float* __restrict__ out)
 {
-    __shared__ float wsh[1024];
+    __shared__ float wsh[1024];   // exp(m_c - m) of chunk c
+    __shared__ float wl[1024];    // l_c exp(m_c - m)
     __shared__ float red[4];
     const int64_t h = blockIdx.x;
     const int64_t kv = h / group, g = h % group;
@@ -342,14 +344,19 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     for (int64_t c0 = 0; c0 < nchunks; c0 += 1024) {
         const int64_t cn = nchunks - c0 < 1024 ? nchunks - c0 : 1024;
         __syncthreads();                                   // wsh of the previous block is consumed
-        for (int64_t c = j; c < cn; c += D) wsh[c] = expf(at(c0 + c)[0] - m);
-        __syncthreads();
-#pragma unroll 8
-        for (int64_t c = 0; c < cn; ++c) {
+        for (int64_t c = j; c < cn; c += D) {
             const float* pr = at(c0 + c);
-            l = __builtin_fmaf(pr[1], wsh[c], l);
-            o = __builtin_fmaf(pr[2 + j], wsh[c], o);
+            const float wv = expf(pr[0] - m);
+            wsh[c] = wv;
+            wl[c] = pr[1] * wv;
         }
+        __syncthreads();
+        // the chunk sums come from LDS, so the loop below issues only the
+        // vector loads of o: 16 in flight (8: one more round trip per 8
+        // chunks; 32: slower again, measured)
+        for (int64_t c = 0; c < cn; ++c) l += wl[c];
+#pragma unroll 16
+        for (int64_t c = 0; c < cn; ++c) o = __builtin_fmaf(at(c0 + c)[2 + j], wsh[c], o);
     }
     out[h * D + j] = o / l;
 }
