@@ -565,11 +565,15 @@ __global__ __launch_bounds__(64 * KS * RG) void q4k_gemv_mfma(Q4KTView w, const 
         // amax = m 2^e with 0.5 <= m < 1, so every |x| < 2^e (e = 0 for zeros)
         const int e_b = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
         // X = trunc(x 2^(30 - e)), |X| < 2^30; its signed base-256 digits are
-        // the bytes of X + 0x80808080, each less 0x80
+        // the bytes of X + 0x80808080, each less 0x80 (a non-finite sub-block
+        // converts zeros: its sum below makes every output NaN, and an
+        // infinity or NaN has no defined int conversion; a select per value
+        // measured cheaper here than a wave-uniform branch per quad)
+        const bool fin = amax < 0x7f800000u;
         uint32_t y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            y[e] = (uint32_t)(int)__builtin_amdgcn_ldexpf(v[e], 30 - e_b) + 0x80808080u;
+            y[e] = (uint32_t)(int)(fin ? __builtin_amdgcn_ldexpf(v[e], 30 - e_b) : 0.0f) + 0x80808080u;
         // transpose: word j = digit j of the 4 values
         uint32_t wd[4];
         {

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma(Q6KTView w, const 
     for (int k = 0; k < QK; ++k) {
         if (64 * wv + k * NT >= NQ) break;
         const int i = tid + k * NT;
-        const float v[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+        float v[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
         uint32_t amax = max(max(__builtin_bit_cast(uint32_t, v[0]) & 0x7fffffffu,
                                 __builtin_bit_cast(uint32_t, v[1]) & 0x7fffffffu),
                             max(__builtin_bit_cast(uint32_t, v[2]) & 0x7fffffffu,
@@ -444,7 +444,14 @@ __global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma(Q6KTView w, const 
         // over the group's 4 quads (4 consecutive lanes): lane ^ 1, lane ^ 2
         amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
         amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
-        bad |= amax >= 0x7f800000u;
+        const bool fin = amax < 0x7f800000u;
+        if (__builtin_amdgcn_ballot_w64(!fin) != 0) {
+            // rare: a non-finite group converts zeros (every output is NaN;
+            // an infinity or NaN has no defined int conversion)
+            bad |= !fin;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = fin ? v[e] : 0.0f;
+        }
         // amax = m 2^e with 0.5 <= m < 1, so every |x| < 2^e (e = 0 for zeros)
         const int e_s = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
         // X = trunc(x 2^(30 - e)), |X| < 2^30; its signed base-256 digits are

@@ -421,15 +421,22 @@ __global__ __launch_bounds__(64 * KS * RG) void q8_0_gemv_i8(Q8GemvArgs a, TileA
         const int it = (int)threadIdx.x + j * NT;
         if (it < items) {   // the 4 lanes of a block agree
             const int b = it / (NB * 4), blk = (it >> 2) % NB, g = it & 3;
-            const float v[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
-                                xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+            float v[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                          xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
             uint32_t amax = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = max(amax, __builtin_bit_cast(uint32_t, v[e]) & 0x7fffffffu);
             // over the block's 4 items (4 consecutive lanes): lane ^ 1, lane ^ 2
             amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
             amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
-            if (amax >= 0x7f800000u) badm |= 1u << b;
+            const bool fin = amax < 0x7f800000u;
+            if (__builtin_amdgcn_ballot_w64(!fin) != 0) {
+                // rare: a non-finite block converts zeros (its row's outputs
+                // are NaN; an infinity or NaN has no defined int conversion)
+                badm |= fin ? 0u : 1u << b;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = fin ? v[e] : 0.0f;
+            }
             // amax = m 2^e with 0.5 <= m < 1, so every |x| < 2^e (e = 0 for zeros)
             const int ex = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
             uint32_t y[8];
