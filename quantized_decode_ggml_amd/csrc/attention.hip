@@ -143,8 +143,16 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
     const int64_t chunk = blockIdx.x, kv = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t nchunks = gridDim.x;
-    for (int u = tid; u < group * D; u += 256) qs[u] = q[(kv * group) * D + u];   // heads kv*group .. +group
-    __syncthreads();
+    // the group's query vectors (heads kv*group .. +group) go to LDS by DMA
+    // ahead of everything else; the wait for the K rows below covers them,
+    // so no load round trip precedes the cache stream
+    {
+        const float* qsrc = q + (kv * group) * D;
+        const int nq4 = group * D / 4;   // 16-byte pieces
+        for (int base = __builtin_amdgcn_readfirstlane(wave) * 64; base < nq4; base += 256)
+            if (base + lane < nq4)
+                __builtin_amdgcn_global_load_lds(qsrc + (base + lane) * 4, (lds_void*)(qs + base * 4), 16, 0, 0);
+    }
 
     const int pl = tid / TPP, seg = tid % TPP;
     const int64_t t = chunk * CH + pl;
