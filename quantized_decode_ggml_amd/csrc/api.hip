@@ -723,7 +723,8 @@ int q6k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const fl
         // one row on the matrix cores, from the fragment-tiled copy; inside a
         // capture that copy may be missing, and the VALU kernel then runs
         QDEC_TRY(repacked(w, kTypeQ6KTiled, n_in, n_out, stream, &buf, false, true));
-        if (buf) return finish(launch_q6k_gemv_mfma(q6kt_view(buf, n_in, n_out), n_in, n_out, x, out, stream), fn);
+        if (buf)
+            return finish(launch_q6k_gemv_mfma(q6kt_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
     }
     QDEC_TRY(repacked(w, QDEC_TYPE_Q6_K, n_in, n_out, stream, &buf));
     return finish(launch_q6k_gemv(q6k_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
@@ -825,9 +826,12 @@ int qdec_check_plans(int64_t n_in, int64_t n_out, int64_t batch)
             if (!why.empty()) return bad(why);
         }
     }
-    // the one-row Q6_K matrix-core GEMV (widths that are multiples of 256)
+    // the Q6_K matrix-core GEMV (widths that are multiples of 256), one row
+    // and this batch
     if (n_in % 256 == 0 && q6k_mfma_supported(n_in, 1)) {
-        const std::string why = q6k_mfma_plan_check(n_in, n_out);
+        std::string why = q6k_mfma_plan_check(n_in, n_out, 1);
+        if (why.empty() && batch > 1 && batch <= QDEC_GEMV_MAX_BATCH && q6k_mfma_supported(n_in, batch))
+            why = q6k_mfma_plan_check(n_in, n_out, batch);
         if (!why.empty()) return bad(why);
     }
     // the batched GEMMs, with and without a workspace (a capture on a stream

@@ -534,6 +534,184 @@ __global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma(Q6KTView w, const 
     if (lane < 16 && Gw < groups && row < n_out) out[row] = acc;
 }
 
+// Two to eight batch rows on the integer matrix cores, from the same tiled
+// copy and with the same arithmetic per row as q6k_gemv_mfma: each chunk's B
+// operand (the unpacked quants) and d sc are formed once and multiplied by
+// every batch row's A cells, one MFMA per row.  The rows' A cells and
+// exponents take B x n_in x 4.25 bytes of LDS (B n_in <= 24576, so 8 rows up
+// to 3072 columns, 4 up to 6144, 2 up to 8192); two row groups a workgroup,
+// each with K over KS waves of T chunks.  B is the batch rounded up to 2, 4
+// or 8: rows past the real batch repeat its last row and are not stored.  A
+// non-finite x makes every output of its batch row NaN.
+template <int B, int KS, int T>
+__global__ __launch_bounds__(128 * KS) void q6k_gemv_mfma_rows(Q6KTView w, const float* __restrict__ x, int64_t n_in,
+                                                                int64_t n_out, int batch, float* __restrict__ out)
+{
+    constexpr int RG = 2;
+    static_assert(T % 4 == 0 && T >= 4 && T <= 16 && KS * RG <= 16, "T chunks per wave, KS * RG waves");
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const uint16_t global_u16;
+    constexpr int n = 64 * T * KS;     // n_in
+    constexpr int NCH = n / 64;
+    constexpr int NW = KS * RG;
+    constexpr int NT = 64 * NW;
+    constexpr int NQ = n / 4;          // quads of one batch row
+    constexpr int QK = (B * NQ + NT - 1) / NT;
+    constexpr int CB = 272;            // LDS bytes a chunk and row: 16 A cells, one zero cell
+    static_assert(QK <= 12 && B * n <= 24576, "quads per thread, LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[B * CB * NCH];
+    __shared__ __attribute__((aligned(16))) int xe[B][4][NCH];   // e_s - 32 of row b, group s, chunk c
+    __shared__ uint32_t wbad[NW];
+    __shared__ float red[RG][KS][B][16];
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wv / KS, kw = wv % KS;
+    const int64_t groups = q6kt_groups(n_out);
+    const int64_t Gw = (int64_t)blockIdx.x * RG + rg;
+    const int64_t G = Gw < groups ? Gw : groups - 1;           // a spare wave reads the last group
+    const int64_t nsb = n_in >> 8;
+    const int c0 = kw * T;
+
+    // quads it = tid + k NT of the B rows: row it / NQ (whole waves, NQ % 64
+    // == 0), quad it % NQ
+    float4 xv[QK];
+#pragma unroll
+    for (int k = 0; k < QK; ++k) {
+        const int it = tid + k * NT;
+        if (64 * wv + k * NT < B * NQ) {
+            const int b = it / NQ;
+            const int br = b < batch ? b : batch - 1;
+            xv[k] = reinterpret_cast<const float4*>(x + (int64_t)br * n_in)[it % NQ];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    Bits12 qv[T];
+    uint32_t scv[T / 4];
+    uint16_t dv[T / 4];
+    {
+        const int64_t cell0 = (G * NCH + c0) * 64 + lane;
+        const uint8_t* qb = w.q + cell0 * 12;
+        const global_u32* st = (const global_u32*)w.sc + (G * nsb + c0 / 4) * 64 + lane;
+        const global_u16* dt = (const global_u16*)w.d + (G * nsb + c0 / 4) * 16 + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            qv[t] = load12(qb, (int64_t)t * 768);
+            if (t % 4 == 0) {
+                scv[t / 4] = __builtin_nontemporal_load(st + (t / 4) * 64);
+                dv[t / 4] = __builtin_nontemporal_load(dt + (t / 4) * 16);
+            }
+        }
+    }
+    asm volatile("" ::: "memory");
+    // A cells and exponents of every row (as in q6k_gemv_mfma, at row offset
+    // b NCH CB)
+    uint32_t badm = 0;
+#pragma unroll
+    for (int k = 0; k < QK; ++k) {
+        if (64 * wv + k * NT >= B * NQ) break;
+        const int it = tid + k * NT;
+        const int b = it / NQ, i = it % NQ;
+        float v[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+        uint32_t amax = max(max(__builtin_bit_cast(uint32_t, v[0]) & 0x7fffffffu,
+                                __builtin_bit_cast(uint32_t, v[1]) & 0x7fffffffu),
+                            max(__builtin_bit_cast(uint32_t, v[2]) & 0x7fffffffu,
+                                __builtin_bit_cast(uint32_t, v[3]) & 0x7fffffffu));
+        amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
+        amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
+        const bool fin = amax < 0x7f800000u;
+        if (__builtin_amdgcn_ballot_w64(!fin) != 0) {
+            // rare: a non-finite group converts zeros (its row's outputs are NaN)
+            badm |= fin ? 0u : 1u << b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = fin ? v[e] : 0.0f;
+        }
+        const int e_s = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
+        uint32_t y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = (uint32_t)(int)__builtin_amdgcn_ldexpf(v[e], 30 - e_s) + 0x80808080u;
+        uint32_t wd[4];
+        {
+            const uint32_t t01l = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
+            const uint32_t t01h = __builtin_amdgcn_perm(y[1], y[0], 0x07030602u);
+            const uint32_t t23l = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
+            const uint32_t t23h = __builtin_amdgcn_perm(y[3], y[2], 0x07030602u);
+            wd[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u) ^ 0x80808080u;
+            wd[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u) ^ 0x80808080u;
+            wd[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u) ^ 0x80808080u;
+            wd[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u) ^ 0x80808080u;
+        }
+        const int c = i >> 4, sg = (i >> 2) & 3, qq = i & 3;
+        uint8_t* chunk = lds + (b * NCH + c) * CB;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(chunk + 64 * sg + 16 * j + 4 * qq) = wd[j];
+        if (qq == 0) xe[b][sg][c] = e_s - 32;
+        if ((i & 15) == 0) *reinterpret_cast<uint4*>(chunk + 256) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t wm = 0;
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+        if (__builtin_amdgcn_ballot_w64(((badm >> b) & 1u) != 0) != 0) wm |= 1u << b;
+    if (lane == 0) wbad[wv] = wm;
+    __syncthreads();
+    uint32_t bad = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) bad |= wbad[k];
+
+    const int m = lane & 15, g = lane >> 4;
+    const int aoff = CB * c0 + ((m >> 2) == g ? 16 * m : 256);
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    int4 e4[B];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (t % 4 == 0) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) e4[b] = *reinterpret_cast<const int4*>(&xe[b][g][c0 + t]);
+        }
+        const uint32_t n0 = qv[t].a, n1 = qv[t].b, hw = qv[t].c;
+        const i32x4 Bop = {(int)(((n0 << 2) & 0x3C3C3C3Cu) | ((hw << 6) & 0xC0C0C0C0u)),
+                           (int)(((n0 >> 2) & 0x3C3C3C3Cu) | ((hw << 4) & 0xC0C0C0C0u)),
+                           (int)(((n1 << 2) & 0x3C3C3C3Cu) | ((hw << 2) & 0xC0C0C0C0u)),
+                           (int)(((n1 >> 2) & 0x3C3C3C3Cu) | (hw & 0xC0C0C0C0u))};
+        const float dsc = fp16_bits_to_f32(dv[t / 4]) * (float)(int8_t)((scv[t / 4] >> (8 * (t % 4))) & 0xffu);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const i32x4 A = *reinterpret_cast<const i32x4*>(lds + b * NCH * CB + aoff + CB * t);
+            const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bop, i32x4{0, 0, 0, 0}, 0, 0, 0);
+            const float u = __builtin_fmaf((float)(D[3] * 256 + D[2]), 65536.0f, (float)(D[1] * 256 + D[0]));
+            const int eb = (t % 4) == 0 ? e4[b].x : (t % 4) == 1 ? e4[b].y : (t % 4) == 2 ? e4[b].z : e4[b].w;
+            acc[b] = __builtin_fmaf(dsc, __builtin_amdgcn_ldexpf(u, eb), acc[b]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        acc[b] += __shfl_xor(acc[b], 16, 64);
+        acc[b] += __shfl_xor(acc[b], 32, 64);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) red[rg][kw][b][lane] = acc[b];
+    }
+    __syncthreads();
+    if (kw != 0) return;
+    const int64_t row = Gw * 16 + lane;
+    if (lane < 16 && Gw < groups && row < n_out) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (b >= batch) break;
+            float sm = red[rg][0][b][lane];
+#pragma unroll
+            for (int k = 1; k < KS; ++k) sm += red[rg][k][b][lane];
+            out[(int64_t)b * n_out + row] = (bad >> b) & 1u ? __builtin_nanf("") : sm;
+        }
+    }
+}
+
 // K split: n_in = 64 KS T, T = 8, 12 or 16 chunks a wave: 1024 on 2 waves,
 // 2048 .. 4096 on 4, 6144 and 8192 on 8.
 bool q6k_mfma_shape(int64_t n_in, int* ks, int* t)
@@ -559,6 +737,40 @@ template <int KS, int T>
 KernelFnT6 q6k_mfma_pick(int rg)
 {
     return rg == 2 ? q6k_gemv_mfma<KS, T, 2> : q6k_gemv_mfma<KS, T, 1>;
+}
+
+using KernelFnR6 = void (*)(Q6KTView, const float*, int64_t, int64_t, int, float*);
+
+// Rows rounded up to 2, 4 or 8, within B n_in <= 24576.
+int q6k_rows_b(int64_t n_in, int64_t batch)
+{
+    const int b = batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
+    return b * n_in <= 24576 ? b : 0;
+}
+
+template <int KS, int T>
+KernelFnR6 q6k_rows_pick_b(int b)
+{
+    if constexpr (8 * 64 * KS * T <= 24576) {
+        if (b == 8) return q6k_gemv_mfma_rows<8, KS, T>;
+    }
+    if constexpr (4 * 64 * KS * T <= 24576) {
+        if (b == 4) return q6k_gemv_mfma_rows<4, KS, T>;
+    }
+    return b == 2 ? q6k_gemv_mfma_rows<2, KS, T> : nullptr;
+}
+
+KernelFnR6 q6k_rows_pick(int ks, int t, int b)
+{
+    switch (ks * 100 + t) {
+        case 208: return q6k_rows_pick_b<2, 8>(b);
+        case 408: return q6k_rows_pick_b<4, 8>(b);
+        case 412: return q6k_rows_pick_b<4, 12>(b);
+        case 416: return q6k_rows_pick_b<4, 16>(b);
+        case 812: return q6k_rows_pick_b<8, 12>(b);
+        case 816: return q6k_rows_pick_b<8, 16>(b);
+        default: return nullptr;
+    }
 }
 
 using KernelFn = void (*)(Q6KArgs);
@@ -659,16 +871,18 @@ hipError_t launch_repack_q6k_tiled(const uint8_t* raw, int64_t n_in, int64_t n_o
 bool q6k_mfma_supported(int64_t n_in, int64_t batch)
 {
     int ks = 0, t = 0;
-    return batch == 1 && q6k_mfma_shape(n_in, &ks, &t);
+    if (batch < 1 || batch > 8 || !q6k_mfma_shape(n_in, &ks, &t)) return false;
+    return batch == 1 || q6k_rows_b(n_in, batch) > 0;
 }
 
-std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out)
+std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch)
 {
     int ks = 0, t = 0;
     if (!q6k_mfma_shape(n_in, &ks, &t)) return "q6k matrix-core GEMV: unsupported width " + std::to_string(n_in);
     if (64LL * ks * t != n_in) return "q6k matrix-core GEMV: K split does not cover the row";
+    if (batch > 1 && !q6k_rows_b(n_in, batch)) return "q6k matrix-core GEMV: batch rows x width beyond LDS";
     const int64_t groups = q6kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
-    const int rg = q6k_mfma_rg(groups, ks);
+    const int rg = batch > 1 ? 2 : q6k_mfma_rg(groups, ks);
     const int64_t grid = (groups + rg - 1) / rg;
     if (grid <= 0 || grid > 0x7fffffffLL) return "q6k matrix-core GEMV: grid out of range";
     // the last wave reads row group min(grid rg - 1, groups - 1), chunks up to
@@ -680,19 +894,29 @@ std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out)
     const int64_t g = groups;
     if (q_end > g * nch * 768 || sc_end > g * nsb * 256 || d_end > g * nsb * 32)
         return "q6k matrix-core GEMV: a weight read runs past the tiled copy";
-    // x: quads tid + k NT below n / 4; out: rows below n_out (checked in the kernel)
-    const int64_t nt = 64LL * ks * rg, nq = n_in / 4;
-    if (nq % 64 != 0 || (nq + nt - 1) / nt > 4) return "q6k matrix-core GEMV: x quads do not fit the threads";
+    // x: quads tid + k NT below B n / 4, rows past the batch reading its last
+    // row; out: rows below n_out and batch rows below batch (in the kernel)
+    const int64_t nt = 64LL * ks * rg, nq = n_in / 4, bp = batch > 1 ? q6k_rows_b(n_in, batch) : 1;
+    if (nq % 64 != 0 || (bp * nq + nt - 1) / nt > (batch > 1 ? 12 : 4))
+        return "q6k matrix-core GEMV: x quads do not fit the threads";
     return "";
 }
 
-hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
                                 hipStream_t s)
 {
     int ks = 0, t = 0;
-    if (!q6k_mfma_shape(n_in, &ks, &t) || !q6k_mfma_plan_check(n_in, n_out).empty())
+    if (!q6k_mfma_shape(n_in, &ks, &t) || !q6k_mfma_plan_check(n_in, n_out, batch).empty())
         return hipErrorInvalidConfiguration;
     const int64_t groups = q6kt_groups(n_out);
+    if (batch > 1) {
+        const KernelFnR6 fr = q6k_rows_pick(ks, t, q6k_rows_b(n_in, batch));
+        if (!fr) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(fr, dim3((unsigned)((groups + 1) / 2)), dim3(128 * ks), 0, s, w, x, n_in, n_out, (int)batch,
+                           out);
+        count_launch();
+        return hipGetLastError();
+    }
     const int rg = q6k_mfma_rg(groups, ks);
     KernelFnT6 fn = ks == 2 ? q6k_mfma_pick<2, 8>(rg)
                   : ks == 4 ? (t == 8 ? q6k_mfma_pick<4, 8>(rg) : t == 12 ? q6k_mfma_pick<4, 12>(rg)

@@ -280,12 +280,13 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
 bool q4k_mfma_supported(int64_t n_in, int64_t batch);
 hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
                                 hipStream_t s);
-// The same for Q6_K (n_in one of 1024, 2048, 3072, 4096, 6144, 8192), with a
-// host-side extent check of its plan ("" when every access stays inside the
-// tiled copy, x and out; the launcher refuses any other plan).
+// The same for Q6_K (n_in one of 1024, 2048, 3072, 4096, 6144, 8192; also
+// 2..8 batch rows while the rows x width fit LDS), with a host-side extent
+// check of its plan ("" when every access stays inside the tiled copy, x and
+// out; the launcher refuses any other plan).
 bool q6k_mfma_supported(int64_t n_in, int64_t batch);
-std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out);
-hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch);
+hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
                                 hipStream_t s);
 
 // Batched GEMM over a Q8_0 copy.  With a workspace of q8_gemm_workspace_bytes,

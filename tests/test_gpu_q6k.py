@@ -192,3 +192,57 @@ def test_capture_before_the_tiled_copy_uses_the_valu_kernel(qd):
     # outside a capture the tiled copy is made, and the result agrees too
     direct = host(qd.q6k_gemv(w, n_in, n_out, xd))
     check_f32(direct, ref, S, "q6k one row after the capture")
+
+
+# 2..8 batch rows take the integer matrix cores while the rows x width fit a
+# workgroup's LDS (rows rounded up to 2, 4 or 8; 8 rows up to 3072 columns,
+# 4 up to 6144, 2 up to 8192); wider products take the VALU kernel.
+@pytest.mark.parametrize("n_in,batch", [(1024, 2), (1024, 8), (2048, 3), (2048, 7), (3072, 5), (3072, 8),
+                                        (4096, 4), (6144, 2), (6144, 4), (8192, 2), (4096, 6), (8192, 3)])
+def test_rows_matrix_core(qd, n_in, batch):
+    n_out = 45   # ragged: 3 groups of 16, the last partly padding; a spare group in the last workgroup
+    raw = synth.q6k_weights(9700 + n_in + batch, n_out, n_in)
+    x = synth.normal_f32(9701 + batch, (batch, n_in))
+    w = dev(raw)
+    qd.prepare(w, qd.TYPE_Q6_K, n_in, n_out)
+    torch.cuda.synchronize()
+    before = qd.launch_count()
+    out = host(qd.q6k_gemv(w, n_in, n_out, dev(x)))
+    assert qd.launch_count() - before == 1
+    ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q6k rows {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("kind", ["outliers", "spread", "zeros", "tiny", "huge"])
+def test_rows_matrix_core_inputs(qd, kind):
+    n_out, n_in, batch = 37, 3072, 8
+    raw = synth.q6k_weights(9710, n_out, n_in)
+    x = np.concatenate([_x_kind(kind, 9711 + b, n_in) for b in range(batch)])
+    out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q6k rows {kind}")
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_rows_non_finite_row(qd, bad):
+    n_out, n_in, batch = 40, 2048, 6
+    raw = synth.q6k_weights(9720, n_out, n_in)
+    x = synth.normal_f32(9721, (batch, n_in))
+    x[3, 500] = bad
+    out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
+    assert np.all(np.isnan(out[3]))
+    keep = [b for b in range(batch) if b != 3]
+    ref, S = oracle.q6k_gemv(raw, n_in, n_out, x[keep])
+    check_f32(out[keep], ref, S, "rows without a non-finite x")
+
+
+def test_rows_output_projection(qd):
+    """The output tensor's shape at 4 and 8 batch rows (a batched decode step)."""
+    n_out, n_in = 128256, 3072
+    raw = synth.q6k_weights(9730, n_out, n_in)
+    w = dev(raw)
+    for batch in (4, 8):
+        x = synth.normal_f32(9731 + batch, (batch, n_in))
+        out = host(qd.q6k_gemv(w, n_in, n_out, dev(x)))
+        ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+        check_f32(out, ref, S, f"q6k 128256x3072 b{batch}")
