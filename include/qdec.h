@@ -266,15 +266,17 @@ QDEC_API int qdec_attention_decode(const float* q, const float* k_cache, const f
                           int64_t max_seq, float scale, float* out, hipStream_t stream);
 
 /* Q4_K dequant-GEMV ([cuda_lane] try_q4k_soa_gemv): as q8_0_gemv over Q4_K
- * weights; n_in % 256 == 0, 1 <= batch <= 8.  One batch row with n_in one of
- * 1024, 2048, 3072, 4096, 6144, 8192 runs on the integer matrix cores from a
- * second, fragment-tiled copy of the weight (made on first use and by
- * qdec_prepare, the same 148 bytes per 256 weights; a graph captured before
- * that copy exists runs the vector kernel instead).  That path takes x as a
+ * weights; n_in % 256 == 0, 1 <= batch <= 8.  With n_in one of 1024, 2048,
+ * 3072, 4096, 6144, 8192 (batch <= 4 at 6144 and 8192) the product runs on the
+ * integer matrix cores from a second, fragment-tiled copy of the weight (made
+ * on first use and by qdec_prepare, the same 148 bytes per 256 weights; a
+ * graph captured before that copy exists runs the vector kernel instead).
+ * That path takes x as a
  * 30-bit fixed-point number per 32 values: a value below 2^-6 of its group's
  * largest |x| keeps its bits down to 2^-29 of that largest value only, which
  * adds at most 2^-29 max|x| sum_k |d sc q_k| per output; a NaN or infinity in
- * x makes the outputs NaN or infinite. */
+ * x makes the outputs NaN or infinite (with 2..8 batch rows: every output of
+ * that batch row NaN). */
 QDEC_API int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
              const float* x, float* out, hipStream_t stream);
 

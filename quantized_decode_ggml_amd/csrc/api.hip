@@ -703,7 +703,8 @@ int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch, const fl
         // one row on the matrix cores, from the fragment-tiled copy; inside a
         // capture that copy may be missing, and the VALU kernel then runs
         QDEC_TRY(repacked(w, kTypeQ4KTiled, n_in, n_out, stream, &buf, false, true));
-        if (buf) return finish(launch_q4k_gemv_mfma(q4kt_view(buf, n_in, n_out), n_in, n_out, x, out, stream), fn);
+        if (buf)
+            return finish(launch_q4k_gemv_mfma(q4kt_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
     }
     QDEC_TRY(repacked(w, QDEC_TYPE_Q4_K, n_in, n_out, stream, &buf));
     return finish(launch_q4k_gemv(q4k_view(buf, n_in, n_out), n_in, n_out, batch, x, out, stream), fn);
@@ -826,8 +827,14 @@ int qdec_check_plans(int64_t n_in, int64_t n_out, int64_t batch)
             if (!why.empty()) return bad(why);
         }
     }
-    // the Q6_K matrix-core GEMV (widths that are multiples of 256), one row
-    // and this batch
+    // the Q4_K and Q6_K matrix-core GEMVs (widths that are multiples of 256),
+    // one row and this batch
+    if (n_in % 256 == 0 && q4k_mfma_supported(n_in, 1)) {
+        std::string why = q4k_mfma_plan_check(n_in, n_out, 1);
+        if (why.empty() && batch > 1 && batch <= QDEC_GEMV_MAX_BATCH && q4k_mfma_supported(n_in, batch))
+            why = q4k_mfma_plan_check(n_in, n_out, batch);
+        if (!why.empty()) return bad(why);
+    }
     if (n_in % 256 == 0 && q6k_mfma_supported(n_in, 1)) {
         std::string why = q6k_mfma_plan_check(n_in, n_out, 1);
         if (why.empty() && batch > 1 && batch <= QDEC_GEMV_MAX_BATCH && q6k_mfma_supported(n_in, batch))

@@ -27,6 +27,8 @@
 // columns, so it is formed once per wave when x stays in registers.
 #include "qdec_internal.h"
 
+#include <algorithm>
+
 namespace qdec {
 
 namespace {
@@ -683,18 +685,296 @@ KernelFnT q4k_mfma_pick(int rg)
     return rg == 2 ? q4k_gemv_mfma<KS, T, 2> : q4k_gemv_mfma<KS, T, 1>;
 }
 
+// 2..8 batch rows on the integer matrix cores from the same tiled copy, one
+// v_mfma_i32_16x16x32_i8 per 32-value sub-block and fragment of 4 batch rows:
+// the B operand is the lane's 8 nibble bytes masked to their low (sub-block
+// 2c) or high (2c + 1) nibbles, which are its 8 k-values of that sub-block as
+// they stand; the A operand stacks 4 batch rows x 4 digits of x as a 30-bit
+// fixed-point number per (batch row, sub-block), as the one-row kernel does
+// per sub-block.  Lane n + 16 b' of fragment f receives the four digit sums of
+// batch row 4 f + b' and weight row n, forms u = (256 D3 + D2) 2^16 + (256 D1
+// + D0) and accumulates (d sc) u 2^(e - 30) - (dmin m) sum_k x_k, the sum of
+// the sub-block's 32 values taken once per workgroup in a fixed order.  A
+// workgroup holds the A operands of whole rows (batch x n_in x 4 bytes of
+// LDS, at most 96 KB), RG row groups x KS waves of T chunks of 64 values.
+// The A cells are XOR-swizzled by sub-block inside each 16-lane group (as in
+// the Q8_0 kernel: conflict-free reads, spread writes).  A non-finite x makes
+// every output of its batch row NaN (through its sub-block sum).
+template <int KS, int T, int NV, int RG>
+__global__ __launch_bounds__(64 * KS * RG) void q4k_gemv_rows(Q4KTView w, const float* __restrict__ x, int64_t n_in,
+                                                             int64_t n_out, int batch, float* __restrict__ out)
+{
+    static_assert(KS * RG <= 16 && T % 4 == 0 && NV >= 1 && NV <= 2, "KS * RG waves, T chunks a wave");
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int NCH = KS * T;                 // 64-value chunks of a row
+    constexpr int NB = 2 * NCH;                 // 32-value sub-blocks of a row
+    constexpr int NW = KS * RG;
+    constexpr int NT = 64 * NW;
+    constexpr int XB = NB * NV * 512;           // A fragments
+    constexpr int RB = NW * NV * 64 * 4;        // wave sums, after the products
+    constexpr int LB = XB > RB ? XB : RB;
+    constexpr int IPT = (4 * NV * NB * 4 + NT - 1) / NT;   // x items (8 values) a thread
+    static_assert(IPT <= 8, "x items per thread");
+    __shared__ __attribute__((aligned(16))) char lds[LB];
+    __shared__ __attribute__((aligned(16))) int xe[4 * NV][NB];     // e - 30 per (batch row, sub-block)
+    __shared__ __attribute__((aligned(16))) float xsum[4 * NV][NB]; // sum of the sub-block's x
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = wv / KS, kw = wv % KS;
+    const int64_t groups = q4kt_groups(n_out);
+    const int64_t Gw = (int64_t)blockIdx.x * RG + rg;
+    const int64_t G = Gw < groups ? Gw : groups - 1;     // a spare wave reads the last group
+    const int64_t nsb = n_in >> 8;
+    const int c0 = kw * T;                               // first chunk of this wave
+
+    // x item it = (b, blk, g), g fastest: values 32 blk + 8 g .. +7 of batch row b
+    const int items = batch * NB * 4;
+    float4 xv[IPT][2];
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+        const int it = (int)threadIdx.x + j * NT;
+        if (it < items) {
+            const float4* src = reinterpret_cast<const float4*>(x + (int64_t)(it / (NB * 4)) * n_in) + 2 * (it % (NB * 4));
+            xv[j][0] = src[0];
+            xv[j][1] = src[1];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): x before the weight requests queue up
+    asm volatile("" ::: "memory");
+    // every weight load of this wave: the chunk tiles, their scale words
+    // (row lane % 16) and per super-block d|dmin
+    u32x2 qv[T];
+    uint32_t smv[T], dmv[T / 4];
+    {
+        const u32x2* qt = reinterpret_cast<const u32x2*>(w.q) + (G * NCH + c0) * 64 + lane;
+        const uint32_t* st = w.sm + (G * NCH + c0) * 16 + (lane & 15);
+        const uint32_t* dt = w.dm + (G * nsb + c0 / 4) * 16 + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            qv[t] = __builtin_nontemporal_load(qt + t * 64);
+            smv[t] = __builtin_nontemporal_load(st + t * 16);
+            if (t % 4 == 0) dmv[t / 4] = __builtin_nontemporal_load(dt + (t / 4) * 16);
+        }
+    }
+    asm volatile("" ::: "memory");
+
+    // A fragments: lane (m, g) of fragment (blk, f) reads the 8 bytes at
+    // ((blk NV + f) 64 + 16 g + (m ^ (blk % 16))) * 8 -- digit m % 4 of batch
+    // row 4 f + m / 4 at k = 8 g .. 8 g + 7 of sub-block blk
+    u32x2* xf = reinterpret_cast<u32x2*>(lds);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+        const int it = (int)threadIdx.x + j * NT;
+        if (it < items) {   // the 4 lanes of a sub-block agree
+            const int b = it / (NB * 4), blk = (it >> 2) % NB, g = it & 3;
+            float v[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                          xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+            uint32_t amax = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = max(amax, __builtin_bit_cast(uint32_t, v[e]) & 0x7fffffffu);
+            float sum = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+            // over the sub-block's 4 items (4 consecutive lanes): lane ^ 1, lane ^ 2
+            amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
+            amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
+            const bool fin = amax < 0x7f800000u;
+            if (__builtin_amdgcn_ballot_w64(!fin) != 0) {
+                // rare: a non-finite sub-block converts zeros; its sum (made
+                // NaN below) carries the NaN to every output of the row
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = fin ? v[e] : 0.0f;
+            }
+            // amax = m 2^e with 0.5 <= m < 1, so every |x| < 2^e (e = 0 for zeros)
+            const int ex = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, amax));
+            uint32_t y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (uint32_t)(int)__builtin_amdgcn_ldexpf(v[e], 30 - ex) + 0x80808080u;
+            uint32_t dg[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t t01l = __builtin_amdgcn_perm(y[4 * h + 1], y[4 * h], 0x05010400u);
+                const uint32_t t01h = __builtin_amdgcn_perm(y[4 * h + 1], y[4 * h], 0x07030602u);
+                const uint32_t t23l = __builtin_amdgcn_perm(y[4 * h + 3], y[4 * h + 2], 0x05010400u);
+                const uint32_t t23h = __builtin_amdgcn_perm(y[4 * h + 3], y[4 * h + 2], 0x07030602u);
+                dg[h][0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u) ^ 0x80808080u;
+                dg[h][1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u) ^ 0x80808080u;
+                dg[h][2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u) ^ 0x80808080u;
+                dg[h][3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u) ^ 0x80808080u;
+            }
+            u32x2* frag = xf + (blk * NV + (b >> 2)) * 64 + 16 * g;
+#pragma unroll
+            for (int dj = 0; dj < 4; ++dj) frag[(4 * (b & 3) + dj) ^ (blk & 15)] = u32x2{dg[0][dj], dg[1][dj]};
+            if (g == 0) {
+                xe[b][blk] = ex - 30;
+                xsum[b][blk] = fin ? sum : __builtin_nanf("");
+            }
+        }
+    }
+    __syncthreads();   // LDS only: the weight loads stay in flight
+
+    // lane (n = lane % 16, b' = lane / 16) of fragment f: batch row 4 f + b';
+    // sub-block blk = 2 (c0 + t) + h
+    const int b4 = lane >> 4;
+    float acc[NV];
+#pragma unroll
+    for (int f = 0; f < NV; ++f) acc[f] = 0.0f;
+    const u32x2* xw = xf + 2 * c0 * NV * 64;
+    int4 e4[NV];
+    float4 s4[NV];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (t % 2 == 0) {
+            // exponents and sums of sub-blocks 2 (c0 + t) .. +3 (t even)
+#pragma unroll
+            for (int f = 0; f < NV; ++f) {
+                e4[f] = *reinterpret_cast<const int4*>(&xe[4 * f + b4][2 * (c0 + t)]);
+                s4[f] = *reinterpret_cast<const float4*>(&xsum[4 * f + b4][2 * (c0 + t)]);
+            }
+        }
+        const uint32_t dm = dmv[t / 4];
+        const float d = fp16_bits_to_f32((uint16_t)(dm & 0xffff));
+        const float dmin = fp16_bits_to_f32((uint16_t)(dm >> 16));
+        const uint32_t smw = smv[t];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int lb = 2 * t + h;   // sub-block within the wave's range
+            const float dsc = d * (float)((smw >> (8 * h)) & 0xffu);
+            const float dmm = dmin * (float)((smw >> (16 + 8 * h)) & 0xffu);
+            const u32x2 Bq = {(h ? (qv[t][0] >> 4) : qv[t][0]) & 0x0f0f0f0fu, (h ? (qv[t][1] >> 4) : qv[t][1]) & 0x0f0f0f0fu};
+            const int sl = lane ^ ((2 * (c0 + t) + h) & 15);
+#pragma unroll
+            for (int f = 0; f < NV; ++f) {
+                const u32x2 A = xw[(lb * NV + f) * 64 + sl];
+                const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, A),
+                                                                      __builtin_bit_cast(long, Bq),
+                                                                      i32x4{0, 0, 0, 0}, 0, 0, 0);
+                const float u = __builtin_fmaf((float)(D[3] * 256 + D[2]), 65536.0f, (float)(D[1] * 256 + D[0]));
+                const int q2 = (t % 2) * 2 + h;   // position of sub-block lb in the 4 read above
+                const int eb = q2 == 0 ? e4[f].x : q2 == 1 ? e4[f].y : q2 == 2 ? e4[f].z : e4[f].w;
+                const float sx = q2 == 0 ? s4[f].x : q2 == 1 ? s4[f].y : q2 == 2 ? s4[f].z : s4[f].w;
+                acc[f] = __builtin_fmaf(dsc, __builtin_amdgcn_ldexpf(u, eb), acc[f]);
+                acc[f] = __builtin_fmaf(-dmm, sx, acc[f]);
+            }
+        }
+    }
+
+    // the KS wave sums of each output in wave order, then the store
+    __syncthreads();   // every wave is done with the A fragments
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int f = 0; f < NV; ++f) red[(wv * NV + f) * 64 + lane] = acc[f];
+    __syncthreads();
+    if (kw != 0) return;
+    const int64_t row = Gw * 16 + (lane & 15);
+#pragma unroll
+    for (int f = 0; f < NV; ++f) {
+        float sm = red[((rg * KS) * NV + f) * 64 + lane];
+#pragma unroll
+        for (int k = 1; k < KS; ++k) sm += red[((rg * KS + k) * NV + f) * 64 + lane];
+        const int b = 4 * f + b4;
+        if (b < batch && Gw < groups && row < n_out) out[(int64_t)b * n_out + row] = sm;
+    }
+}
+
+// Shapes of the rows kernel: n_in = 64 KS T with T = 8 chunks a wave; whole
+// rows of up to 8 batch rows to 4096 columns (6144 and 8192 up to 4 rows).
+bool q4k_rows_shape(int64_t n_in, int64_t batch, int* ks)
+{
+    switch (n_in) {
+        case 1024: *ks = 2; return true;
+        case 2048: *ks = 4; return true;
+        case 3072: *ks = 6; return true;
+        case 4096: *ks = 8; return true;
+        case 6144: *ks = 12; return batch <= 4;
+        case 8192: *ks = 16; return batch <= 4;
+        default: return false;
+    }
+}
+
+int q4k_rows_rg(int64_t groups, int ks) { return groups >= 512 && ks <= 6 ? 2 : 1; }
+
+using KernelFnR4 = void (*)(Q4KTView, const float*, int64_t, int64_t, int, float*);
+
+template <int KS>
+KernelFnR4 q4k_rows_pick_nv(int nv, int rg)
+{
+    if constexpr (KS <= 6) {
+        if (rg == 2) return nv == 1 ? q4k_gemv_rows<KS, 8, 1, 2> : q4k_gemv_rows<KS, 8, 2, 2>;
+    }
+    if constexpr (KS <= 8) return nv == 1 ? q4k_gemv_rows<KS, 8, 1, 1> : q4k_gemv_rows<KS, 8, 2, 1>;
+    return nv == 1 ? q4k_gemv_rows<KS, 8, 1, 1> : nullptr;
+}
+
+KernelFnR4 q4k_rows_pick(int ks, int nv, int rg)
+{
+    switch (ks) {
+        case 2: return q4k_rows_pick_nv<2>(nv, rg);
+        case 4: return q4k_rows_pick_nv<4>(nv, rg);
+        case 6: return q4k_rows_pick_nv<6>(nv, rg);
+        case 8: return q4k_rows_pick_nv<8>(nv, rg);
+        case 12: return q4k_rows_pick_nv<12>(nv, rg);
+        case 16: return q4k_rows_pick_nv<16>(nv, rg);
+        default: return nullptr;
+    }
+}
+
 }  // namespace
 
 bool q4k_mfma_supported(int64_t n_in, int64_t batch)
 {
     int ks = 0, t = 0;
-    return batch == 1 && q4k_mfma_shape(n_in, &ks, &t);
+    if (batch == 1) return q4k_mfma_shape(n_in, &ks, &t);
+    return batch >= 2 && batch <= 8 && q4k_rows_shape(n_in, batch, &ks);
 }
 
-hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+std::string q4k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch)
+{
+    int ks = 0, t = 0;
+    const int64_t groups = q4kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
+    int64_t grid = 0, rg = 1, tt = 0;
+    if (batch == 1) {
+        if (!q4k_mfma_shape(n_in, &ks, &t) || 64LL * ks * t != n_in) return "q4k matrix-core GEMV: unsupported width";
+        rg = groups >= 512 ? 2 : 1;
+        tt = t;
+    } else {
+        if (!q4k_rows_shape(n_in, batch, &ks) || 64LL * ks * 8 != n_in) return "q4k rows GEMV: unsupported shape";
+        rg = q4k_rows_rg(groups, ks);
+        tt = 8;
+        const int64_t nv = (batch + 3) / 4, nb = 2 * nch;
+        if (nb * nv * 512 + 2 * 4 * nv * nb * 4 > 160 * 1024) return "q4k rows GEMV: LDS";
+        // x: items (b, blk, g) below batch nb 4 read floats b n_in + 32 blk + 8 g .. +7
+        if ((int64_t)(4 * nv * nb * 4 + 64 * ks * rg - 1) / (64 * ks * rg) > 8) return "q4k rows GEMV: x items per thread";
+    }
+    grid = (groups + rg - 1) / rg;
+    if (grid <= 0 || grid > 0x7fffffffLL) return "q4k matrix-core GEMV: grid out of range";
+    const int64_t g_last = std::min<int64_t>(grid * rg - 1, groups - 1);
+    const int64_t q_end = ((g_last * nch + (int64_t)(ks - 1) * tt + tt - 1) * 64 + 63) * 8 + 8;
+    const int64_t sm_end = ((g_last * nch + (int64_t)(ks - 1) * tt + tt - 1) * 16 + 15) * 4 + 4;
+    const int64_t dm_end = ((g_last * nsb + nsb - 1) * 16 + 15) * 4 + 4;
+    if (q_end > groups * nch * 512 || sm_end > groups * nch * 64 || dm_end > groups * nsb * 64)
+        return "q4k matrix-core GEMV: a weight read runs past the tiled copy";
+    return "";
+}
+
+hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
                                 hipStream_t s)
 {
     int ks = 0, t = 0;
+    if (!q4k_mfma_plan_check(n_in, n_out, batch).empty()) return hipErrorInvalidConfiguration;
+    if (batch > 1) {
+        if (!q4k_rows_shape(n_in, batch, &ks)) return hipErrorNotSupported;
+        const int64_t groups = q4kt_groups(n_out);
+        const int rg = q4k_rows_rg(groups, ks), nv = (int)((batch + 3) / 4);
+        const KernelFnR4 fr = q4k_rows_pick(ks, nv, rg);
+        if (!fr) return hipErrorNotSupported;
+        hipLaunchKernelGGL(fr, dim3((unsigned)((groups + rg - 1) / rg)), dim3(64 * ks * rg), 0, s, w, x, n_in, n_out,
+                           (int)batch, out);
+        count_launch();
+        return hipGetLastError();
+    }
     if (!q4k_mfma_shape(n_in, &ks, &t)) return hipErrorNotSupported;
     const int64_t groups = q4kt_groups(n_out);
     const int rg = groups >= 512 ? 2 : 1;

@@ -277,8 +277,12 @@ hipError_t launch_q4k_gemv(Q4KView w, int64_t n_in, int64_t n_out, int64_t batch
 // One batch row on the integer matrix cores from the tiled copy (n_in one of
 // 1024, 2048, 3072, 4096, 6144, 8192); q4k_mfma_supported says whether it
 // takes the shape.
+// 2..8 batch rows run the rows kernel on the same copy (whole rows up to 4096
+// columns; 6144 and 8192 up to 4 rows).  q4k_mfma_plan_check: host-side
+// extent check of either plan ("" when every access stays inside).
 bool q4k_mfma_supported(int64_t n_in, int64_t batch);
-hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, const float* x, float* out,
+std::string q4k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch);
+hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, int64_t batch, const float* x, float* out,
                                 hipStream_t s);
 // The same for Q6_K (n_in one of 1024, 2048, 3072, 4096, 6144, 8192; also
 // 2..8 batch rows while the rows x width fit LDS), with a host-side extent

@@ -553,3 +553,44 @@ def test_qdec_log_lines(tmp_path):
     assert "type=q8_0_tiled" in "".join(lines)
     assert kinds.count("workspace") == 1, lines       # the K slices' sums of the 6-row product
     assert kinds.count("release") == 2 and kinds[-1] == "clear_cache", lines
+
+
+# 2..8 batch rows of Q4_K on the integer matrix cores (whole rows up to 4096
+# columns, 6144 and 8192 up to 4 rows), from the one-row kernel's tiled copy.
+@pytest.mark.parametrize("n_in,batch", [(1024, 2), (1024, 8), (2048, 3), (2048, 7), (3072, 4), (3072, 8),
+                                        (4096, 5), (6144, 2), (6144, 4), (8192, 3), (8192, 6)])
+def test_q4k_rows_matrix_core(qd, n_in, batch):
+    n_out = 45   # ragged: the last 16-row group partly padding
+    raw = synth.q4k_weights(6300 + n_in + batch, n_out, n_in)
+    x = synth.normal_f32(6301 + batch, (batch, n_in))
+    w = dev(raw)
+    qd.prepare(w, qd.TYPE_Q4_K, n_in, n_out)
+    torch.cuda.synchronize()
+    before = qd.launch_count()
+    out = host(qd.q4k_gemv(w, n_in, n_out, dev(x)))
+    assert qd.launch_count() - before == 1
+    ref, S = oracle.q4k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q4k rows {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("kind", ["outliers", "spread", "zeros", "tiny", "huge"])
+@pytest.mark.parametrize("n_out,n_in,batch", [(37, 3072, 8), (8197, 2048, 5)])
+def test_q4k_rows_matrix_core_inputs(qd, kind, n_out, n_in, batch):
+    raw = synth.q4k_weights(6310 + n_out, n_out, n_in)
+    x = np.concatenate([_x_kind(kind, 6311 + b, n_in) for b in range(batch)])
+    out = host(qd.q4k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q4k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q4k rows {kind} {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_q4k_rows_non_finite_row(qd, bad):
+    n_out, n_in, batch = 40, 3072, 6
+    raw = synth.q4k_weights(6320, n_out, n_in)
+    x = synth.normal_f32(6321, (batch, n_in))
+    x[4, 1000] = bad
+    out = host(qd.q4k_gemv(dev(raw), n_in, n_out, dev(x)))
+    assert np.all(np.isnan(out[4]))
+    keep = [b for b in range(batch) if b != 4]
+    ref, S = oracle.q4k_gemv(raw, n_in, n_out, x[keep])
+    check_f32(out[keep], ref, S, "q4k rows without a non-finite x")
