@@ -474,6 +474,11 @@ def suite(args):
         x4, o4 = xdev(synth.seed(4, 2), (1, n_in)), torch.empty((1, n_out), device=dev)
         timed(f"c4 q4k_gemv {n_out}x{n_in} b1", [lambda w=w: qd.q4k_gemv(w, n_in, n_out, x4, out=o4) for w in ws],
               nb4 + n_in * 4 + n_out * 4)
+        for bt in (2, 4, 8):   # several batch rows: the integer matrix-core kernel
+            xb, ob = xdev(synth.seed(4, 10 + bt), (bt, n_in)), torch.empty((bt, n_out), device=dev)
+            timed(f"c4 q4k_gemv {n_out}x{n_in} b{bt}",
+                  [lambda w=w, xb=xb, ob=ob: qd.q4k_gemv(w, n_in, n_out, xb, out=ob) for w in ws],
+                  nb4 + bt * (n_in + n_out) * 4)
         del ws, raw
     # Q6_K (next-row f3): the FFN shapes and the output-projection shape
     for n_out, n_in in ((8192, 3072), (3072, 8192), (128256, 3072)):
@@ -487,6 +492,11 @@ def suite(args):
         x6, o6 = xdev(synth.seed(6, 50), (1, n_in)), torch.empty((1, n_out), device=dev)
         timed(f"f3 q6k_gemv {n_out}x{n_in} b1", [lambda w=w: qd.q6k_gemv(w, n_in, n_out, x6, out=o6) for w in ws],
               nb6 + n_in * 4 + n_out * 4, iters=40 if n_out > 100000 else 100)
+        for bt in (2, 4, 8):
+            xb, ob = xdev(synth.seed(6, 60 + bt), (bt, n_in)), torch.empty((bt, n_out), device=dev)
+            timed(f"f3 q6k_gemv {n_out}x{n_in} b{bt}",
+                  [lambda w=w, xb=xb, ob=ob: qd.q6k_gemv(w, n_in, n_out, xb, out=ob) for w in ws],
+                  nb6 + bt * (n_in + n_out) * 4, iters=40 if n_out > 100000 else 100)
         del ws, raw
     wvoc = q8_dev(4, 3, 128256, 3072, 2)
     xv, ov = xdev(synth.seed(4, 4), (1, 3072)), torch.empty((1, 128256), device=dev)

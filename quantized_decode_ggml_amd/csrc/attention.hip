@@ -323,12 +323,16 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const float* __restrict
 // Merge of the chunk partials of one query head (log-sum-exp): the chunk
 // maxima and sums are read in parallel (one chunk per thread, strided), each
 // chunk's weight exp(m_c - m) and weighted sum l_c exp(m_c - m) kept in LDS,
-// then each thread sums its column over the chunks.  (A variant
+// then each thread sums its column over the chunks in chunk order.  The
+// column values of the first PF chunks (PF <= nchunks, chosen by the
+// launcher) are loaded together with the maxima, before the maximum is known,
+// so up to PF chunks cost one memory round trip instead of three (maxima;
+// maxima and sums again; columns).  (A variant
 // with 256 threads splitting the chunks four ways and an exp per chunk and
 // thread measured slower, and so did a one-pass merge with a running maximum
 // (two exponentials per chunk in one dependent chain per thread: 26 -> 42 us
 // at 64 chunks).)
-template <int D>
+template <int D, int PF>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int64_t nchunks, int group,
                                                          float* __restrict__ out)
 {
@@ -339,8 +343,17 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     const int64_t kv = h / group, g = h % group;
     const int j = threadIdx.x;
     auto at = [&](int64_t c) { return part + ((kv * nchunks + c) * group + g) * (D + 2); };
-    float m = -INFINITY;
-    for (int64_t c = j; c < nchunks; c += D) m = fmaxf(m, at(c)[0]);
+    float op[PF > 0 ? PF : 1];
+    {
+        const float* p = at(0) + 2 + j;   // per-lane address: a vector pointer step per chunk
+        const int64_t step = (int64_t)group * (D + 2);
+#pragma unroll
+        for (int c = 0; c < PF; ++c, p += step) op[c] = *p;
+    }
+    // (m, l) of chunk j (8-byte aligned: D + 2 is even)
+    const float2 ml0 = j < nchunks ? *reinterpret_cast<const float2*>(at(j)) : make_float2(-INFINITY, 0.0f);
+    float m = ml0.x;
+    for (int64_t c = j + D; c < nchunks; c += D) m = fmaxf(m, at(c)[0]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     if ((j & 63) == 0) red[j >> 6] = m;
@@ -352,19 +365,34 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     for (int64_t c0 = 0; c0 < nchunks; c0 += 1024) {
         const int64_t cn = nchunks - c0 < 1024 ? nchunks - c0 : 1024;
         __syncthreads();                                   // wsh of the previous block is consumed
-        for (int64_t c = j; c < cn; c += D) {
-            const float* pr = at(c0 + c);
-            const float wv = expf(pr[0] - m);
-            wsh[c] = wv;
-            wl[c] = pr[1] * wv;
+        int64_t cj = j;
+        if (c0 == 0) {   // chunk j: (m, l) already loaded
+            if (j < cn) {
+                const float wv = expf(ml0.x - m);
+                wsh[j] = wv;
+                wl[j] = ml0.y * wv;
+            }
+            cj += D;
+        }
+        for (; cj < cn; cj += D) {
+            const float2 ml = *reinterpret_cast<const float2*>(at(c0 + cj));
+            const float wv = expf(ml.x - m);
+            wsh[cj] = wv;
+            wl[cj] = ml.y * wv;
         }
         __syncthreads();
+        for (int64_t c = 0; c < cn; ++c) l += wl[c];
+        int64_t c = 0;
+        if (c0 == 0) {   // cn >= PF here
+#pragma unroll
+            for (int q = 0; q < PF; ++q) o = __builtin_fmaf(op[q], wsh[q], o);
+            c = PF;
+        }
         // the chunk sums come from LDS, so the loop below issues only the
         // vector loads of o: 16 in flight (8: one more round trip per 8
         // chunks; 32: slower again, measured)
-        for (int64_t c = 0; c < cn; ++c) l += wl[c];
 #pragma unroll 16
-        for (int64_t c = 0; c < cn; ++c) o = __builtin_fmaf(at(c0 + c)[2 + j], wsh[c], o);
+        for (; c < cn; ++c) o = __builtin_fmaf(at(c0 + c)[2 + j], wsh[c], o);
     }
     out[h * D + j] = o / l;
 }
@@ -385,6 +413,21 @@ ChunkFn pick_group(int group)
         case 6: return attn_chunk_kernel<D, FINAL, 6, CH>;
         case 8: return attn_chunk_kernel<D, FINAL, 8, CH>;
         default: return attn_chunk_kernel<D, FINAL, 0, CH>;
+    }
+}
+
+using CombineFn = void (*)(const float*, int64_t, int, float*);
+
+// Combine kernel prefetching the first pf chunks (pf <= nchunks).
+template <int D>
+CombineFn pick_combine(int pf)
+{
+    switch (pf) {
+        case 64: return attn_combine_kernel<D, 64>;
+        case 32: return attn_combine_kernel<D, 32>;
+        case 16: return attn_combine_kernel<D, 16>;
+        case 8: return attn_combine_kernel<D, 8>;
+        default: return attn_combine_kernel<D, 0>;
     }
 }
 
@@ -427,11 +470,9 @@ hipError_t launch_attention(const float* q, const float* k_cache, const float* v
     hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, q, k_cache, v_cache, n_kv, group, n_ctx, max_seq, scale, part, out);
     count_launch();
     if (final) return hipGetLastError();
-    if (d == 64)
-        hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((unsigned)n_head), dim3(64), 0, s, part, nchunks, group, out);
-    else
-        hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((unsigned)n_head), dim3(128), 0, s, part, nchunks, group,
-                           out);
+    const int pf = nchunks >= 64 ? 64 : nchunks >= 32 ? 32 : nchunks >= 16 ? 16 : nchunks >= 8 ? 8 : 0;
+    const CombineFn cf = d == 64 ? pick_combine<64>(pf) : pick_combine<128>(pf);
+    hipLaunchKernelGGL(cf, dim3((unsigned)n_head), dim3((unsigned)d), 0, s, part, nchunks, group, out);
     count_launch();
     return hipGetLastError();
 }
