@@ -267,8 +267,9 @@ QDEC_API int qdec_attention_decode(const float* q, const float* k_cache, const f
 
 /* Q4_K dequant-GEMV ([cuda_lane] try_q4k_soa_gemv): as q8_0_gemv over Q4_K
  * weights; n_in % 256 == 0, 1 <= batch <= 8.  With n_in one of 1024, 2048,
- * 3072, 4096, 6144, 8192 (batch <= 4 at 6144 and 8192) the product runs on the
- * integer matrix cores from a second, fragment-tiled copy of the weight (made
+ * 3072, 4096, 6144, 8192 the product runs on the integer matrix cores (5..8
+ * rows at 6144 and 8192 as two launches of 2..4 rows each; a captured graph
+ * then holds both) from a second, fragment-tiled copy of the weight (made
  * on first use and by qdec_prepare, the same 148 bytes per 256 weights; a
  * graph captured before that copy exists runs the vector kernel instead).
  * That path takes x as a

@@ -923,15 +923,29 @@ KernelFnR4 q4k_rows_pick(int ks, int nv, int rg)
 
 }  // namespace
 
+// 5..8 rows at 6144 and 8192 columns (whose A cells would not fit one
+// workgroup's LDS) run as two launches of (batch + 1) / 2 and the remaining
+// rows, each 2..4 rows, on x and out offset by the first part's rows.
+bool q4k_rows_split(int64_t n_in, int64_t batch)
+{
+    return batch > 4 && batch <= 8 && (n_in == 6144 || n_in == 8192);
+}
+
 bool q4k_mfma_supported(int64_t n_in, int64_t batch)
 {
     int ks = 0, t = 0;
     if (batch == 1) return q4k_mfma_shape(n_in, &ks, &t);
+    if (q4k_rows_split(n_in, batch)) return true;
     return batch >= 2 && batch <= 8 && q4k_rows_shape(n_in, batch, &ks);
 }
 
 std::string q4k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch)
 {
+    if (q4k_rows_split(n_in, batch)) {
+        const int64_t b0 = (batch + 1) / 2;
+        const std::string e = q4k_mfma_plan_check(n_in, n_out, b0);
+        return e.empty() ? q4k_mfma_plan_check(n_in, n_out, batch - b0) : e;
+    }
     int ks = 0, t = 0;
     const int64_t groups = q4kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
     int64_t grid = 0, rg = 1, tt = 0;
@@ -964,6 +978,12 @@ hipError_t launch_q4k_gemv_mfma(Q4KTView w, int64_t n_in, int64_t n_out, int64_t
 {
     int ks = 0, t = 0;
     if (!q4k_mfma_plan_check(n_in, n_out, batch).empty()) return hipErrorInvalidConfiguration;
+    if (q4k_rows_split(n_in, batch)) {
+        const int64_t b0 = (batch + 1) / 2;
+        const hipError_t e = launch_q4k_gemv_mfma(w, n_in, n_out, b0, x, out, s);
+        if (e != hipSuccess) return e;
+        return launch_q4k_gemv_mfma(w, n_in, n_out, batch - b0, x + b0 * n_in, out + b0 * n_out, s);
+    }
     if (batch > 1) {
         if (!q4k_rows_shape(n_in, batch, &ks)) return hipErrorNotSupported;
         const int64_t groups = q4kt_groups(n_out);
