@@ -539,15 +539,16 @@ __global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma(Q6KTView w, const 
 // operand (the unpacked quants) and d sc are formed once and multiplied by
 // every batch row's A cells, one MFMA per row.  The rows' A cells and
 // exponents take B x n_in x 4.25 bytes of LDS (B n_in <= 24576, so 8 rows up
-// to 3072 columns, 4 up to 6144, 2 up to 8192); two row groups a workgroup,
-// each with K over KS waves of T chunks.  B is the batch rounded up to 2, 4
+// to 3072 columns, 4 up to 6144, 2 up to 8192); RG row groups a workgroup
+// (2, or 3-4 for tall matrices, see q6k_rows_rg), each with K over KS waves
+// of T chunks.  B is the batch rounded up to 2, 4
 // or 8: rows past the real batch repeat its last row and are not stored.  A
 // non-finite x makes every output of its batch row NaN.
-template <int B, int KS, int T>
-__global__ __launch_bounds__(128 * KS) void q6k_gemv_mfma_rows(Q6KTView w, const float* __restrict__ x, int64_t n_in,
-                                                                int64_t n_out, int batch, float* __restrict__ out)
+template <int B, int KS, int T, int RG>
+__global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma_rows(Q6KTView w, const float* __restrict__ x,
+                                                                     int64_t n_in, int64_t n_out, int batch,
+                                                                     float* __restrict__ out)
 {
-    constexpr int RG = 2;
     static_assert(T % 4 == 0 && T >= 4 && T <= 16 && KS * RG <= 16, "T chunks per wave, KS * RG waves");
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(1))) const uint16_t global_u16;
@@ -748,27 +749,44 @@ int q6k_rows_b(int64_t n_in, int64_t batch)
     return b * n_in <= 24576 ? b : 0;
 }
 
-template <int KS, int T>
-KernelFnR6 q6k_rows_pick_b(int b)
+// Row groups a workgroup of the multi-row kernel: 3 for 4 and 8 rows of a
+// tall matrix (>= 2048 row groups, so >= 680 workgroups remain), which cuts
+// the x preparation per weight row by a third against 2.  Measured at
+// 128256 x 3072 (graph-replayed): b4 84.2 -> 76.8 us, b8 189 -> 151-153 us;
+// 4 row groups were slower at b4 (93.9) and spill at b8; else 2.
+int q6k_rows_rg(int64_t groups, int ks, int b)
 {
-    if constexpr (8 * 64 * KS * T <= 24576) {
-        if (b == 8) return q6k_gemv_mfma_rows<8, KS, T>;
-    }
-    if constexpr (4 * 64 * KS * T <= 24576) {
-        if (b == 4) return q6k_gemv_mfma_rows<4, KS, T>;
-    }
-    return b == 2 ? q6k_gemv_mfma_rows<2, KS, T> : nullptr;
+    if (ks > 4 || groups < 2048) return 2;
+    return b >= 4 ? 3 : 2;
 }
 
-KernelFnR6 q6k_rows_pick(int ks, int t, int b)
+template <int KS, int T>
+KernelFnR6 q6k_rows_pick_rg(int b, int rg)
+{
+    if constexpr (8 * 64 * KS * T <= 24576) {
+        if constexpr (3 * KS <= 16) {
+            if (b == 8 && rg == 3) return q6k_gemv_mfma_rows<8, KS, T, 3>;
+        }
+        if (b == 8) return rg == 2 ? q6k_gemv_mfma_rows<8, KS, T, 2> : nullptr;
+    }
+    if constexpr (4 * 64 * KS * T <= 24576) {
+        if constexpr (3 * KS <= 16) {
+            if (b == 4 && rg == 3) return q6k_gemv_mfma_rows<4, KS, T, 3>;
+        }
+        if (b == 4) return rg == 2 ? q6k_gemv_mfma_rows<4, KS, T, 2> : nullptr;
+    }
+    return b == 2 ? q6k_gemv_mfma_rows<2, KS, T, 2> : nullptr;
+}
+
+KernelFnR6 q6k_rows_pick(int ks, int t, int b, int rg)
 {
     switch (ks * 100 + t) {
-        case 208: return q6k_rows_pick_b<2, 8>(b);
-        case 408: return q6k_rows_pick_b<4, 8>(b);
-        case 412: return q6k_rows_pick_b<4, 12>(b);
-        case 416: return q6k_rows_pick_b<4, 16>(b);
-        case 812: return q6k_rows_pick_b<8, 12>(b);
-        case 816: return q6k_rows_pick_b<8, 16>(b);
+        case 208: return q6k_rows_pick_rg<2, 8>(b, rg);
+        case 408: return q6k_rows_pick_rg<4, 8>(b, rg);
+        case 412: return q6k_rows_pick_rg<4, 12>(b, rg);
+        case 416: return q6k_rows_pick_rg<4, 16>(b, rg);
+        case 812: return rg == 2 ? q6k_rows_pick_rg<8, 12>(b, 2) : nullptr;
+        case 816: return rg == 2 ? q6k_rows_pick_rg<8, 16>(b, 2) : nullptr;
         default: return nullptr;
     }
 }
@@ -882,7 +900,7 @@ std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch)
     if (64LL * ks * t != n_in) return "q6k matrix-core GEMV: K split does not cover the row";
     if (batch > 1 && !q6k_rows_b(n_in, batch)) return "q6k matrix-core GEMV: batch rows x width beyond LDS";
     const int64_t groups = q6kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
-    const int rg = batch > 1 ? 2 : q6k_mfma_rg(groups, ks);
+    const int rg = batch > 1 ? q6k_rows_rg(groups, ks, q6k_rows_b(n_in, batch)) : q6k_mfma_rg(groups, ks);
     const int64_t grid = (groups + rg - 1) / rg;
     if (grid <= 0 || grid > 0x7fffffffLL) return "q6k matrix-core GEMV: grid out of range";
     // the last wave reads row group min(grid rg - 1, groups - 1), chunks up to
@@ -910,10 +928,11 @@ hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, int64_t
         return hipErrorInvalidConfiguration;
     const int64_t groups = q6kt_groups(n_out);
     if (batch > 1) {
-        const KernelFnR6 fr = q6k_rows_pick(ks, t, q6k_rows_b(n_in, batch));
+        const int b = q6k_rows_b(n_in, batch), rg = q6k_rows_rg(groups, ks, b);
+        const KernelFnR6 fr = q6k_rows_pick(ks, t, b, rg);
         if (!fr) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(fr, dim3((unsigned)((groups + 1) / 2)), dim3(128 * ks), 0, s, w, x, n_in, n_out, (int)batch,
-                           out);
+        hipLaunchKernelGGL(fr, dim3((unsigned)((groups + rg - 1) / rg)), dim3(64 * ks * rg), 0, s, w, x, n_in, n_out,
+                           (int)batch, out);
         count_launch();
         return hipGetLastError();
     }

@@ -246,3 +246,16 @@ def test_rows_output_projection(qd):
         out = host(qd.q6k_gemv(w, n_in, n_out, dev(x)))
         ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
         check_f32(out, ref, S, f"q6k 128256x3072 b{batch}")
+
+
+@pytest.mark.parametrize("n_in,batch", [(3072, 3), (3072, 5), (3072, 8), (2048, 4), (2048, 7), (1024, 8)])
+def test_rows_tall_ragged(qd, n_in, batch):
+    """A tall matrix (2051 row groups, the last one partly padding): 4 rows take
+    four row groups a workgroup and 8 rows three, so the last workgroup holds
+    spare groups."""
+    n_out = 2050 * 16 + 5
+    raw = synth.q6k_weights(9740 + n_in + batch, n_out, n_in)
+    x = synth.normal_f32(9741 + batch, (batch, n_in))
+    out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
+    ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
+    check_f32(out, ref, S, f"q6k {n_out}x{n_in} b{batch}")
