@@ -753,9 +753,13 @@ int q6k_rows_b(int64_t n_in, int64_t batch)
 // tall matrix (>= 2048 row groups, so >= 680 workgroups remain), which cuts
 // the x preparation per weight row by a third against 2.  Measured at
 // 128256 x 3072 (graph-replayed): b4 84.2 -> 76.8 us, b8 189 -> 151-153 us;
-// 4 row groups were slower at b4 (93.9) and spill at b8; else 2.
-int q6k_rows_rg(int64_t groups, int ks, int b)
+// 4 row groups were slower at b4 (93.9) and spill at b8.  Below 512 row
+// groups one (as the one-row kernel), so that a 3072-row matrix still has
+// 192 workgroups, where the x quads still fit the threads (B T / 4 <= 12);
+// else 2.
+int q6k_rows_rg(int64_t groups, int ks, int t, int b)
 {
+    if (groups < 512 && b * t <= 48) return 1;
     if (ks > 4 || groups < 2048) return 2;
     return b >= 4 ? 3 : 2;
 }
@@ -773,9 +777,13 @@ KernelFnR6 q6k_rows_pick_rg(int b, int rg)
         if constexpr (3 * KS <= 16) {
             if (b == 4 && rg == 3) return q6k_gemv_mfma_rows<4, KS, T, 3>;
         }
+        if constexpr (4 * T <= 48) {
+            if (b == 4 && rg == 1) return q6k_gemv_mfma_rows<4, KS, T, 1>;
+        }
         if (b == 4) return rg == 2 ? q6k_gemv_mfma_rows<4, KS, T, 2> : nullptr;
     }
-    return b == 2 ? q6k_gemv_mfma_rows<2, KS, T, 2> : nullptr;
+    if (b != 2) return nullptr;
+    return rg == 2 ? q6k_gemv_mfma_rows<2, KS, T, 2> : rg == 1 ? q6k_gemv_mfma_rows<2, KS, T, 1> : nullptr;
 }
 
 KernelFnR6 q6k_rows_pick(int ks, int t, int b, int rg)
@@ -785,8 +793,8 @@ KernelFnR6 q6k_rows_pick(int ks, int t, int b, int rg)
         case 408: return q6k_rows_pick_rg<4, 8>(b, rg);
         case 412: return q6k_rows_pick_rg<4, 12>(b, rg);
         case 416: return q6k_rows_pick_rg<4, 16>(b, rg);
-        case 812: return rg == 2 ? q6k_rows_pick_rg<8, 12>(b, 2) : nullptr;
-        case 816: return rg == 2 ? q6k_rows_pick_rg<8, 16>(b, 2) : nullptr;
+        case 812: return rg <= 2 ? q6k_rows_pick_rg<8, 12>(b, rg) : nullptr;
+        case 816: return rg <= 2 ? q6k_rows_pick_rg<8, 16>(b, rg) : nullptr;
         default: return nullptr;
     }
 }
@@ -900,7 +908,7 @@ std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch)
     if (64LL * ks * t != n_in) return "q6k matrix-core GEMV: K split does not cover the row";
     if (batch > 1 && !q6k_rows_b(n_in, batch)) return "q6k matrix-core GEMV: batch rows x width beyond LDS";
     const int64_t groups = q6kt_groups(n_out), nch = n_in / 64, nsb = n_in / 256;
-    const int rg = batch > 1 ? q6k_rows_rg(groups, ks, q6k_rows_b(n_in, batch)) : q6k_mfma_rg(groups, ks);
+    const int rg = batch > 1 ? q6k_rows_rg(groups, ks, t, q6k_rows_b(n_in, batch)) : q6k_mfma_rg(groups, ks);
     const int64_t grid = (groups + rg - 1) / rg;
     if (grid <= 0 || grid > 0x7fffffffLL) return "q6k matrix-core GEMV: grid out of range";
     // the last wave reads row group min(grid rg - 1, groups - 1), chunks up to
@@ -928,7 +936,7 @@ hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, int64_t
         return hipErrorInvalidConfiguration;
     const int64_t groups = q6kt_groups(n_out);
     if (batch > 1) {
-        const int b = q6k_rows_b(n_in, batch), rg = q6k_rows_rg(groups, ks, b);
+        const int b = q6k_rows_b(n_in, batch), rg = q6k_rows_rg(groups, ks, t, b);
         const KernelFnR6 fr = q6k_rows_pick(ks, t, b, rg);
         if (!fr) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(fr, dim3((unsigned)((groups + rg - 1) / rg)), dim3(64 * ks * rg), 0, s, w, x, n_in, n_out,
