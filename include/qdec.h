@@ -285,10 +285,10 @@ QDEC_API int q4k_gemv(const void* w, int64_t n_in, int64_t n_out, int64_t batch,
  * that [QTensorEngine] uses for the output and embedding tensors): as
  * q8_0_gemv over Q6_K weights; n_in % 256 == 0, 1 <= batch <= 8.  Products
  * are exact (each weight is an integer times an exact scale), f32 sums.  With
- * n_in one of 1024, 2048, 3072, 4096, 6144, 8192 one batch row, and 2..8
- * rows while the batch (rounded up to 2, 4 or 8) times n_in is at most 24576,
- * run on the integer matrix cores from a second, fragment-tiled copy of the
- * weight (made
+ * n_in one of 1024, 2048, 3072, 4096, 6144, 8192 every batch runs on the
+ * integer matrix cores (one launch while the batch, rounded up to 2, 4 or 8,
+ * times n_in is at most 32768; 5..8 rows at 6144 and 8192 as two launches)
+ * from a second, fragment-tiled copy of the weight (made
  * on first use and by qdec_prepare, 210 bytes per 256 weights; a graph
  * captured before that copy exists runs the vector kernel instead).  That
  * path takes x as a 30-bit fixed-point number per 16 values (one scale

@@ -538,8 +538,8 @@ __global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma(Q6KTView w, const 
 // copy and with the same arithmetic per row as q6k_gemv_mfma: each chunk's B
 // operand (the unpacked quants) and d sc are formed once and multiplied by
 // every batch row's A cells, one MFMA per row.  The rows' A cells and
-// exponents take B x n_in x 4.25 bytes of LDS (B n_in <= 24576, so 8 rows up
-// to 3072 columns, 4 up to 6144, 2 up to 8192); RG row groups a workgroup
+// exponents take B x n_in x 4.25 bytes of LDS (B n_in <= 32768, so 8 rows up
+// to 4096 columns, 4 up to 8192: at most 139 KB); RG row groups a workgroup
 // (2, or 3-4 for tall matrices, see q6k_rows_rg), each with K over KS waves
 // of T chunks.  B is the batch rounded up to 2, 4
 // or 8: rows past the real batch repeat its last row and are not stored.  A
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(64 * KS * RG) void q6k_gemv_mfma_rows(Q6KTView w, c
     constexpr int NQ = n / 4;          // quads of one batch row
     constexpr int QK = (B * NQ + NT - 1) / NT;
     constexpr int CB = 272;            // LDS bytes a chunk and row: 16 A cells, one zero cell
-    static_assert(QK <= 12 && B * n <= 24576, "quads per thread, LDS");
+    static_assert(QK <= 16 && B * n <= 32768, "quads per thread, LDS");
     __shared__ __attribute__((aligned(16))) uint8_t lds[B * CB * NCH];
     __shared__ __attribute__((aligned(16))) int xe[B][4][NCH];   // e_s - 32 of row b, group s, chunk c
     __shared__ uint32_t wbad[NW];
@@ -742,11 +742,19 @@ KernelFnT6 q6k_mfma_pick(int rg)
 
 using KernelFnR6 = void (*)(Q6KTView, const float*, int64_t, int64_t, int, float*);
 
-// Rows rounded up to 2, 4 or 8, within B n_in <= 24576.
+// Rows rounded up to 2, 4 or 8, within B n_in <= 32768.
 int q6k_rows_b(int64_t n_in, int64_t batch)
 {
     const int b = batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
-    return b * n_in <= 24576 ? b : 0;
+    return b * n_in <= 32768 ? b : 0;
+}
+
+// 5..8 rows at 6144 and 8192 columns (beyond one workgroup's LDS) run as two
+// launches of (batch + 1) / 2 and the remaining rows on x and out offset by
+// the first part's rows.
+bool q6k_rows_split(int64_t n_in, int64_t batch)
+{
+    return batch > 4 && batch <= 8 && !q6k_rows_b(n_in, batch) && q6k_rows_b(n_in, 4);
 }
 
 // Row groups a workgroup of the multi-row kernel: 3 for 4 and 8 rows of a
@@ -755,11 +763,11 @@ int q6k_rows_b(int64_t n_in, int64_t batch)
 // 128256 x 3072 (graph-replayed): b4 84.2 -> 76.8 us, b8 189 -> 151-153 us;
 // 4 row groups were slower at b4 (93.9) and spill at b8.  Below 512 row
 // groups one (as the one-row kernel), so that a 3072-row matrix still has
-// 192 workgroups, where the x quads still fit the threads (B T / 4 <= 12);
+// 192 workgroups, where the x quads still fit the threads (B T / 4 <= 16);
 // else 2.
 int q6k_rows_rg(int64_t groups, int ks, int t, int b)
 {
-    if (groups < 512 && b * t <= 48) return 1;
+    if (groups < 512 && b * t <= 64) return 1;
     if (ks > 4 || groups < 2048) return 2;
     return b >= 4 ? 3 : 2;
 }
@@ -767,19 +775,20 @@ int q6k_rows_rg(int64_t groups, int ks, int t, int b)
 template <int KS, int T>
 KernelFnR6 q6k_rows_pick_rg(int b, int rg)
 {
-    if constexpr (8 * 64 * KS * T <= 24576) {
+    if constexpr (8 * 64 * KS * T <= 32768) {
         if constexpr (3 * KS <= 16) {
             if (b == 8 && rg == 3) return q6k_gemv_mfma_rows<8, KS, T, 3>;
         }
+        if constexpr (8 * T <= 64) {
+            if (b == 8 && rg == 1) return q6k_gemv_mfma_rows<8, KS, T, 1>;
+        }
         if (b == 8) return rg == 2 ? q6k_gemv_mfma_rows<8, KS, T, 2> : nullptr;
     }
-    if constexpr (4 * 64 * KS * T <= 24576) {
+    if constexpr (4 * 64 * KS * T <= 32768) {
         if constexpr (3 * KS <= 16) {
             if (b == 4 && rg == 3) return q6k_gemv_mfma_rows<4, KS, T, 3>;
         }
-        if constexpr (4 * T <= 48) {
-            if (b == 4 && rg == 1) return q6k_gemv_mfma_rows<4, KS, T, 1>;
-        }
+        if (b == 4 && rg == 1) return q6k_gemv_mfma_rows<4, KS, T, 1>;
         if (b == 4) return rg == 2 ? q6k_gemv_mfma_rows<4, KS, T, 2> : nullptr;
     }
     if (b != 2) return nullptr;
@@ -898,11 +907,16 @@ bool q6k_mfma_supported(int64_t n_in, int64_t batch)
 {
     int ks = 0, t = 0;
     if (batch < 1 || batch > 8 || !q6k_mfma_shape(n_in, &ks, &t)) return false;
-    return batch == 1 || q6k_rows_b(n_in, batch) > 0;
+    return batch == 1 || q6k_rows_b(n_in, batch) > 0 || q6k_rows_split(n_in, batch);
 }
 
 std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch)
 {
+    if (q6k_rows_split(n_in, batch)) {
+        const int64_t b0 = (batch + 1) / 2;
+        const std::string e = q6k_mfma_plan_check(n_in, n_out, b0);
+        return e.empty() ? q6k_mfma_plan_check(n_in, n_out, batch - b0) : e;
+    }
     int ks = 0, t = 0;
     if (!q6k_mfma_shape(n_in, &ks, &t)) return "q6k matrix-core GEMV: unsupported width " + std::to_string(n_in);
     if (64LL * ks * t != n_in) return "q6k matrix-core GEMV: K split does not cover the row";
@@ -923,7 +937,7 @@ std::string q6k_mfma_plan_check(int64_t n_in, int64_t n_out, int64_t batch)
     // x: quads tid + k NT below B n / 4, rows past the batch reading its last
     // row; out: rows below n_out and batch rows below batch (in the kernel)
     const int64_t nt = 64LL * ks * rg, nq = n_in / 4, bp = batch > 1 ? q6k_rows_b(n_in, batch) : 1;
-    if (nq % 64 != 0 || (bp * nq + nt - 1) / nt > (batch > 1 ? 12 : 4))
+    if (nq % 64 != 0 || (bp * nq + nt - 1) / nt > (batch > 1 ? 16 : 4))
         return "q6k matrix-core GEMV: x quads do not fit the threads";
     return "";
 }
@@ -934,6 +948,12 @@ hipError_t launch_q6k_gemv_mfma(Q6KTView w, int64_t n_in, int64_t n_out, int64_t
     int ks = 0, t = 0;
     if (!q6k_mfma_shape(n_in, &ks, &t) || !q6k_mfma_plan_check(n_in, n_out, batch).empty())
         return hipErrorInvalidConfiguration;
+    if (q6k_rows_split(n_in, batch)) {
+        const int64_t b0 = (batch + 1) / 2;
+        const hipError_t e = launch_q6k_gemv_mfma(w, n_in, n_out, b0, x, out, s);
+        if (e != hipSuccess) return e;
+        return launch_q6k_gemv_mfma(w, n_in, n_out, batch - b0, x + b0 * n_in, out + b0 * n_out, s);
+    }
     const int64_t groups = q6kt_groups(n_out);
     if (batch > 1) {
         const int b = q6k_rows_b(n_in, batch), rg = q6k_rows_rg(groups, ks, t, b);

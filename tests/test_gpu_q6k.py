@@ -194,11 +194,12 @@ def test_capture_before_the_tiled_copy_uses_the_valu_kernel(qd):
     check_f32(direct, ref, S, "q6k one row after the capture")
 
 
-# 2..8 batch rows take the integer matrix cores while the rows x width fit a
-# workgroup's LDS (rows rounded up to 2, 4 or 8; 8 rows up to 3072 columns,
-# 4 up to 6144, 2 up to 8192); wider products take the VALU kernel.
+# 2..8 batch rows take the integer matrix cores in one launch while the rows x
+# width fit a workgroup's LDS (rows rounded up to 2, 4 or 8; 8 rows up to 4096
+# columns, 4 up to 8192); 5..8 rows at 6144 and 8192 take two launches.
 @pytest.mark.parametrize("n_in,batch", [(1024, 2), (1024, 8), (2048, 3), (2048, 7), (3072, 5), (3072, 8),
-                                        (4096, 4), (6144, 2), (6144, 4), (8192, 2), (4096, 6), (8192, 3)])
+                                        (4096, 4), (6144, 2), (6144, 4), (8192, 2), (4096, 6), (8192, 3),
+                                        (4096, 8), (8192, 4), (6144, 5), (6144, 8), (8192, 6), (8192, 8)])
 def test_rows_matrix_core(qd, n_in, batch):
     n_out = 45   # ragged: 3 groups of 16, the last partly padding; a spare group in the last workgroup
     raw = synth.q6k_weights(9700 + n_in + batch, n_out, n_in)
@@ -208,7 +209,7 @@ def test_rows_matrix_core(qd, n_in, batch):
     torch.cuda.synchronize()
     before = qd.launch_count()
     out = host(qd.q6k_gemv(w, n_in, n_out, dev(x)))
-    assert qd.launch_count() - before == 1
+    assert qd.launch_count() - before == (2 if n_in >= 6144 and batch > 4 else 1)
     ref, S = oracle.q6k_gemv(raw, n_in, n_out, x)
     check_f32(out, ref, S, f"q6k rows {n_out}x{n_in} b{batch}")
 
@@ -224,14 +225,15 @@ def test_rows_matrix_core_inputs(qd, kind):
 
 
 @pytest.mark.parametrize("bad", [float("nan"), float("inf")])
-def test_rows_non_finite_row(qd, bad):
-    n_out, n_in, batch = 40, 2048, 6
+@pytest.mark.parametrize("n_in,batch,row", [(2048, 6, 3), (8192, 7, 5)])
+def test_rows_non_finite_row(qd, bad, n_in, batch, row):
+    n_out = 40
     raw = synth.q6k_weights(9720, n_out, n_in)
     x = synth.normal_f32(9721, (batch, n_in))
-    x[3, 500] = bad
+    x[row, 500] = bad
     out = host(qd.q6k_gemv(dev(raw), n_in, n_out, dev(x)))
-    assert np.all(np.isnan(out[3]))
-    keep = [b for b in range(batch) if b != 3]
+    assert np.all(np.isnan(out[row]))
+    keep = [b for b in range(batch) if b != row]
     ref, S = oracle.q6k_gemv(raw, n_in, n_out, x[keep])
     check_f32(out[keep], ref, S, "rows without a non-finite x")
 
@@ -248,7 +250,8 @@ def test_rows_output_projection(qd):
         check_f32(out, ref, S, f"q6k 128256x3072 b{batch}")
 
 
-@pytest.mark.parametrize("n_in,batch", [(3072, 3), (3072, 5), (3072, 8), (2048, 4), (2048, 7), (1024, 8)])
+@pytest.mark.parametrize("n_in,batch", [(3072, 3), (3072, 5), (3072, 8), (2048, 4), (2048, 7), (1024, 8),
+                                        (4096, 8)])
 def test_rows_tall_ragged(qd, n_in, batch):
     """A tall matrix (2051 row groups, the last one partly padding): 4 rows take
     four row groups a workgroup and 8 rows three, so the last workgroup holds
