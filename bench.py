@@ -502,6 +502,12 @@ def suite(args):
     xv, ov = xdev(synth.seed(4, 4), (1, 3072)), torch.empty((1, 128256), device=dev)
     timed("c4 q8_0_gemv vocab 128256x3072 b1", [lambda w=w: qd.q8_0_gemv(w, 3072, 128256, xv, out=ov) for w in wvoc],
           q8_bytes(128256, 3072) + 3072 * 4 + 128256 * 4, iters=40)
+    for bt in (4, 8):   # a batched decode step's output projection (integer matrix-core kernel)
+        xb, ob = xdev(synth.seed(4, 20 + bt), (bt, 3072)), torch.empty((bt, 128256), device=dev)
+        timed(f"c4 q8_0_gemv vocab 128256x3072 b{bt}",
+              [lambda w=w, xb=xb, ob=ob: qd.q8_0_gemv(w, 3072, 128256, xb, out=ob) for w in wvoc],
+              q8_bytes(128256, 3072) + bt * (3072 + 128256) * 4, iters=40)
+        del xb, ob
     # the same projection with the on-device top-k (logits kept, k candidates out)
     for k in (1, 40):
         ti = torch.empty((1, k), dtype=torch.int32, device=dev)
