@@ -471,18 +471,23 @@ __global__ __launch_bounds__(64 * KS * RG) void q8_0_gemv_i8(Q8GemvArgs a, TileA
 #pragma unroll
     for (int k = 0; k < NW; ++k) bad |= wbad[k];
 
-    // lane (n = lane % 16, b' = lane / 16) of fragment f: batch row 4 f + b'
-    int eb[NV][T];
+    // lane (n = lane % 16, b' = lane / 16) of fragment f: batch row 4 f + b'.
+    // Up to 16 blocks a wave the exponents are read once into registers;
+    // longer waves read each block's from LDS where it is used.
+    constexpr bool EBL = T > 16;
+    int eb[NV][EBL ? 1 : T];
+    if constexpr (!EBL) {
 #pragma unroll
-    for (int f = 0; f < NV; ++f)
+        for (int f = 0; f < NV; ++f)
 #pragma unroll
-        for (int q = 0; q < T / 4; ++q) {
-            const int4 e4 = *reinterpret_cast<const int4*>(&xe[4 * f + (lane >> 4)][blk0 + 4 * q]);
-            eb[f][4 * q] = e4.x;
-            eb[f][4 * q + 1] = e4.y;
-            eb[f][4 * q + 2] = e4.z;
-            eb[f][4 * q + 3] = e4.w;
-        }
+            for (int q = 0; q < T / 4; ++q) {
+                const int4 e4 = *reinterpret_cast<const int4*>(&xe[4 * f + (lane >> 4)][blk0 + 4 * q]);
+                eb[f][4 * q] = e4.x;
+                eb[f][4 * q + 1] = e4.y;
+                eb[f][4 * q + 2] = e4.z;
+                eb[f][4 * q + 3] = e4.w;
+            }
+    }
     float acc[NM][NV];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -505,7 +510,8 @@ __global__ __launch_bounds__(64 * KS * RG) void q8_0_gemv_i8(Q8GemvArgs a, TileA
                                                                       i32x4{0, 0, 0, 0}, 0, 0, 0);
                 const float u =
                     __builtin_fmaf((float)(D[3] * 256 + D[2]), 65536.0f, (float)(D[1] * 256 + D[0]));
-                acc[m][f] = __builtin_fmaf(dsc, __builtin_amdgcn_ldexpf(u, eb[f][i]), acc[m][f]);
+                const int e = EBL ? xe[4 * f + (lane >> 4)][blk0 + i] : eb[f][EBL ? 0 : i];
+                acc[m][f] = __builtin_fmaf(dsc, __builtin_amdgcn_ldexpf(u, e), acc[m][f]);
             }
         }
     }
@@ -581,6 +587,26 @@ bool i8_shape(int64_t n_in, int64_t batch, int mode, int* ks, int* t)
 }
 
 int i8_rg(int64_t groups, int ks) { return groups >= 512 && ks <= 6 ? 2 : 1; }
+
+// 5..8 rows of a tall plain or residual product at 3072 columns (>= 2048 row
+// groups): kTallRG row groups a workgroup of 4 waves x 24 blocks, so each
+// workgroup's x preparation (two fragments) serves 16 kTallRG weight rows
+// instead of 32.  Measured at 128256 x 3072 (graph-replayed): b8 125 -> 106
+// us with four row groups (118 us with three); at 3..4 rows (one fragment)
+// it was slower than two row groups of 6 waves (b4 74 -> 86 us).
+constexpr int kTallRG = 4;
+
+bool i8_tall(int64_t n_in, int64_t batch, int mode, int64_t groups)
+{
+    return n_in == 3072 && batch > 4 && batch <= 8 && groups >= 2048 && (mode == kPlain || mode == kResidual);
+}
+
+template <int MODE>
+MfmaFn pick_i8_tall()
+{
+    if constexpr (MODE == kPlain || MODE == kResidual) return q8_0_gemv_i8<MODE, 4, 24, 2, kTallRG>;
+    return nullptr;
+}
 
 template <int MODE, int KS, int T>
 MfmaFn pick_i8_rg(int nv, int rg)
@@ -755,14 +781,21 @@ hipError_t launch_q8_0_gemv_mfma(const Q8GemvProblem& p, const Q8TView* tiles, v
     int iks = 0, it = 0;
     if (i8_shape(p.n_in, p.batch, p.mode, &iks, &it)) {
         if (!q8_mfma_plan_check(p, 0).empty()) return hipErrorInvalidConfiguration;
-        const int rg = i8_rg(t.groups, iks), nv = (int)((p.batch + 3) / 4);
+        int rg = i8_rg(t.groups, iks);
+        const int nv = (int)((p.batch + 3) / 4);
         t.ksplit = 1;
         MfmaFn fn = nullptr;
-        switch (p.mode) {
-            case kPlain: fn = pick_i8<kPlain>(iks, nv, rg); break;
-            case kResidual: fn = pick_i8<kResidual>(iks, nv, rg); break;
-            case kQKV: fn = pick_i8<kQKV>(iks, nv, rg); break;
-            default: fn = pick_i8<kSwiGLU>(iks, nv, rg); break;
+        if (i8_tall(p.n_in, p.batch, p.mode, t.groups)) {
+            iks = 4;   // 4 waves x 24 blocks = 3072 columns
+            rg = kTallRG;
+            fn = p.mode == kPlain ? pick_i8_tall<kPlain>() : pick_i8_tall<kResidual>();
+        } else {
+            switch (p.mode) {
+                case kPlain: fn = pick_i8<kPlain>(iks, nv, rg); break;
+                case kResidual: fn = pick_i8<kResidual>(iks, nv, rg); break;
+                case kQKV: fn = pick_i8<kQKV>(iks, nv, rg); break;
+                default: fn = pick_i8<kSwiGLU>(iks, nv, rg); break;
+            }
         }
         if (!fn) return hipErrorNotSupported;
         hipLaunchKernelGGL(fn, dim3((unsigned)((t.groups + rg - 1) / rg)), dim3(64 * iks * rg), 0, s, a, t);

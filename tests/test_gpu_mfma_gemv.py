@@ -450,3 +450,39 @@ def test_wide_swiglu_and_qkv(qd, n_in, batch):
     check_f32(host(q), rq, sq, "q")
     check_f32(host(k), rk, sk, "k")
     check_f32(host(v), rv, sv, "v")
+
+
+@pytest.mark.parametrize("batch,mode", [(3, "plain"), (4, "residual"), (5, "plain"), (8, "plain"),
+                                        (6, "residual"), (8, "residual")])
+def test_integer_path_tall(qd, batch, mode):
+    """A tall product at 3072 columns (2051 row groups): 5..8 rows take four
+    row groups a workgroup of 4 waves x 24 blocks (three spare groups in the
+    last workgroup), 3..4 rows two row groups of 6 waves; one launch, no
+    workspace."""
+    n_in, n_out = 3072, 2050 * 16 + 5
+    raw = q8_weights(9990 + batch, n_out, n_in)
+    x = synth.normal_f32(9991 + batch, (batch, n_in))
+    w, xd = dev(raw), dev(x)
+    qd.prepare(w, qd.TYPE_Q8_0, n_in, n_out)
+    if mode == "plain":
+        out, n = launches(qd, lambda: qd.q8_0_gemv(w, n_in, n_out, xd))
+        ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x)
+    else:
+        r = synth.normal_f32(9992 + batch, (batch, n_out))
+        out, n = launches(qd, lambda: qd.q8_0_gemv_residual(w, n_in, n_out, xd, dev(r)))
+        ref, S = oracle.q8_0_gemv_residual(raw, n_in, n_out, x, r)
+    assert n == 1
+    check_f32(host(out), ref, S, f"integer tall {mode} {n_out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_integer_path_tall_non_finite_row(qd, bad):
+    n_in, n_out, batch = 3072, 2048 * 16, 7
+    raw = q8_weights(9995, n_out, n_in)
+    x = synth.normal_f32(9996, (batch, n_in))
+    x[5, 3000] = bad
+    out = host(qd.q8_0_gemv(dev(raw), n_in, n_out, dev(x)))
+    assert np.all(np.isnan(out[5]))
+    keep = [b for b in range(batch) if b != 5]
+    ref, S = oracle.q8_0_gemv(raw, n_in, n_out, x[keep])
+    check_f32(out[keep], ref, S, "tall rows without a non-finite x")
